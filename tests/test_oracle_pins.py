@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU).
+
+Each test checks the oracle against something it does not share code with:
+torch's own float8 / bfloat16 casts, the OCP E2M1 value table, a brute-force
+nearest-code search, scipy's logistic function, a float64 dense evaluation of
+the whole layer (tests/dense_ref.py), brute-force dispatch, and invariants
+that must hold exactly (pad slots contribute nothing, zero W2 gives zero, a
+W2 exponent + 1 doubles the output, permuting tokens or relabelling experts
+permutes nothing else).
+"""
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle
+import synth
+from dense_ref import E2M1_VALUES, dec_fp4_rows, dec_fp8_rows, dense_layer, q8_rows
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- codecs ----
+
+def test_e4m3_decode_every_code_matches_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle.e4m3_decode(c) for c in range(256)], np.float32)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert nan.sum() == 2  # 0x7F and 0xFF
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert oracle.e4m3_decode(0x7E) == 448.0 and oracle.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def test_e8m0_decode_every_byte_matches_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).float().numpy()
+    got = np.array([oracle.e8m0_decode(b) for b in range(256)], np.float32)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+
+
+def test_e2m1_decode_matches_ocp_table():
+    got = np.array([oracle.e2m1_decode(n) for n in range(16)])
+    np.testing.assert_array_equal(got, E2M1_VALUES)
+    assert np.signbit(got[8])
+
+
+def _e4m3_finite_table():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.int64)
+    vals = np.array([oracle.e4m3_decode(c) for c in codes], np.float64)
+    return codes, vals
+
+
+def _brute_force_e4m3(v, codes, vals):
+    """Nearest finite e4m3 code; ties to the even code (mantissa LSB 0);
+    magnitudes past 448 saturate; between +0 and -0 the sign of v decides."""
+    out = np.zeros(v.size, np.int64)
+    for i, x in enumerate(v):
+        if abs(x) >= 448.0:
+            out[i] = 0xFE if x < 0 else 0x7E
+            continue
+        d = np.abs(vals - x)
+        cand = codes[d == d.min()]
+        if cand.size > 1:
+            cand = cand[(cand & 1) == 0]
+        if cand.size > 1:
+            cand = cand[(cand >= 0x80) == bool(np.signbit(x))]
+        assert cand.size == 1
+        out[i] = cand[0]
+    return out
+
+
+def test_e4m3_encode_brute_force_and_torch():
+    codes, vals = _e4m3_finite_table()
+    rng = np.random.default_rng(7)
+    mags = np.exp2(rng.uniform(-13, 9.5, 4000))
+    v = mags * rng.choice([-1.0, 1.0], mags.size)
+    # exact midpoints between neighbouring positive codes and their negatives
+    pos = np.sort(vals[vals > 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    v = np.concatenate([v, mids, -mids, [0.0, -0.0, 448.0, 449.0, 464.0, 470.0, 1e6, -1e6,
+                                        2.0 ** -10, 2.0 ** -9, 3 * 2.0 ** -10]])
+    got = np.array([oracle.e4m3_encode(x) for x in v], np.int64)
+    want = _brute_force_e4m3(v, codes, vals)
+    np.testing.assert_array_equal(got, want)
+    # torch rounds to nearest even but does not saturate: clip first
+    t = torch.from_numpy(np.clip(v, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(got, t.view(torch.uint8).numpy().astype(np.int64))
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes, vals = _e4m3_finite_table()
+    for c, x in zip(codes, vals):
+        assert oracle.e4m3_encode(x) == c
+
+
+def test_bf16_encode_matches_torch():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    f = np.concatenate([f, np.float32([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.4e38])])
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    lib = oracle.lib()
+    got = np.array([lib.orc_bf16_encode(float(x)) for x in f], np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_swiglu_against_logistic_and_clamps():
+    rng = np.random.default_rng(1)
+    g = rng.normal(0, 8, 2000).astype(np.float32)
+    u = rng.normal(0, 8, 2000).astype(np.float32)
+    got = np.array([oracle.swiglu(a, b) for a, b in zip(g, u)], np.float64)
+    gc = np.minimum(g.astype(np.float64), 10.0)
+    uc = np.clip(u.astype(np.float64), -10.0, 10.0)
+    want = gc * expit(gc) * uc
+    np.testing.assert_allclose(got, want, rtol=3e-7, atol=1e-30)
+    # closed-form points
+    assert oracle.swiglu(0.0, 5.0) == 0.0
+    assert oracle.swiglu(1.0, 1.0) == pytest.approx(0.7310585786300049, rel=1e-7)
+    assert oracle.swiglu(50.0, 50.0) == pytest.approx(10 * expit(10.0) * 10, rel=1e-7)
+    assert oracle.swiglu(50.0, -50.0) == pytest.approx(-10 * expit(10.0) * 10, rel=1e-7)
+    # the gate has no lower clamp: a very negative gate tends to -0
+    assert abs(oracle.swiglu(-30.0, 1.0)) < 1e-11
+
+
+def test_mx8_block_scale_rule_and_dense_requant():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        scale = np.exp2(rng.integers(-20, 20))
+        v = (rng.standard_normal(32) * scale).astype(np.float32)
+        if trial % 7 == 0:
+            v[rng.integers(0, 32, 5)] = 0.0
+        codes, sb = oracle.mx8_quant_block(v)
+        amax = np.abs(v).max()
+        E = sb - 127
+        assert 2.0 ** (E + 8) <= amax < 2.0 ** (E + 9)
+        deq = np.array([oracle.e4m3_decode(c) for c in codes]) * 2.0 ** E
+        # matches the independent float64 requantiser exactly
+        np.testing.assert_array_equal(deq, q8_rows(v.astype(np.float64)[None, :])[0])
+    codes, sb = oracle.mx8_quant_block(np.zeros(32, np.float32))
+    assert sb == 127 and not codes.any()
+    # a block of exactly representable values whose largest mantissa is at
+    # most 1.75 survives unchanged (1.875 would saturate to 448 after the
+    # floor(log2 amax) - 8 shift)
+    vals = [oracle.e4m3_decode(c) for c in range(0x40, 0x57)] + [0.0] * 9
+    exact = np.float32(vals) * np.float32(2.0 ** -5)
+    codes, sb = oracle.mx8_quant_block(exact)
+    assert sb - 127 == -10     # amax = 1.75 * 2^3 * 2^-5 = 1.75 * 2^-2
+    deq = np.array([oracle.e4m3_decode(c) for c in codes]) * 2.0 ** (sb - 127)
+    np.testing.assert_array_equal(deq, exact)
+    assert oracle.e4m3_decode(max(codes)) == 448.0
+
+
+# -------------------------------------------------------------- dispatch ----
+
+def _brute_dispatch(spec, ids):
+    K, T = spec.K, spec.T
+    rows = {e: [] for e in range(spec.E_local)}
+    invalid = 0
+    for r in range(T * K):
+        i = int(ids.reshape(-1)[r])
+        if i == -1:
+            continue
+        if i < 0 or i >= spec.E_total:
+            invalid += 1
+            continue
+        e = i - spec.expert_begin
+        if 0 <= e < spec.E_local:
+            rows[e].append(r)
+    return rows, invalid
+
+
+def _random_ids(rng, T, K, E_total):
+    ids = rng.integers(0, E_total, size=(T, K)).astype(np.int32)
+    m = rng.random((T, K))
+    ids[m < 0.15] = -1
+    ids[(m >= 0.15) & (m < 0.18)] = E_total + 3      # invalid, too large
+    ids[(m >= 0.18) & (m < 0.20)] = -7               # invalid, negative
+    return ids
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dispatch_matches_brute_force(mode, seed):
+    rng = np.random.default_rng(seed)
+    spec = synth.CONFIGS["tiny"].with_(T=97, K=6, E_total=40, E_local=9, expert_begin=5,
+                                       dispatch_mode=mode, capacity=11)
+    ids = _random_ids(rng, spec.T, spec.K, spec.E_total)
+    d = oracle.dispatch(spec, ids)
+    rows, invalid = _brute_dispatch(spec, ids)
+    assert d["status"][0] == invalid
+    counts = np.array([len(rows[e]) for e in range(spec.E_local)])
+    np.testing.assert_array_equal(d["counts"], counts)
+    rr = d["route_row"]
+    if mode == 0:
+        assert d["offsets"][0] == 0
+        np.testing.assert_array_equal(np.diff(d["offsets"]), counts)
+        assert counts.sum() == d["offsets"][-1]   # histogram sums to the valid routes
+        for e in range(spec.E_local):
+            seg = d["row_route"][d["offsets"][e]:d["offsets"][e + 1]]
+            np.testing.assert_array_equal(seg, rows[e])   # stable: ascending r
+        dropped = 0
+    else:
+        C = spec.capacity
+        np.testing.assert_array_equal(d["offsets"], np.arange(spec.E_local + 1) * C)
+        for e in range(spec.E_local):
+            kept = min(counts[e], C)
+            seg = d["row_route"][e * C:e * C + kept]
+            assert set(seg.tolist()) <= set(rows[e]) and len(set(seg.tolist())) == kept
+        dropped = int(np.maximum(counts - C, 0).sum())
+        assert dropped > 0  # this case is built to overflow
+    assert d["status"][1] == dropped
+    kept_routes = np.nonzero(rr >= 0)[0]
+    assert kept_routes.size == counts.sum() - dropped
+    np.testing.assert_array_equal(d["row_route"][rr[kept_routes]], kept_routes)
+
+
+# ------------------------------------------------------------ the layer ----
+
+def _case(name="tiny", **kw):
+    return synth.make_case(name, **kw)
+
+
+def _f(bits):
+    return oracle.bf16_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", [1000, 1001, 1002])
+def test_layer_matches_float64_dense_evaluation(seed):
+    case = _case(seed=seed)
+    spec = case["spec"]
+    out = _f(oracle.moe_layer(case))
+    dense, parts = dense_layer(case, return_parts=True)
+    rms = np.sqrt((dense ** 2).mean())
+    # float32 accumulation, rare requant flips and one bf16 rounding
+    err = np.abs(out - dense)
+    assert err.max() <= 2.0 ** -8 * np.abs(dense).max() + 2e-3 * rms, err.max() / rms
+    # per route: requantised intermediate equals the dense one except for
+    # rare single-step flips at rounding boundaries
+    d = oracle.dispatch(spec, case["topk_ids"])
+    routes = np.nonzero(d["route_row"] >= 0)[0]
+    ffn = oracle.routes_ffn(case, routes)
+    flips = 0
+    for i, r in enumerate(routes):
+        t, e = r // spec.K, case["topk_ids"].reshape(-1)[r] - spec.expert_begin
+        hq = dec_fp8_rows(ffn["h_codes"][i:i + 1], ffn["h_scale"][i:i + 1])[0]
+        flips += int((hq != parts[e]["Hq"][t]).sum())
+        np.testing.assert_allclose(ffn["y"][i], parts[e]["Y"][t], rtol=0,
+                                   atol=5e-3 * np.abs(parts[e]["Y"][t]).max() + 1e-6)
+    assert flips <= 0.002 * routes.size * spec.I + 2
+
+
+def test_single_expert_weight_one_is_a_dense_ffn():
+    case = _case(E_total=1, E_local=1, pad_frac=0.0, seed=77)
+    spec = case["spec"]
+    ids = np.full((spec.T, spec.K), -1, np.int32)
+    ids[:, 2] = 0
+    w = np.zeros((spec.T, spec.K), np.float32)
+    w[:, 2] = 1.0
+    case["topk_ids"], case["topk_w"] = ids, w
+    out = _f(oracle.moe_layer(case))
+    X = dec_fp8_rows(case["x_fp8"], case["x_scale"])
+    W13 = dec_fp4_rows(case["w13"][0], case["w13_scale"][0])
+    W2 = dec_fp4_rows(case["w2"][0], case["w2_scale"][0])
+    GU = X @ W13.T
+    g, u = np.minimum(GU[:, :spec.I], 10), np.clip(GU[:, spec.I:], -10, 10)
+    Y = q8_rows(g * expit(g) * u) @ W2.T
+    rms = np.sqrt((Y ** 2).mean())
+    assert np.abs(out - Y).max() <= 2.0 ** -8 * np.abs(Y).max() + 2e-3 * rms
+
+
+def test_all_pad_slots_give_exact_zero_and_pad_weights_do_not_matter():
+    case = _case(seed=1003)
+    base = oracle.moe_layer(case)
+    c2 = dict(case)
+    c2["topk_w"] = case["topk_w"].copy()
+    c2["topk_w"][case["topk_ids"] == -1] = 123.0
+    np.testing.assert_array_equal(oracle.moe_layer(c2), base)
+    c3 = dict(case)
+    c3["topk_ids"] = np.full_like(case["topk_ids"], -1)
+    assert not oracle.moe_layer(c3).any()   # +0 everywhere
+
+
+def test_zero_w2_gives_zero_and_restoring_is_exact():
+    case = _case(seed=1004)
+    base = oracle.moe_layer(case)
+    c2 = dict(case)
+    c2["w2"] = np.zeros_like(case["w2"])
+    assert not _f(oracle.moe_layer(c2)).any()
+    np.testing.assert_array_equal(oracle.moe_layer(case), base)
+
+
+def test_w2_exponent_plus_one_doubles_exactly():
+    case = _case(seed=1005)
+    base = _f(oracle.moe_layer(case))
+    c2 = dict(case)
+    c2["w2_scale"] = case["w2_scale"] + 1
+    np.testing.assert_array_equal(_f(oracle.moe_layer(c2)), 2 * base)
+
+
+def test_token_permutation_and_expert_relabel_are_exact():
+    case = _case(seed=1006)
+    spec = case["spec"]
+    base = oracle.moe_layer(case)
+    perm = np.random.default_rng(5).permutation(spec.T)
+    c2 = dict(case)
+    for k in ("x_fp8", "x_scale", "topk_ids", "topk_w"):
+        c2[k] = np.ascontiguousarray(case[k][perm])
+    np.testing.assert_array_equal(oracle.moe_layer(c2), base[perm])
+    # relabel local experts with a permutation p: expert e's weights move to
+    # slot p[e] and every id e becomes p[e]
+    p = np.random.default_rng(6).permutation(spec.E_local)
+    c3 = dict(case)
+    for k in ("w13", "w13_scale", "w2", "w2_scale"):
+        a = np.empty_like(case[k])
+        a[p] = case[k]
+        c3[k] = a
+    ids = case["topk_ids"].copy()
+    loc = (ids >= 0) & (ids < spec.E_local)
+    ids[loc] = p[ids[loc]]
+    c3["topk_ids"] = ids
+    np.testing.assert_array_equal(oracle.moe_layer(c3), base)
+
+
+def test_expert_shards_sum_to_the_whole():
+    case = _case(seed=1007)
+    spec = case["spec"]
+    full = _f(oracle.moe_layer(case))
+    total = np.zeros_like(full)
+    half = spec.E_local // 2
+    for begin, n in ((0, half), (half, spec.E_local - half)):
+        c = dict(case)
+        c["spec"] = spec.with_(expert_begin=begin, E_local=n)
+        for k in ("w13", "w13_scale", "w2", "w2_scale"):
+            c[k] = np.ascontiguousarray(case[k][begin:begin + n])
+        total += _f(oracle.moe_layer(c))
+    rms = np.sqrt((full ** 2).mean())
+    assert np.abs(total - full).max() <= 2.0 ** -7 * np.abs(full).max() + 1e-3 * rms
+
+
+def test_duplicate_ids_are_independent_routes():
+    case = _case(seed=1008)
+    spec = case["spec"]
+    ids = case["topk_ids"].copy()
+    ids[:, 1] = ids[:, 0] = 3
+    case["topk_ids"] = ids
+    case["topk_w"] = case["topk_w"].copy()
+    w = case["topk_w"]
+    out = _f(oracle.moe_layer(case))
+    dense = dense_layer(case)
+    rms = np.sqrt((dense ** 2).mean())
+    assert np.abs(out - dense).max() <= 2.0 ** -8 * np.abs(dense).max() + 2e-3 * rms
+    assert oracle.dispatch(spec, ids)["counts"][3] >= spec.T
+
+
+def test_generator_pad_count_and_determinism():
+    a = synth.make_case("tiny")
+    b = synth.make_case("tiny")
+    for k in ("x_fp8", "x_scale", "topk_ids", "topk_w", "w13", "w2"):
+        np.testing.assert_array_equal(a[k], b[k])
+    s = a["spec"]
+    assert (a["topk_ids"] == -1).sum() == round(0.10 * s.T * s.K)
+    # routing weights renormalised over the top-k
+    np.testing.assert_allclose(a["topk_w"].sum(axis=1), 1.0, rtol=1e-6)
+    # the x codes decode to BF16-rounded N(0,1) values within e4m3 precision
+    x = dec_fp8_rows(a["x_fp8"], a["x_scale"])
+    assert 0.9 < x.std() < 1.1
