@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the a8w4 MoE expert layer on MI355X.
+
+A step is one moe_forward (dispatch, GEMM1 + SwiGLU + FP8 requant, GEMM2,
+combine) over one synthetic batch whose inputs and weights are already
+resident in HBM.  The layer is captured once in a HIP graph and replayed;
+W warmup replays, then exactly K timed replays between two device
+synchronisations.
+
+Reported (one JSON line):
+  value        weight GB/s: touched-expert W13+W2 bytes per step / step time
+  us_per_layer, routed_tflops, hbm_frac (all algorithmic bytes / 8 TB/s),
+  mfma_frac (routed FLOP / 5.0 PFLOP/s dense FP8)
+  roofline     the dominant kernel (GEMM1 + SwiGLU + requant): its
+               algorithmic bytes per launch / its mean launch time, the time
+               taken with HIP events on the launch stream over K back-to-back
+               launches of the four steps
+  cpu_baseline the CPU oracle timed on a bounded sample of the same batch
+               (whole tokens), scaled to the full batch by its routes
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer µs + routed TFLOP/s + weight GB/s, fraction of roofline, "
+          "1 MI355X")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+DEFAULT_WORKLOAD = "v4_decode_t128_fixed"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-routes", type=int, default=32,
+                   help="routes in the oracle's timed sample")
+    p.add_argument("--kernel-iters", type=int, default=0,
+                   help="launches per kernel for the roofline timing (default: steps)")
+    return p.parse_args()
+
+
+def gemm1_algorithmic_bytes(spec, work) -> int:
+    """W13 codes + exponents of each touched expert, the MX FP8 x row of each
+    token with a local route, the MX FP8 h row written per route."""
+    H, I = spec.H, spec.I
+    w13 = work["touched"] * (2 * I * H // 2 + 2 * I * H // 32)
+    xin = work["tokens_with_route"] * (H + H // 32)
+    hout = work["routes"] * (I + I // 32)
+    return w13 + xin + hout
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dispatch_grouped_gemm_amd as moe
+    import synth
+
+    dev = torch.device("cuda", 0)
+    spec_name = args.workload
+    case = synth.make_case(spec_name)
+    spec = case["spec"]
+    work = synth.algorithmic_work(case)
+    shape = moe.MoeShape.of(spec)
+    g = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+         for k, v in case.items() if isinstance(v, np.ndarray)}
+    ws = moe.alloc_workspace(shape, dev)
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=dev)
+
+    def forward(stream=None):
+        moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
+                        g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream)
+
+    # ---- whole layer: graph replays ---------------------------------------------
+    forward()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        forward(stream=torch.cuda.current_stream())
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- per-kernel times: the four steps back to back on one stream --------------
+    d = moe.alloc_dispatch(shape, dev)
+    R = max(moe.moe_row_capacity(shape), 1)
+    h = torch.empty((R, spec.I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((R, spec.I // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((R, spec.H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    iters = args.kernel_iters or args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))   # keep the GPU busy while the launches are queued
+    for i in range(iters):
+        e = ev[i]
+        e[0].record(st)
+        moe.moe_dispatch(shape, g["topk_ids"], d, stream=st)
+        e[1].record(st)
+        moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"],
+                             h, hs, stream=st)
+        e[2].record(st)
+        moe.moe_gemm2(shape, h, hs, d, g["w2"], g["w2_scale"], y, stream=st)
+        e[3].record(st)
+        moe.moe_combine(shape, g["topk_w"], d.route_row, y, out, stream=st)
+        e[4].record(st)
+    torch.cuda.synchronize()
+    names = ["dispatch", "gemm1_swiglu", "gemm2", "combine"]
+    kern_us = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(iters)]))
+               * 1e3 for j, n in enumerate(names)}
+    status = d.status.cpu().numpy()
+
+    us = ms_per_step * 1e3
+    t_s = ms_per_step * 1e-3
+    weight_gbs = work["weight_bytes"] / t_s / 1e9
+    tflops = work["flop"] / t_s / 1e12
+    g1_bytes = gemm1_algorithmic_bytes(spec, work)
+    g1_gbs = g1_bytes / (kern_us["gemm1_swiglu"] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(weight_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": spec_name, "T": spec.T, "H": spec.H, "I": spec.I,
+                   "K": spec.K, "E_total": spec.E_total, "E_local": spec.E_local,
+                   "dispatch": "fixed-slot" if spec.dispatch_mode else "compact",
+                   "capacity": spec.capacity, "routes": work["routes"],
+                   "touched_experts": work["touched"]},
+        "us_per_layer": round(us, 2),
+        "routed_tflops": round(tflops, 3),
+        "weight_gbps": round(weight_gbs, 2),
+        "hbm_frac": round(work["bytes"] / t_s / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / FP8_PEAK_TFLOPS, 5),
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "dispatch_status": status.tolist(),
+        "roofline": {"bound": "hbm", "kernel": "gemm1_swiglu", "achieved": round(g1_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(g1_bytes)},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        ids = case["topk_ids"]
+        e = ids.astype(np.int64) - spec.expert_begin
+        loc = (ids >= 0) & (ids < spec.E_total) & (e >= 0) & (e < spec.E_local)
+        per_tok = loc.sum(axis=1)
+        toks = np.nonzero(per_tok)[0]
+        rng = np.random.default_rng(0)
+        rng.shuffle(toks)
+        take = toks[np.cumsum(per_tok[toks]) <= args.cpu_routes]
+        if take.size == 0:
+            take = toks[:1]
+        n_routes = int(per_tok[take].sum())
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        threads = max(1, min(threads, take.size))
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+        oracle.lib()
+        c0 = time.perf_counter()
+        oracle.moe_layer(case, np.sort(take))
+        cpu_s = time.perf_counter() - c0
+        full_s = cpu_s * work["routes"] / max(n_routes, 1)
+        result["cpu_baseline"] = {
+            "value": round(work["weight_bytes"] / full_s / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d tokens / %d of %d routes, %.2f s wall, scaled by routes to the "
+                      "full batch (%.1f s)" % (take.size, n_routes, work["routes"], cpu_s,
+                                               full_s)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,311 @@
+"""Python binding of libmoe_a8w4.so, the gfx950 a8w4 MoE expert layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI (include/moe_a8w4.h).  PyTorch provides device memory and
+streams.  There is no fallback: if the shared library is missing the import
+of any entry point raises.
+
+Entry points (same names as the C ABI):
+    moe_dispatch, moe_gemm1_swiglu, moe_gemm2, moe_combine, moe_forward,
+    moe_workspace_size, moe_dispatch_workspace_size, moe_row_capacity,
+    moe_check_shape, moe_strerror
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
+    "moe_dispatch_workspace_size", "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu",
+    "moe_gemm2", "moe_combine", "moe_forward", "moe_strerror", "DispatchBuffers",
+    "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT",
+]
+
+COMPACT = 0
+FIXED_SLOT = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoe_a8w4.so")
+
+EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
+            "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
+            "moe_combine", "moe_forward", "moe_strerror"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, moe_strerror(code), code))
+
+
+class _CShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("E_total", ctypes.c_int32),
+                ("expert_begin", ctypes.c_int32), ("E_local", ctypes.c_int32),
+                ("dispatch_mode", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("gate_limit", ctypes.c_float), ("up_limit", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class MoeShape:
+    T: int
+    H: int
+    I: int
+    K: int
+    E_total: int
+    E_local: int
+    expert_begin: int = 0
+    dispatch_mode: int = COMPACT
+    capacity: int = 0
+    gate_limit: float = 10.0
+    up_limit: float = 10.0
+
+    @classmethod
+    def of(cls, spec) -> "MoeShape":
+        """From any object with the same field names (e.g. a synth.CaseSpec)."""
+        return cls(spec.T, spec.H, spec.I, spec.K, spec.E_total, spec.E_local,
+                   spec.expert_begin, spec.dispatch_mode, spec.capacity,
+                   spec.gate_limit, spec.up_limit)
+
+    def c(self) -> _CShape:
+        return _CShape(self.T, self.H, self.I, self.K, self.E_total, self.expert_begin,
+                       self.E_local, self.dispatch_mode, self.capacity, self.gate_limit,
+                       self.up_limit)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                "libmoe_a8w4.so is not built; run `python -m dispatch_grouped_gemm_amd._build` "
+                "(hipcc --offload-arch=gfx950)")
+        h = ctypes.CDLL(library_path)
+        P = ctypes.c_void_p
+        S = ctypes.POINTER(_CShape)
+        h.moe_check_shape.argtypes = [S]
+        h.moe_check_shape.restype = ctypes.c_int
+        h.moe_row_capacity.argtypes = [S]
+        h.moe_row_capacity.restype = ctypes.c_int64
+        h.moe_dispatch_workspace_size.argtypes = [S]
+        h.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+        h.moe_workspace_size.argtypes = [S]
+        h.moe_workspace_size.restype = ctypes.c_size_t
+        h.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        h.moe_dispatch.restype = ctypes.c_int
+        h.moe_gemm1_swiglu.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        h.moe_gemm1_swiglu.restype = ctypes.c_int
+        h.moe_gemm2.argtypes = [S, P, P, P, P, P, P, P, P]
+        h.moe_gemm2.restype = ctypes.c_int
+        h.moe_combine.argtypes = [S, P, P, P, P, P]
+        h.moe_combine.restype = ctypes.c_int
+        h.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        h.moe_forward.restype = ctypes.c_int
+        h.moe_strerror.argtypes = [ctypes.c_int]
+        h.moe_strerror.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def moe_strerror(code: int) -> str:
+    return lib().moe_strerror(int(code)).decode()
+
+
+def moe_check_shape(shape: MoeShape) -> int:
+    c = shape.c()
+    return lib().moe_check_shape(ctypes.byref(c))
+
+
+def moe_row_capacity(shape: MoeShape) -> int:
+    c = shape.c()
+    return int(lib().moe_row_capacity(ctypes.byref(c)))
+
+
+def moe_dispatch_workspace_size(shape: MoeShape) -> int:
+    c = shape.c()
+    return int(lib().moe_dispatch_workspace_size(ctypes.byref(c)))
+
+
+def moe_workspace_size(shape: MoeShape) -> int:
+    c = shape.c()
+    return int(lib().moe_workspace_size(ctypes.byref(c)))
+
+
+# ---- tensor checks -------------------------------------------------------------
+
+_BYTE_DTYPES = {torch.uint8}
+for _n in ("float8_e8m0fnu", "float8_e4m3fn", "float4_e2m1fn_x2"):
+    if hasattr(torch, _n):
+        _BYTE_DTYPES.add(getattr(torch, _n))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, shape, dtypes, device) -> int:
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t.data_ptr()
+
+
+def _e8m0(name):
+    # E8M0 exponents are read as bytes; an e4m3 view is refused
+    return {torch.uint8} | ({torch.float8_e8m0fnu} if hasattr(torch, "float8_e8m0fnu") else set())
+
+
+def _fp8():
+    return {torch.uint8} | ({torch.float8_e4m3fn} if hasattr(torch, "float8_e4m3fn") else set())
+
+
+def _fp4():
+    return {torch.uint8} | (
+        {torch.float4_e2m1fn_x2} if hasattr(torch, "float4_e2m1fn_x2") else set())
+
+
+def _stream(stream, device) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise MoeError(rc, where)
+
+
+# ---- entry points -----------------------------------------------------------------
+
+@dataclass
+class DispatchBuffers:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    row_route: torch.Tensor
+    route_row: torch.Tensor
+    status: torch.Tensor
+    workspace: Optional[torch.Tensor]
+
+
+def alloc_dispatch(shape: MoeShape, device) -> DispatchBuffers:
+    R = max(moe_row_capacity(shape), 1)
+    ws = moe_dispatch_workspace_size(shape)
+    i32 = dict(dtype=torch.int32, device=device)
+    return DispatchBuffers(
+        counts=torch.zeros(shape.E_local, **i32),
+        offsets=torch.zeros(shape.E_local + 1, **i32),
+        row_route=torch.full((R,), -1, **i32),
+        route_row=torch.full((max(shape.T * shape.K, 1),), -1, **i32),
+        status=torch.zeros(4, **i32),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device) if ws else None)
+
+
+def alloc_workspace(shape: MoeShape, device) -> torch.Tensor:
+    return torch.empty(max(moe_workspace_size(shape), 1), dtype=torch.uint8, device=device)
+
+
+def moe_dispatch(shape: MoeShape, topk_ids, d: DispatchBuffers, stream=None):
+    dev = topk_ids.device
+    T, K, E = shape.T, shape.K, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(topk_ids, "topk_ids", (T, K), i32, dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            _ptr(d.row_route, "row_route", (R,), i32, dev),
+            _ptr(d.route_row, "route_row", (max(T * K, 1),), i32, dev),
+            _ptr(d.status, "status", (4,), i32, dev)]
+    ws_ptr, ws_n = None, 0
+    if d.workspace is not None:
+        ws_ptr = _ptr(d.workspace, "workspace", None, {torch.uint8}, dev)
+        ws_n = d.workspace.numel()
+    c = shape.c()
+    _check(lib().moe_dispatch(ctypes.byref(c), *args, ws_ptr, ws_n, _stream(stream, dev)),
+           "moe_dispatch")
+
+
+def moe_gemm1_swiglu(shape: MoeShape, x_fp8, x_scale, d: DispatchBuffers, w13, w13_scale,
+                     h_fp8, h_scale, stream=None):
+    dev = x_fp8.device
+    T, H, I, E = shape.T, shape.H, shape.I, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev),
+            _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            _ptr(d.row_route, "row_route", (R,), i32, dev),
+            _ptr(w13, "w13", (E, 2 * I, H // 2), _fp4(), dev),
+            _ptr(w13_scale, "w13_scale", (E, 2 * I, H // 32), _e8m0("w13_scale"), dev),
+            _ptr(h_fp8, "h_fp8", (R, I), _fp8(), dev),
+            _ptr(h_scale, "h_scale", (R, I // 32), _e8m0("h_scale"), dev)]
+    c = shape.c()
+    _check(lib().moe_gemm1_swiglu(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_gemm1_swiglu")
+
+
+def moe_gemm2(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_scale, y_f32,
+              stream=None):
+    dev = h_fp8.device
+    H, I, E = shape.H, shape.I, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(h_fp8, "h_fp8", (R, I), _fp8(), dev),
+            _ptr(h_scale, "h_scale", (R, I // 32), _e8m0("h_scale"), dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
+            _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
+            _ptr(y_f32, "y_f32", (R, H), {torch.float32}, dev)]
+    c = shape.c()
+    _check(lib().moe_gemm2(ctypes.byref(c), *args, _stream(stream, dev)), "moe_gemm2")
+
+
+def moe_combine(shape: MoeShape, topk_w, route_row, y_f32, out_bf16, stream=None):
+    dev = topk_w.device
+    T, K, H = shape.T, shape.K, shape.H
+    R = max(moe_row_capacity(shape), 1)
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
+            _ptr(route_row, "route_row", (max(T * K, 1),), {torch.int32}, dev),
+            _ptr(y_f32, "y_f32", (R, H), {torch.float32}, dev),
+            _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
+    c = shape.c()
+    _check(lib().moe_combine(ctypes.byref(c), *args, _stream(stream, dev)), "moe_combine")
+
+
+def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2,
+                w2_scale, out_bf16, workspace, stream=None):
+    dev = x_fp8.device
+    T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev),
+            _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev),
+            _ptr(topk_ids, "topk_ids", (T, K), {torch.int32}, dev),
+            _ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
+            _ptr(w13, "w13", (E, 2 * I, H // 2), _fp4(), dev),
+            _ptr(w13_scale, "w13_scale", (E, 2 * I, H // 32), _e8m0("w13_scale"), dev),
+            _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
+            _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
+            _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
+    ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
+    c = shape.c()
+    _check(lib().moe_forward(ctypes.byref(c), *args, ws, workspace.numel(),
+                             _stream(stream, dev)), "moe_forward")

@@ -1,0 +1,222 @@
+// C ABI of the a8w4 MoE layer: argument checks (all before the first
+// launch), workspace layout and the launch sequence.
+#include <math.h>
+
+#include "moe_common.hpp"
+
+namespace {
+
+using moe::kMaxLocalExperts;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Byte layout of the moe_forward workspace.
+struct Layout {
+    size_t counts, offsets, row_route, route_row, status, scratch, h, hs, y, total;
+};
+
+Layout layout_of(const moe_shape &s)
+{
+    const size_t R = (size_t)moe_row_capacity(&s);
+    const size_t TK = (size_t)s.T * (size_t)s.K;
+    Layout L{};
+    size_t p = 0;
+    L.counts = p;
+    p = align_up(p + sizeof(int32_t) * (size_t)s.E_local);
+    L.offsets = p;
+    p = align_up(p + sizeof(int32_t) * ((size_t)s.E_local + 1));
+    L.row_route = p;
+    p = align_up(p + sizeof(int32_t) * R);
+    L.route_row = p;
+    p = align_up(p + sizeof(int32_t) * TK);
+    L.status = p;
+    p = align_up(p + sizeof(int32_t) * 4);
+    L.scratch = p;
+    p = align_up(p + moe::dispatch_scratch_bytes(s));
+    L.h = p;
+    p = align_up(p + R * (size_t)s.I);
+    L.hs = p;
+    p = align_up(p + R * (size_t)(s.I / 32));
+    L.y = p;
+    p = align_up(p + R * (size_t)s.H * sizeof(float));
+    L.total = p;
+    return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+hipStream_t as_stream(void *p) { return static_cast<hipStream_t>(p); }
+
+} // namespace
+
+extern "C" {
+
+int moe_check_shape(const moe_shape *s)
+{
+    if (!s)
+        return MOE_EINVAL;
+    if (s->T < 0 || s->H <= 0 || s->I <= 0 || s->K < 1 || s->E_total < 1 || s->E_local < 1 ||
+        s->expert_begin < 0)
+        return MOE_EINVAL;
+    if (s->dispatch_mode != MOE_DISPATCH_COMPACT && s->dispatch_mode != MOE_DISPATCH_FIXED_SLOT)
+        return MOE_EINVAL;
+    if (s->dispatch_mode == MOE_DISPATCH_FIXED_SLOT && s->capacity < 1)
+        return MOE_EINVAL;
+    if (isnan(s->gate_limit) || isnan(s->up_limit))
+        return MOE_EINVAL;
+    if ((long long)s->expert_begin + s->E_local > s->E_total)
+        return MOE_EINVAL;
+    if (s->K > 8 || s->E_local > kMaxLocalExperts)
+        return MOE_ENOTSUP;
+    if (s->H % 128 != 0 || s->I % 128 != 0)
+        return MOE_ENOTSUP;
+    if ((long long)s->T * s->K >= (1ll << 31))
+        return MOE_ENOTSUP;
+    if (s->dispatch_mode == MOE_DISPATCH_FIXED_SLOT &&
+        (long long)s->E_local * s->capacity >= (1ll << 31))
+        return MOE_ENOTSUP;
+    return MOE_OK;
+}
+
+int64_t moe_row_capacity(const moe_shape *s)
+{
+    if (moe_check_shape(s) != MOE_OK)
+        return -1;
+    if (s->dispatch_mode == MOE_DISPATCH_FIXED_SLOT)
+        return (int64_t)s->E_local * s->capacity;
+    return (int64_t)s->T * s->K;
+}
+
+size_t moe_dispatch_workspace_size(const moe_shape *s)
+{
+    if (moe_check_shape(s) != MOE_OK)
+        return 0;
+    return moe::dispatch_scratch_bytes(*s);
+}
+
+size_t moe_workspace_size(const moe_shape *s)
+{
+    if (moe_check_shape(s) != MOE_OK)
+        return 0;
+    return layout_of(*s).total;
+}
+
+int moe_dispatch(const moe_shape *s, const int32_t *ids, int32_t *counts, int32_t *offsets,
+                 int32_t *row_route, int32_t *route_row, int32_t *status, void *ws,
+                 size_t ws_bytes, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (!counts || !offsets || !status)
+        return MOE_EINVAL;
+    if (s->T > 0 && (!ids || !row_route || !route_row))
+        return MOE_EINVAL;
+    const size_t need = moe::dispatch_scratch_bytes(*s);
+    if (need && (!ws || ws_bytes < need))
+        return MOE_EWORKSPACE;
+    return hip_status(moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
+                                           ws, as_stream(stream)));
+}
+
+int moe_gemm1_swiglu(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
+                     const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
+                     const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
+                     void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!x || !xs || !counts || !offsets || !row_route || !w13 || !w13s || !h || !hs)
+        return MOE_EINVAL;
+    return hip_status(moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
+                                        as_stream(stream)));
+}
+
+int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int32_t *counts,
+              const int32_t *offsets, const uint8_t *w2, const uint8_t *w2s, float *y,
+              void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!h || !hs || !counts || !offsets || !w2 || !w2s || !y)
+        return MOE_EINVAL;
+    return hip_status(
+        moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, as_stream(stream)));
+}
+
+int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, const float *y,
+                uint16_t *out, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!tw || !route_row || !y || !out)
+        return MOE_EINVAL;
+    return hip_status(moe::launch_combine(*s, tw, route_row, y, out, as_stream(stream)));
+}
+
+int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
+                const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!x || !xs || !ids || !tw || !w13 || !w13s || !w2 || !w2s || !out)
+        return MOE_EINVAL;
+    const Layout L = layout_of(*s);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
+        return MOE_EWORKSPACE;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *row_route = reinterpret_cast<int32_t *>(base + L.row_route);
+    int32_t *route_row = reinterpret_cast<int32_t *>(base + L.route_row);
+    int32_t *status = reinterpret_cast<int32_t *>(base + L.status);
+    void *scratch = base + L.scratch;
+    uint8_t *h = base + L.h;
+    uint8_t *hs = base + L.hs;
+    float *y = reinterpret_cast<float *>(base + L.y);
+    hipStream_t st = as_stream(stream);
+    hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
+                                        scratch, st);
+    if (e == hipSuccess)
+        e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
+    if (e == hipSuccess)
+        e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
+    if (e == hipSuccess)
+        e = moe::launch_combine(*s, tw, route_row, y, out, st);
+    return hip_status(e);
+}
+
+const char *moe_strerror(int code)
+{
+    switch (code) {
+    case MOE_OK:
+        return "ok";
+    case MOE_EINVAL:
+        return "invalid argument";
+    case MOE_ENOTSUP:
+        return "shape not supported (H and I multiples of 128, K <= 8, E_local <= 512)";
+    case MOE_EWORKSPACE:
+        return "workspace missing, too small or not 256-byte aligned";
+    case MOE_EHIP:
+        return "HIP launch failed";
+    default:
+        return "unknown error";
+    }
+}
+
+} // extern "C"

@@ -1,0 +1,446 @@
+// Route dispatch for gfx950: compact (histogram -> exclusive scan -> stable
+// scatter) and fixed-slot (atomic claim of a slot in a per-expert segment of
+// fixed capacity, no prepare pass).
+//
+// Both modes group the same routes: a slot (t, k) is kept when its id names
+// one of this GPU's experts.  Compact packs the kept routes of each expert
+// contiguously in ascending route order r = t*K + k; fixed-slot gives each
+// route the next free slot of its expert, in whatever order the claims land.
+//
+// Stable ranks inside a wavefront come from ballots: the lanes that hold the
+// same expert form a 64-bit mask, a lane's rank is the popcount of the mask
+// below it, and one leader per expert does the bookkeeping for the group.
+#include "moe_common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 1024; // 16 wavefronts
+constexpr int kWaves = kThreads / 64;
+constexpr int kSlotsPerWaveLarge = 256;
+constexpr int kSlotsPerBlockLarge = kWaves * kSlotsPerWaveLarge;
+// compact dispatch of at most this many slots runs in one workgroup
+constexpr long kSmallSlots = 16384;
+
+struct Match {
+    int rank;                 // lanes below with the same key
+    int count;                // lanes with the same key
+    unsigned long long mask;  // those lanes
+};
+
+// Group the active lanes of the wavefront by key.
+__device__ __forceinline__ Match wave_match(int key, bool active)
+{
+    Match m{0, 0, 0ull};
+    const unsigned long long lt = __lanemask_lt();
+    unsigned long long rem = __ballot(active);
+    while (rem) {
+        const int leader = __ffsll((long long)rem) - 1;
+        const int k = __builtin_amdgcn_readlane(key, leader);
+        const bool mine = active && key == k;
+        const unsigned long long mk = __ballot(mine);
+        if (mine) {
+            m.rank = __popcll(mk & lt);
+            m.count = __popcll(mk);
+            m.mask = mk;
+        }
+        rem &= ~mk;
+    }
+    return m;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        v += __shfl_xor(v, d);
+    return v;
+}
+
+// Per-wavefront histogram of the slots [b, e) into hist_row (LDS); returns
+// the wavefront's count of invalid ids (in every lane).
+__device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
+                              int *hist_row)
+{
+    const int lane = threadIdx.x & 63;
+    int invalid = 0;
+    for (long base = b; base < e; base += 64) {
+        const long r = base + lane;
+        const int ex = r < e ? route_local(s, ids[r]) : -1;
+        const Match m = wave_match(ex, ex >= 0);
+        if (ex >= 0 && m.rank == 0)
+            hist_row[ex] += m.count; // one leader per expert: no two lanes collide
+        invalid += ex == -2;
+    }
+    return wave_sum(invalid);
+}
+
+// Stable scatter of the slots [b, e): base_row[ex] (LDS, this wavefront's
+// own row) is the next row of expert ex for this wavefront.
+__device__ void wave_scatter(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
+                             int *base_row, int32_t *__restrict__ row_route,
+                             int32_t *__restrict__ route_row)
+{
+    const int lane = threadIdx.x & 63;
+    for (long base = b; base < e; base += 64) {
+        const long r = base + lane;
+        const int ex = r < e ? route_local(s, ids[r]) : -1;
+        const Match m = wave_match(ex, ex >= 0);
+        int row = -1;
+        if (ex >= 0)
+            row = base_row[ex] + m.rank;
+        // every lane has read its base before a leader moves it on
+        __builtin_amdgcn_wave_barrier();
+        if (ex >= 0 && m.rank == 0)
+            base_row[ex] += m.count;
+        __builtin_amdgcn_wave_barrier();
+        if (r < e) {
+            route_row[r] = row;
+            if (row >= 0)
+                row_route[row] = (int32_t)r;
+        }
+    }
+}
+
+// Exclusive scan of v over the 1024 threads; returns the exclusive prefix
+// and writes the total to *total (every thread).
+__device__ int block_exclusive_scan(int v, int *total)
+{
+    __shared__ int wsum[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (lane >= d)
+            inc += o;
+    }
+    if (lane == 63)
+        wsum[wave] = inc;
+    __syncthreads();
+    int base = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        const int x = wsum[w];
+        if (w < wave)
+            base += x;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return base + inc - v;
+}
+
+// ---- compact, one workgroup ------------------------------------------------
+
+__global__ void __launch_bounds__(kThreads)
+compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
+                     int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
+                     int32_t *__restrict__ route_row, int32_t *__restrict__ status)
+{
+    extern __shared__ int hist[]; // [kWaves][E_local]
+    __shared__ int invalid_total;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = s.E_local;
+    const long n = (long)s.T * s.K;
+    const long per_wave = (n + kWaves - 1) / kWaves;
+    const long b = min(n, per_wave * wave), e = min(n, b + per_wave);
+
+    for (int i = tid; i < kWaves * E; i += kThreads)
+        hist[i] = 0;
+    if (tid == 0)
+        invalid_total = 0;
+    __syncthreads();
+    const int inv = wave_histogram(s, ids, b, e, hist + wave * E);
+    if (lane == 0 && inv)
+        atomicAdd(&invalid_total, inv);
+    __syncthreads();
+
+    // totals per expert, exclusive scan over experts
+    int cnt = 0;
+    if (tid < E)
+        for (int w = 0; w < kWaves; ++w)
+            cnt += hist[w * E + tid];
+    int total;
+    const int off = block_exclusive_scan(tid < E ? cnt : 0, &total);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = off;
+        int run = off; // per-wavefront bases, wavefronts in slot order
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = hist[w * E + tid];
+            hist[w * E + tid] = run;
+            run += c;
+        }
+    }
+    if (tid == 0) {
+        offsets[E] = total;
+        status[0] = invalid_total;
+        status[1] = status[2] = status[3] = 0;
+    }
+    __syncthreads();
+    wave_scatter(s, ids, b, e, hist + wave * E, row_route, route_row);
+}
+
+// ---- compact, many workgroups ------------------------------------------------
+
+// Pass 1: per-workgroup histograms; scratch[blk][E] holds the invalid count.
+__global__ void __launch_bounds__(kThreads)
+compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ scratch)
+{
+    extern __shared__ int hist[]; // [E_local]
+    __shared__ int invalid_total;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = s.E_local;
+    const long n = (long)s.T * s.K;
+    for (int i = tid; i < E; i += kThreads)
+        hist[i] = 0;
+    if (tid == 0)
+        invalid_total = 0;
+    __syncthreads();
+    const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
+    const long e = min(n, b + kSlotsPerWaveLarge);
+    // wavefronts share the workgroup histogram: add with LDS atomics
+    int inv = 0;
+    for (long base = b; base < e; base += 64) {
+        const long r = base + lane;
+        const int ex = r < e ? route_local(s, ids[r]) : -1;
+        const Match m = wave_match(ex, ex >= 0);
+        if (ex >= 0 && m.rank == 0)
+            atomicAdd(&hist[ex], m.count);
+        inv += ex == -2;
+    }
+    inv = wave_sum(inv);
+    if (lane == 0 && inv)
+        atomicAdd(&invalid_total, inv);
+    __syncthreads();
+    int32_t *row = scratch + (size_t)blockIdx.x * (E + 1);
+    for (int i = tid; i < E; i += kThreads)
+        row[i] = hist[i];
+    if (tid == 0)
+        row[E] = invalid_total;
+}
+
+// Pass 2 (one workgroup): counts, offsets, status, and every workgroup's
+// first row per expert, written back over its histogram.
+__global__ void __launch_bounds__(kThreads)
+compact_scan_kernel(Shape s, int nblk, int32_t *__restrict__ scratch, int32_t *__restrict__ counts,
+                    int32_t *__restrict__ offsets, int32_t *__restrict__ status)
+{
+    const int tid = threadIdx.x;
+    const int E = s.E_local;
+    int cnt = 0;
+    if (tid < E) {
+        for (int b = 0; b < nblk; ++b) {
+            int32_t *p = scratch + (size_t)b * (E + 1) + tid;
+            const int c = *p;
+            *p = cnt;
+            cnt += c;
+        }
+    }
+    int total;
+    const int off = block_exclusive_scan(tid < E ? cnt : 0, &total);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = off;
+        for (int b = 0; b < nblk; ++b)
+            scratch[(size_t)b * (E + 1) + tid] += off;
+    }
+    if (tid == 0) {
+        offsets[E] = total;
+        int inv = 0;
+        for (int b = 0; b < nblk; ++b)
+            inv += scratch[(size_t)b * (E + 1) + E];
+        status[0] = inv;
+        status[1] = status[2] = status[3] = 0;
+    }
+}
+
+// Pass 3: stable scatter of each workgroup's slots from its first rows.
+__global__ void __launch_bounds__(kThreads)
+compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *__restrict__ scratch,
+                       int32_t *__restrict__ row_route, int32_t *__restrict__ route_row)
+{
+    extern __shared__ int hist[]; // [kWaves][E_local]
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int E = s.E_local;
+    const long n = (long)s.T * s.K;
+    for (int i = tid; i < kWaves * E; i += kThreads)
+        hist[i] = 0;
+    __syncthreads();
+    const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
+    const long e = min(n, b + kSlotsPerWaveLarge);
+    (void)wave_histogram(s, ids, b, e, hist + wave * E);
+    __syncthreads();
+    if (tid < E) {
+        int run = scratch[(size_t)blockIdx.x * (E + 1) + tid];
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = hist[w * E + tid];
+            hist[w * E + tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    wave_scatter(s, ids, b, e, hist + wave * E, row_route, route_row);
+}
+
+// ---- fixed-slot ----------------------------------------------------------------
+
+// Claim one slot per kept route: the leader of each expert group adds the
+// group's size to the expert's counter and hands out consecutive slots.
+template <bool kLds>
+__device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
+                            int32_t *cnt, int32_t *__restrict__ row_route,
+                            int32_t *__restrict__ route_row, int &invalid, int &dropped)
+{
+    const int lane = threadIdx.x & 63;
+    for (long base = b; base < e; base += 64) {
+        const long r = base + lane;
+        const int ex = r < e ? route_local(s, ids[r]) : -1;
+        const Match m = wave_match(ex, ex >= 0);
+        int first = 0;
+        if (ex >= 0 && m.rank == 0)
+            first = atomicAdd(&cnt[ex], m.count);
+        const int leader = ex >= 0 ? __ffsll((long long)m.mask) - 1 : lane;
+        first = __shfl(first, leader);
+        int row = -1;
+        if (ex >= 0) {
+            const int slot = first + m.rank;
+            if (slot < s.capacity)
+                row = ex * s.capacity + slot;
+            else
+                ++dropped;
+        }
+        invalid += ex == -2;
+        if (r < e) {
+            route_row[r] = row;
+            if (row >= 0)
+                row_route[row] = (int32_t)r;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
+                   int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
+                   int32_t *__restrict__ route_row, int32_t *__restrict__ status)
+{
+    extern __shared__ int cnt[]; // [E_local]
+    __shared__ int inv_total, drop_total;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = s.E_local;
+    const long n = (long)s.T * s.K;
+    for (int i = tid; i < E; i += kThreads)
+        cnt[i] = 0;
+    if (tid == 0)
+        inv_total = drop_total = 0;
+    __syncthreads();
+    const long per_wave = (n + kWaves - 1) / kWaves;
+    const long b = min(n, per_wave * wave), e = min(n, b + per_wave);
+    int invalid = 0, dropped = 0;
+    claim_slots<true>(s, ids, b, e, cnt, row_route, route_row, invalid, dropped);
+    invalid = wave_sum(invalid);
+    dropped = wave_sum(dropped);
+    if (lane == 0) {
+        if (invalid)
+            atomicAdd(&inv_total, invalid);
+        if (dropped)
+            atomicAdd(&drop_total, dropped);
+    }
+    __syncthreads();
+    for (int i = tid; i <= E; i += kThreads) {
+        if (i < E)
+            counts[i] = cnt[i];
+        offsets[i] = i * s.capacity;
+    }
+    if (tid == 0) {
+        status[0] = inv_total;
+        status[1] = drop_total;
+        status[2] = status[3] = 0;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+fixed_reset_kernel(Shape s, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                   int32_t *__restrict__ status)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i <= s.E_local; i += gridDim.x * 256) {
+        if (i < s.E_local)
+            counts[i] = 0;
+        offsets[i] = i * s.capacity;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 4)
+        status[threadIdx.x] = 0;
+}
+
+__global__ void __launch_bounds__(kThreads)
+fixed_claim_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
+                   int32_t *__restrict__ row_route, int32_t *__restrict__ route_row,
+                   int32_t *__restrict__ status)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long n = (long)s.T * s.K;
+    const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
+    const long e = min(n, b + kSlotsPerWaveLarge);
+    int invalid = 0, dropped = 0;
+    claim_slots<false>(s, ids, b, e, counts, row_route, route_row, invalid, dropped);
+    invalid = wave_sum(invalid);
+    dropped = wave_sum(dropped);
+    if (lane == 0) {
+        if (invalid)
+            atomicAdd(&status[0], invalid);
+        if (dropped)
+            atomicAdd(&status[1], dropped);
+    }
+}
+
+long num_slots(const moe_shape &s) { return (long)s.T * s.K; }
+
+bool compact_is_small(const moe_shape &s) { return num_slots(s) <= kSmallSlots; }
+
+int large_blocks(const moe_shape &s)
+{
+    return (int)((num_slots(s) + kSlotsPerBlockLarge - 1) / kSlotsPerBlockLarge);
+}
+
+} // namespace
+
+size_t dispatch_scratch_bytes(const moe_shape &s)
+{
+    if (s.dispatch_mode != MOE_DISPATCH_COMPACT || compact_is_small(s))
+        return 0;
+    return (size_t)large_blocks(s) * (size_t)(s.E_local + 1) * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *counts,
+                           int32_t *offsets, int32_t *row_route, int32_t *route_row,
+                           int32_t *status, void *scratch, hipStream_t st)
+{
+    const Shape s = to_dev(sh);
+    const size_t E = (size_t)sh.E_local;
+    if (sh.dispatch_mode == MOE_DISPATCH_COMPACT) {
+        if (compact_is_small(sh)) {
+            compact_small_kernel<<<1, kThreads, kWaves * E * sizeof(int), st>>>(
+                s, ids, counts, offsets, row_route, route_row, status);
+            return hipGetLastError();
+        }
+        const int nblk = large_blocks(sh);
+        int32_t *blk = static_cast<int32_t *>(scratch);
+        compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk);
+        compact_scan_kernel<<<1, kThreads, 0, st>>>(s, nblk, blk, counts, offsets, status);
+        compact_scatter_kernel<<<nblk, kThreads, kWaves * E * sizeof(int), st>>>(
+            s, ids, blk, row_route, route_row);
+        return hipGetLastError();
+    }
+    if (num_slots(sh) <= kSmallSlots) {
+        fixed_small_kernel<<<1, kThreads, E * sizeof(int), st>>>(s, ids, counts, offsets, row_route,
+                                                                  route_row, status);
+        return hipGetLastError();
+    }
+    fixed_reset_kernel<<<(int)((E + 256) / 256), 256, 0, st>>>(s, counts, offsets, status);
+    fixed_claim_kernel<<<large_blocks(sh), kThreads, 0, st>>>(s, ids, counts, row_route, route_row,
+                                                              status);
+    return hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,209 @@
+// Internal declarations shared by the gfx950 kernels of the a8w4 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_a8w4.h"
+
+namespace moe {
+
+constexpr int kMaxLocalExperts = 512;
+
+// Kernel-side copy of moe_shape, passed by value.
+struct Shape {
+    int T, H, I, K;
+    int E_total, expert_begin, E_local;
+    int mode, capacity;
+    float gate_limit, up_limit;
+};
+
+inline Shape to_dev(const moe_shape &s)
+{
+    return Shape{s.T, s.H, s.I, s.K, s.E_total, s.expert_begin, s.E_local,
+                 s.dispatch_mode, s.capacity, s.gate_limit, s.up_limit};
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Route filter: local expert of an id, -1 (pad slot or another GPU's expert)
+// or -2 (id outside [-1, E_total)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int route_local(const Shape &s, int id)
+{
+    if (id == -1)
+        return -1;
+    if ((unsigned)id >= (unsigned)s.E_total)
+        return -2;
+    const int e = id - s.expert_begin;
+    return (unsigned)e < (unsigned)s.E_local ? e : -1;
+}
+
+// Rows of expert e actually held by its segment.
+__device__ __forceinline__ int used_rows(const Shape &s, int count)
+{
+    return s.mode == MOE_DISPATCH_FIXED_SLOT ? min(count, s.capacity) : count;
+}
+
+// ---------------------------------------------------------------------------
+// Scaled MFMA: D(16x16) += A(16x128) * B(128x16) with one E8M0 exponent per
+// 32 K values of every A row and every B column.  Lane l serves row / column
+// (l & 15); with g = l >> 4:
+//   A, MXFP4 (weights): 16 bytes in the low four dwords, K = 32g .. 32g+31,
+//     two values per byte, low nibble first;
+//   B, MXFP8 (activations): bytes 0..15 hold K = 16g .. 16g+15 and bytes
+//     16..31 hold K = 64+16g .. 64+16g+15;
+//   the exponent byte (bits 0..7) of lane l scales K block g (K = 32g ..
+//     32g+31) of its row / column, whichever lanes hold that block's data;
+//   D: lane l holds column (l & 15), rows 4g .. 4g+3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_w4a8(const v8i &a_fp4, const v8i &b_fp8, v4f c, int sa,
+                                         int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp8, c, 4, 0, 0, sa, 0,
+                                                            sb);
+}
+
+// ---------------------------------------------------------------------------
+// e4m3 encode (round to nearest even, saturate at 448) done on the float's
+// bit pattern: the 23-bit mantissa is cut to 3 bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u)
+        return 0x7Fu;                           // NaN
+    if (mag >= 0x43E00000u)                     // |v| >= 448
+        return sign | 0x7Eu;
+    if (mag < 0x3C800000u) {                    // |v| < 2^-6: multiples of 2^-9
+        const float q = __uint_as_float(mag) * 512.0f;   // exact
+        return sign | (uint32_t)__builtin_rintf(q);       // 0..8
+    }
+    uint32_t expo = (mag >> 23) - 120u;         // biased e4m3 exponent, 1..15
+    uint32_t keep = (mag >> 20) & 7u;
+    const uint32_t rest = mag & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
+        ++keep;
+    if (keep == 8u) {
+        keep = 0;
+        ++expo;
+    }
+    const uint32_t code = (expo << 3) | keep;
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// float -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (u + 0x7FFFu + lsb) >> 16;
+}
+
+// Exponent of the 1x32 block: floor(log2(amax)) - 8 clamped to [-127, 127].
+__device__ __forceinline__ int mx8_block_exponent(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;
+    int ex;
+    (void)frexpf(amax, &ex);                    // amax in [2^(ex-1), 2^ex)
+    int E = ex - 1 - 8;
+    return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+__device__ __forceinline__ float swiglu_clamped(float g, float u, float gl, float ul)
+{
+    const float gc = fminf(g, gl);
+    const float uc = fminf(fmaxf(u, -ul), ul);
+    return gc / (1.0f + expf(-gc)) * uc;
+}
+
+// ---------------------------------------------------------------------------
+// Row chunks of the expert segments: every workgroup derives the same plan
+// from counts.  prefix[e] = first chunk of expert e, prefix[E] = total.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict__ counts, int ch,
+                                           int *prefix)
+{
+    // 256 threads, E_local <= 1024: each thread sums up to 4 experts (512 used)
+    const int tid = threadIdx.x;
+    const int E = s.E_local;
+    int local[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        const int n = e < E ? (used_rows(s, counts[e]) + ch - 1) / ch : 0;
+        local[i] = n;
+        sum += n;
+    }
+    // inclusive scan of sum over the 256 threads
+    const int lane = tid & 63, wave = tid >> 6;
+    int inc = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (lane >= d)
+            inc += o;
+    }
+    __shared__ int wtot[4];
+    if (lane == 63)
+        wtot[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w)
+        base += wtot[w];
+    int run = base + inc - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        if (e < E)
+            prefix[e] = run;
+        run += local[i];
+    }
+    if (tid == 255)
+        prefix[E] = base + inc;
+    __syncthreads();
+    return prefix[E];
+}
+
+// Expert owning chunk q: the last e with prefix[e] <= q.
+__device__ __forceinline__ int chunk_expert(const int *prefix, int E, int q)
+{
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= q)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined in the kernel sources).
+// ---------------------------------------------------------------------------
+size_t dispatch_scratch_bytes(const moe_shape &s);
+hipError_t launch_dispatch(const moe_shape &s, const int32_t *ids, int32_t *counts,
+                           int32_t *offsets, int32_t *row_route, int32_t *route_row,
+                           int32_t *status, void *scratch, hipStream_t st);
+hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
+                        const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
+                        const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
+                        hipStream_t st);
+hipError_t launch_gemm2(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
+                        const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
+                        const uint8_t *w2s, float *y, hipStream_t st);
+hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
+                          const float *y, uint16_t *out, hipStream_t st);
+
+int device_cu_count();
+
+} // namespace moe

@@ -1,0 +1,172 @@
+/*
+ * moe_a8w4.h -- C ABI of one GPU's share of an a8w4 MoE expert layer on
+ * MI355X (gfx950).
+ *
+ * The layer ("MegaMoEV2: fuse Dispatch, GEMM1, GEMM2 and Combine into one
+ * kernel", Technical Details; "full-expert DeepSeek V4.1 Flash MegaMoE
+ * tuning", Summary) takes top-k routes (token, expert id, weight), keeps the
+ * routes whose expert this GPU owns, groups them into per-expert row
+ * segments (dispatch), runs each row through its expert -- GEMM1 with the
+ * gate/up weights W13, a clamped SwiGLU, FP8 1x32 requantisation of the
+ * intermediate, GEMM2 with W2 -- and sums each token's routed rows weighted
+ * by its routing weights (combine), skipping -1 slots.
+ *
+ * Formats (all buffers row-major and contiguous):
+ *   FP8   OCP e4m3 (E4M3FN) codes, one byte each.
+ *   MXFP4 OCP E2M1 codes, two per byte, the low nibble holding the even index.
+ *   E8M0  one unsigned exponent byte (value 2^(b-127)) per 32 consecutive
+ *         elements along the contraction dimension (x, h: along H or I;
+ *         W13, W2: along their K).
+ *   BF16  raw 16-bit patterns.
+ *
+ * Buffers (T tokens, K slots per token, E = E_local experts, R = rows):
+ *   x_fp8     [T, H]        x_scale   [T, H/32]
+ *   topk_ids  int32 [T, K]  global expert ids; -1 = no expert
+ *   topk_w    float [T, K]  routing weights (a -1 slot's weight is ignored)
+ *   w13       [E, 2I, H/2]  rows 0..I-1 gate, rows I..2I-1 up
+ *   w13_scale [E, 2I, H/32]
+ *   w2        [E, H, I/2]   w2_scale [E, H, I/32]
+ *   out_bf16  [T, H]
+ * Dispatch results (R = moe_row_capacity(shape)):
+ *   counts    int32 [E]     routes kept for each expert (fixed-slot: routes
+ *                           that asked for a slot, which may exceed capacity)
+ *   offsets   int32 [E+1]   first row of each expert's segment; compact:
+ *                           exclusive scan of counts, offsets[E] = rows used;
+ *                           fixed-slot: e * capacity
+ *   row_route int32 [R]     route slot r = t*K + k held by each row; rows
+ *                           outside every segment's used part are not written
+ *   route_row int32 [T*K]   row of each route slot, or -1 when the slot is
+ *                           -1, not local, invalid or dropped
+ *   status    int32 [4]     [0] ids outside [-1, E_total) (skipped),
+ *                           [1] fixed-slot routes dropped for capacity,
+ *                           [2], [3] zero
+ * Intermediates, indexed by row:
+ *   h_fp8 [R, I], h_scale [R, I/32], y_f32 [R, H] (float32)
+ *
+ * Rows inside a compact segment are in ascending r (a stable scatter);
+ * inside a fixed-slot segment their order is unspecified.
+ *
+ * Ownership: the caller owns every buffer; pointers are device pointers
+ * unless stated.  The library allocates nothing in these calls and keeps no
+ * pointer after a call returns.  All calls are asynchronous on `stream`
+ * (a hipStream_t; NULL is the null stream) and never synchronise, so they
+ * can be captured into a HIP graph.
+ *
+ * Errors: every argument check runs before the first launch; a refused call
+ * returns a negative code and leaves every buffer untouched.  Device-side
+ * anomalies (an id outside [-1, E_total), a fixed-slot overflow) never
+ * fault: the route is skipped and counted in status.
+ */
+#ifndef MOE_A8W4_H
+#define MOE_A8W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* null pointer, negative size, bad enum */
+#define MOE_ENOTSUP (-2)    /* shape outside what the kernels support */
+#define MOE_EWORKSPACE (-3) /* workspace missing or too small */
+#define MOE_EHIP (-4)       /* a HIP launch or query failed */
+
+#define MOE_DISPATCH_COMPACT 0    /* histogram, scan, stable scatter */
+#define MOE_DISPATCH_FIXED_SLOT 1 /* atomic claim into per-expert capacity */
+
+typedef struct moe_shape {
+    int32_t T;             /* source tokens (0 is a valid no-op) */
+    int32_t H;             /* hidden size, a multiple of 128 */
+    int32_t I;             /* expert intermediate size, a multiple of 128 */
+    int32_t K;             /* top-k slots per token, 1..8 */
+    int32_t E_total;       /* experts in the model */
+    int32_t expert_begin;  /* first global id owned here */
+    int32_t E_local;       /* experts owned here, 1..512 */
+    int32_t dispatch_mode; /* MOE_DISPATCH_* */
+    int32_t capacity;      /* fixed-slot rows per expert (>= 1 if fixed-slot) */
+    float gate_limit;      /* gate' = min(gate, gate_limit)            (10) */
+    float up_limit;        /* up'   = clamp(up, -up_limit, up_limit)   (10) */
+} moe_shape;
+
+/* Check a shape; MOE_OK or the code a call with it would return. */
+int moe_check_shape(const moe_shape *shape);
+
+/* Rows of the dispatch buffers: T*K (compact) or E_local*capacity. */
+int64_t moe_row_capacity(const moe_shape *shape);
+
+/* Device scratch bytes moe_dispatch needs (0 for small T). */
+size_t moe_dispatch_workspace_size(const moe_shape *shape);
+
+/* Device scratch bytes moe_forward needs (dispatch results, h, y). */
+size_t moe_workspace_size(const moe_shape *shape);
+
+/*
+ * Dispatch ("AITER MegaMoEV2 ... two dispatch schemes": compact packs the
+ * routes in a prepare pass; fixed-slot writes each route straight into a
+ * per-expert slot).  Reads topk_ids; writes counts, offsets, row_route,
+ * route_row and status.  A slot is local when its id is in
+ * [expert_begin, expert_begin + E_local).  workspace may be NULL when
+ * moe_dispatch_workspace_size() is 0.
+ */
+int moe_dispatch(const moe_shape *shape, const int32_t *topk_ids, int32_t *counts,
+                 int32_t *offsets, int32_t *row_route, int32_t *route_row, int32_t *status,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * GEMM1 + clamped SwiGLU + FP8 1x32 requantisation ("full-expert DeepSeek
+ * V4.1 Flash MegaMoE tuning", Summary: W13, clamp-10 SwiGLU, FP8
+ * intermediate quantisation).  For every used row of every expert segment:
+ *   gu[j] = sum_h x[t,h] * W13[e,j,h], t = row_route[row] / K
+ *   h[i]  = min(gu[i], gate_limit) * sigmoid(min(gu[i], gate_limit))
+ *           * clamp(gu[I+i], -up_limit, up_limit)
+ * then per 32 columns the exponent floor(log2(amax)) - 8 (byte 127 for an
+ * all-zero block) and e4m3 codes rounded to nearest even, saturating at 448.
+ * Writes h_fp8 / h_scale rows of used rows only.
+ */
+int moe_gemm1_swiglu(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
+                     const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
+                     const uint8_t *w13, const uint8_t *w13_scale, uint8_t *h_fp8,
+                     uint8_t *h_scale, void *stream);
+
+/*
+ * GEMM2 (MXFP4 W2): y[row, n] = sum_i h[row,i] * W2[e,n,i] in float32 for
+ * every used row.  Writes y rows of used rows only.  y stays float32: the
+ * combine rounds to bf16 once, after the weighted sum.
+ */
+int moe_gemm2(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_scale,
+              const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
+              const uint8_t *w2_scale, float *y_f32, void *stream);
+
+/*
+ * Combine ("MegaMoEV2 ...": the combine skips invalid (-1) top-k slots;
+ * "route before the rows move": routed contributions summed in f32 and
+ * rounded once).  For every token t:
+ *   out[t,:] = bf16( sum over k = 0..K-1 with route_row[t*K+k] >= 0 of
+ *                    topk_w[t,k] * y_f32[route_row[t*K+k], :] )
+ * in float32, k ascending, each term a product then an add; a token with no
+ * kept route gets +0.
+ */
+int moe_combine(const moe_shape *shape, const float *topk_w, const int32_t *route_row,
+                const float *y_f32, uint16_t *out_bf16, void *stream);
+
+/*
+ * The whole layer: dispatch, GEMM1 + SwiGLU + requant, GEMM2, combine, with
+ * the dispatch results and intermediates in `workspace`
+ * (>= moe_workspace_size(shape) bytes, 256-byte aligned).  Equal to calling
+ * the four steps above in order.
+ */
+int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
+                const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,
+                const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
+                uint16_t *out_bf16, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a return code. */
+const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_A8W4_H */

@@ -199,3 +199,32 @@ def moe_layer(case: dict, tokens: Optional[np.ndarray] = None) -> np.ndarray:
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def gemm2_rows(case: dict, h_codes: np.ndarray, h_scale: np.ndarray,
+               experts: np.ndarray) -> np.ndarray:
+    """float32 y [n, H] of given MX FP8 rows through the given local experts."""
+    spec = case["spec"]
+    s = shape_of(spec)
+    hc = np.ascontiguousarray(h_codes, dtype=np.uint8)
+    hs = np.ascontiguousarray(h_scale, dtype=np.uint8)
+    ex = np.ascontiguousarray(experts, dtype=np.int32)
+    n = ex.size
+    y = np.zeros((max(n, 1), spec.H), np.float32)
+    w2 = np.ascontiguousarray(case["w2"])
+    w2s = np.ascontiguousarray(case["w2_scale"])
+    rc = lib().orc_gemm2_rows(ctypes.byref(s), _p(hc), _p(hs), _p(ex), ctypes.c_int(n), _p(w2),
+                              _p(w2s), _p(y))
+    assert rc == 0
+    return y[:n]
+
+
+def combine(spec, topk_w: np.ndarray, route_row: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """bf16 bits [T, H] of the combine of given float32 rows y [R, H]."""
+    s = shape_of(spec)
+    tw = np.ascontiguousarray(topk_w, dtype=np.float32)
+    rr = np.ascontiguousarray(route_row, dtype=np.int32)
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.zeros((max(spec.T, 1), spec.H), np.uint16)
+    lib().orc_combine(ctypes.byref(s), _p(tw), _p(rr), _p(y), _p(out))
+    return out[:spec.T]

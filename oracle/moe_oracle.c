@@ -404,3 +404,71 @@ ORC_EXPORT int orc_routes_ffn(const orc_shape *s, const uint8_t *x, const uint8_
     }
     return bad ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Single steps on given inputs                                            */
+/* ---------------------------------------------------------------------- */
+
+/* GEMM2 of given MX FP8 rows: row i holds h codes [I] and exponents [I/32]
+ * and belongs to local expert experts[i]; y[i, n] = sum_i' hq * W2[e, n, i']
+ * in float32, ascending i'. */
+ORC_EXPORT int orc_gemm2_rows(const orc_shape *s, const uint8_t *h_codes, const uint8_t *h_scale,
+                              const int32_t *experts, int n, const uint8_t *w2,
+                              const uint8_t *w2s, float *y)
+{
+    const int H = s->H, I = s->I;
+    int r, bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (r = 0; r < n; ++r) {
+        const uint8_t *hc = h_codes + (size_t)r * I;
+        const uint8_t *hs = h_scale + (size_t)r * (I / 32);
+        float *hq = (float *)malloc(sizeof(float) * (size_t)I);
+        int e = experts[r], i, col;
+        if (e < 0 || e >= s->E_local) {
+            bad++;
+            free(hq);
+            continue;
+        }
+        for (i = 0; i < I; ++i)
+            hq[i] = orc_e4m3_decode(hc[i]) * orc_e8m0_decode(hs[i / 32]);
+        for (col = 0; col < H; ++col) {
+            const uint8_t *wr = w2 + ((size_t)e * H + col) * (size_t)(I / 2);
+            const uint8_t *sr = w2s + ((size_t)e * H + col) * (size_t)(I / 32);
+            float acc = 0.0f;
+            for (i = 0; i < I; ++i) {
+                uint8_t byte = wr[i / 2];
+                uint8_t nib = (i & 1) ? (byte >> 4) : (byte & 15);
+                acc = acc + hq[i] * (orc_e2m1_decode(nib) * orc_e8m0_decode(sr[i / 32]));
+            }
+            y[(size_t)r * H + col] = acc;
+        }
+        free(hq);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Combine of given float32 rows y[R, H]: out[t] = bf16(sum over k
+ * ascending with route_row >= 0 of w[t,k] * y[route_row]) in float32. */
+ORC_EXPORT int orc_combine(const orc_shape *s, const float *tw, const int32_t *route_row,
+                           const float *y, uint16_t *out)
+{
+    const int H = s->H, K = s->K;
+    int t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < s->T; ++t) {
+        int n, k;
+        for (n = 0; n < H; ++n) {
+            float o = 0.0f;
+            for (k = 0; k < K; ++k) {
+                int32_t row = route_row[(size_t)t * K + k];
+                float p;
+                if (row < 0)
+                    continue;
+                p = tw[(size_t)t * K + k] * y[(size_t)row * H + n];
+                o = o + p;
+            }
+            out[(size_t)t * H + n] = orc_bf16_encode(o);
+        }
+    }
+    return 0;
+}

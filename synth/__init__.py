@@ -31,7 +31,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["CaseSpec", "CONFIGS", "make_case", "case_names"]
+__all__ = ["CaseSpec", "CONFIGS", "make_case", "make_routing", "case_names",
+           "workload_counts", "algorithmic_work"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -162,6 +163,24 @@ def _quant_x(xf: np.ndarray):
     return codes.numpy().copy(), scale
 
 
+def make_routing(spec: CaseSpec | str, seed: Optional[int] = None, **overrides):
+    """(topk_ids, topk_w) exactly as make_case draws them, without the
+    activations and weights."""
+    if isinstance(spec, str):
+        spec = CONFIGS[spec]
+    if overrides:
+        spec = spec.with_(**overrides)
+    if seed is not None:
+        spec = spec.with_(seed=seed)
+    rng = np.random.Generator(np.random.PCG64(spec.seed))
+    ids, w = _routing(spec, rng)
+    npad = int(round(spec.pad_frac * spec.T * spec.K))
+    if npad:
+        flat = rng.choice(spec.T * spec.K, size=npad, replace=False)
+        ids.reshape(-1)[flat] = -1
+    return spec, ids, w
+
+
 def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> dict:
     """Draw one case.  Returns a dict of numpy arrays plus the spec:
 
@@ -190,6 +209,7 @@ def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> 
     if npad:
         flat = rng.choice(T * K, size=npad, replace=False)
         ids.reshape(-1)[flat] = -1
+    # the draws above are the same as make_routing's
 
     xf = _bf16_round(rng.standard_normal((T, H), dtype=np.float32))
     x_fp8, x_scale = _quant_x(xf)

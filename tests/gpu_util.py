@@ -1,0 +1,126 @@
+"""Helpers of the GPU tests: upload synthetic cases and run the layer's
+steps through the C ABI binding."""
+
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import dispatch_grouped_gemm_amd as moe
+import synth
+
+DEV = torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=2)
+def cached_case(name: str):
+    return synth.make_case(name)
+
+
+def upload(case: dict) -> dict:
+    return {k: dev(v) for k, v in case.items() if isinstance(v, np.ndarray)}
+
+
+def shape_of(spec) -> moe.MoeShape:
+    return moe.MoeShape.of(spec)
+
+
+def run_dispatch(spec, ids_dev: torch.Tensor) -> moe.DispatchBuffers:
+    shape = shape_of(spec)
+    d = moe.alloc_dispatch(shape, DEV)
+    moe.moe_dispatch(shape, ids_dev, d)
+    return d
+
+
+def run_steps(case: dict, g: dict | None = None) -> dict:
+    """All four steps one after the other; returns device tensors."""
+    spec = case["spec"]
+    shape = shape_of(spec)
+    g = g or upload(case)
+    d = run_dispatch(spec, g["topk_ids"])
+    R = max(moe.moe_row_capacity(shape), 1)
+    h = torch.zeros((R, spec.I), dtype=torch.uint8, device=DEV)
+    hs = torch.zeros((R, spec.I // 32), dtype=torch.uint8, device=DEV)
+    y = torch.zeros((R, spec.H), dtype=torch.float32, device=DEV)
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+    moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"], h, hs)
+    moe.moe_gemm2(shape, h, hs, d, g["w2"], g["w2_scale"], y)
+    moe.moe_combine(shape, g["topk_w"], d.route_row, y, out)
+    return dict(d=d, h=h, hs=hs, y=y, out=out)
+
+
+def run_forward(case: dict, g: dict | None = None, ws: torch.Tensor | None = None):
+    spec = case["spec"]
+    shape = shape_of(spec)
+    g = g or upload(case)
+    if ws is None:
+        ws = moe.alloc_workspace(shape, DEV)
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+    moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
+                    g["w13_scale"], g["w2"], g["w2_scale"], out, ws)
+    return out
+
+
+def bf16_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def sample_tokens(case: dict, n_routed: int = 6, n_empty: int = 2) -> np.ndarray:
+    """Tokens spread over the batch: some with local routes, some without."""
+    s = case["spec"]
+    ids = case["topk_ids"]
+    e = ids.astype(np.int64) - s.expert_begin
+    loc = ((ids >= 0) & (ids < s.E_total) & (e >= 0) & (e < s.E_local)).any(axis=1)
+    routed = np.nonzero(loc)[0]
+    empty = np.nonzero(~loc)[0]
+    pick = []
+    if routed.size:
+        pick += list(routed[np.linspace(0, routed.size - 1, min(n_routed, routed.size)).astype(int)])
+    if empty.size:
+        pick += list(empty[np.linspace(0, empty.size - 1, min(n_empty, empty.size)).astype(int)])
+    return np.unique(np.array(pick, dtype=np.int64))
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def assert_layer_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = ""):
+    """Every element within 2e-2 * RMS(ref) of the oracle, except that where
+    one bf16 step of the reference element is larger than that bound the
+    element may differ by that one step (two float32 sums of the same terms
+    in different orders can round to neighbouring bf16 values).  An all-zero
+    reference demands exact zeros.  Returns max|err| / RMS (literal)."""
+    got = bf16_f64(got_bits)
+    ref = bf16_f64(ref_bits)
+    rms = float(np.sqrt((ref ** 2).mean())) if ref.size else 0.0
+    if rms == 0.0:
+        assert not np.any(got), what + ": reference is zero, output is not"
+        return 0.0
+    err = np.abs(got - ref)
+    allowed = np.maximum(2e-2 * rms, bf16_ulp(ref))
+    bad = err > allowed
+    lit = float(err.max()) / rms
+    say("%s: %d of %d elements differ, max|err|/RMS %.4g, RMS %.4g, over the bar %d" % (
+        what, int((got != ref).sum()), got.size, lit, rms, int(bad.sum())))
+    assert not bad.any(), "%s: %d elements beyond max(2e-2 * RMS, 1 bf16 step), worst %.4g * RMS" % (
+        what, int(bad.sum()), float((err - allowed).max() + 2e-2 * rms) / rms)
+    return lit

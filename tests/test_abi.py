@@ -1,0 +1,89 @@
+"""The C ABI library loads, exports every declared entry point, and refuses
+bad arguments before touching a GPU (these tests run without one)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dispatch_grouped_gemm_amd as moe
+from dispatch_grouped_gemm_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_a8w4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _build.build(force=False)
+    return moe.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.EXPORTED)
+
+
+V4 = dict(T=128, H=7168, I=3072, K=6, E_total=384, E_local=48)
+
+
+def test_shape_checks(lib):
+    ok = moe.MoeShape(**V4)
+    assert moe.moe_check_shape(ok) == 0
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "T": 0})) == 0
+    bad = [
+        ({"T": -1}, -1), ({"K": 0}, -1), ({"E_local": 0}, -1), ({"H": 0}, -1),
+        ({"expert_begin": 380}, -1), ({"dispatch_mode": 3}, -1),
+        ({"dispatch_mode": 1, "capacity": 0}, -1), ({"K": 9}, -2), ({"H": 7168 + 64}, -2),
+        ({"I": 3072 + 32}, -2), ({"E_local": 513, "E_total": 1024}, -2),
+        ({"gate_limit": float("nan")}, -1),
+    ]
+    for kw, code in bad:
+        assert moe.moe_check_shape(moe.MoeShape(**{**V4, **kw})) == code, kw
+
+
+def test_sizes(lib):
+    s = moe.MoeShape(**V4, dispatch_mode=1, capacity=128)
+    assert moe.moe_row_capacity(s) == 48 * 128
+    c = moe.MoeShape(**V4)
+    assert moe.moe_row_capacity(c) == 128 * 6
+    assert moe.moe_dispatch_workspace_size(c) == 0
+    big = moe.MoeShape(**{**V4, "T": 65536})
+    assert moe.moe_dispatch_workspace_size(big) > 0
+    R = 128 * 6
+    assert moe.moe_workspace_size(c) >= R * (3072 + 96 + 2 * 7168)
+    assert moe.moe_workspace_size(moe.MoeShape(**{**V4, "K": 0})) == 0
+
+
+def test_refusals_return_before_any_launch(lib):
+    c = moe.MoeShape(**V4).c()
+    bad = moe.MoeShape(**{**V4, "K": 0}).c()
+    null = None
+    # bad shape
+    assert lib.moe_dispatch(ctypes.byref(bad), *([null] * 7), 0, null) == -1
+    assert lib.moe_forward(ctypes.byref(bad), *([null] * 10), 0, null) == -1
+    # null buffers with a good shape
+    assert lib.moe_dispatch(ctypes.byref(c), *([null] * 7), 0, null) == -1
+    assert lib.moe_gemm1_swiglu(ctypes.byref(c), *([null] * 9), null) == -1
+    assert lib.moe_gemm2(ctypes.byref(c), *([null] * 7), null) == -1
+    assert lib.moe_combine(ctypes.byref(c), *([null] * 4), null) == -1
+    assert lib.moe_forward(ctypes.byref(c), *([null] * 10), 0, null) == -1
+    # a workspace that is too small is refused (pointers are never touched)
+    fake = ctypes.c_void_p(256)
+    args = [fake] * 9
+    assert lib.moe_forward(ctypes.byref(c), *args, fake, 16, null) == -3
+    # T = 0 is a no-op for the steps that have nothing to do
+    z = moe.MoeShape(**{**V4, "T": 0}).c()
+    assert lib.moe_forward(ctypes.byref(z), *([null] * 10), 0, null) == 0
+    assert lib.moe_combine(ctypes.byref(z), *([null] * 4), null) == 0
+    assert moe.moe_strerror(-3).startswith("workspace")

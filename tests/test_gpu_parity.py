@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Dispatch is compared bit-exactly (compact: counts, offsets, row order,
+route_row; fixed-slot: counts, offsets, the set of routes in each expert's
+segment).  GEMM1 + SwiGLU + requant is compared code by code (a float32 sum
+in another order may move a value across an e4m3 rounding boundary: such
+flips must be single steps and rare).  GEMM2 is compared to the oracle's
+float32 rows, the difference bounded by the magnitudes of the summed terms.
+Combine is bit-exact given the same y.  The whole layer must be within
+2e-2 * RMS(oracle) of the oracle element by element, or one bf16 step of the
+element where that step is larger, on every workload (all tokens of the
+small one; a spread sample of tokens on the full sizes, each of which the
+oracle computes on its own).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dispatch_grouped_gemm_amd as moe
+import oracle
+import synth
+from gpu_util import (DEV, assert_layer_close, bf16_f64, cached_case, dev, host, run_dispatch,
+                      run_forward, run_steps, say, sample_tokens, shape_of, upload)
+
+pytestmark = pytest.mark.gpu
+
+ALL = list(synth.CONFIGS)
+BIG = [n for n in ALL if n != "tiny"]
+
+
+def check_dispatch(spec, ids: np.ndarray, d):
+    ref = oracle.dispatch(spec, ids)
+    counts, offsets, status = host(d.counts), host(d.offsets), host(d.status)
+    np.testing.assert_array_equal(counts, ref["counts"])
+    np.testing.assert_array_equal(offsets, ref["offsets"])
+    np.testing.assert_array_equal(status, ref["status"])
+    rr = host(d.route_row)[:spec.T * spec.K]
+    row_route = host(d.row_route)
+    if spec.dispatch_mode == 0:
+        total = int(offsets[-1])
+        np.testing.assert_array_equal(row_route[:total], ref["row_route"][:total])
+        np.testing.assert_array_equal(rr, ref["route_row"])
+    else:
+        C = spec.capacity
+        for e in range(spec.E_local):
+            kept = min(int(counts[e]), C)
+            seg = row_route[e * C:e * C + kept]
+            refseg = ref["row_route"][e * C:e * C + kept]
+            if counts[e] <= C:
+                np.testing.assert_array_equal(np.sort(seg), np.sort(refseg))
+            else:
+                assert len(set(seg.tolist())) == kept
+            assert (row_route[e * C + kept:(e + 1) * C] == -1).all()  # untouched
+        kept_r = np.nonzero(rr >= 0)[0]
+        np.testing.assert_array_equal(row_route[rr[kept_r]], kept_r)
+        assert ((rr >= 0) == (ref["route_row"] >= 0)).all() or status[1] > 0
+    return ref
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_dispatch_matches_oracle(name):
+    spec, ids, _ = synth.make_routing(name)
+    say("dispatch", name, spec.T, spec.dispatch_mode)
+    d = run_dispatch(spec, dev(ids))
+    torch.cuda.synchronize()
+    check_dispatch(spec, ids, d)
+    if spec.dispatch_mode == 1:
+        # the same routes in compact mode
+        c = spec.with_(dispatch_mode=0)
+        d2 = run_dispatch(c, dev(ids))
+        torch.cuda.synchronize()
+        check_dispatch(c, ids, d2)
+
+
+def _edge_ids(rng, T, K, E_total):
+    ids = rng.integers(0, E_total, size=(T, K)).astype(np.int32)
+    m = rng.random((T, K))
+    ids[m < 0.10] = -1
+    ids[(m >= 0.10) & (m < 0.12)] = E_total + 5
+    ids[(m >= 0.12) & (m < 0.13)] = -9
+    return ids
+
+
+@pytest.mark.parametrize("T", [0, 1, 5, 700, 5000])
+@pytest.mark.parametrize("mode,cap", [(0, 0), (1, 3), (1, 64)])
+def test_dispatch_edges(T, mode, cap):
+    rng = np.random.default_rng(T * 7 + cap)
+    spec = synth.CaseSpec("edge", T=T, H=512, I=256, E_total=40, E_local=9, expert_begin=5,
+                          K=8, dispatch_mode=mode, capacity=cap)
+    ids = _edge_ids(rng, T, 8, 40)
+    say("dispatch edge", T, mode, cap)
+    d = run_dispatch(spec, dev(ids) if T else torch.zeros((0, 8), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    check_dispatch(spec, ids, d)
+
+
+def test_dispatch_single_hot_expert_large():
+    T, K = 9000, 6
+    spec = synth.CaseSpec("hot", T=T, H=512, I=256, E_total=64, E_local=16, K=K)
+    ids = np.full((T, K), 40, np.int32)
+    ids[:, 3] = 2
+    say("dispatch hot")
+    d = run_dispatch(spec, dev(ids))
+    torch.cuda.synchronize()
+    check_dispatch(spec, ids, d)
+    assert host(d.counts)[2] == T
+
+
+# ------------------------------------------------------------ single steps ----
+
+def _gemm1_compare(case, steps, rows_to_check=None):
+    spec = case["spec"]
+    d = steps["d"]
+    rr = host(d.route_row)
+    routes = np.nonzero(rr >= 0)[0]
+    if rows_to_check is not None:
+        routes = routes[np.isin(routes // spec.K, rows_to_check)]
+    ref = oracle.routes_ffn(case, routes)
+    rows = rr[routes]
+    h = host(steps["h"])[rows]
+    hs = host(steps["hs"])[rows]
+    # decoded values: e4m3 code * 2^(scale-127)
+    lut = np.array([oracle.e4m3_decode(c) for c in range(256)], np.float64)
+    got = lut[h] * np.exp2(np.repeat(hs.astype(np.float64) - 127, 32, axis=1))
+    want = lut[ref["h_codes"]] * np.exp2(np.repeat(ref["h_scale"].astype(np.float64) - 127, 32,
+                                                   axis=1))
+    diff = got != want
+    n = diff.sum()
+    # a flip is one e4m3 step: at most 1/8 of the larger magnitude (or a
+    # subnormal step of the block)
+    step = np.maximum(np.abs(got), np.abs(want)) / 8 + np.exp2(
+        np.repeat(hs.astype(np.float64) - 127 - 9, 32, axis=1))
+    assert (np.abs(got - want)[diff] <= step[diff] * 1.0001).all()
+    assert n <= max(3, 0.005 * got.size), (n, got.size)
+    return ref, routes, rows
+
+
+def test_gemm1_tiny_every_row():
+    case = cached_case("tiny")
+    say("gemm1 tiny")
+    steps = run_steps(case)
+    torch.cuda.synchronize()
+    _gemm1_compare(case, steps)
+
+
+def test_gemm2_tiny_given_h():
+    case = cached_case("tiny")
+    spec = case["spec"]
+    g = upload(case)
+    d = run_dispatch(spec, g["topk_ids"])
+    shape = shape_of(spec)
+    R = moe.moe_row_capacity(shape)
+    rng = np.random.default_rng(5)
+    # synthetic MX FP8 rows: normal finite codes (exponent field 1..15, not
+    # NaN), exponents around the real ones
+    codes = rng.integers(0, 256, size=(R, spec.I), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    codes[(codes & 0x78) == 0] |= 0x08
+    scales = rng.integers(116, 122, size=(R, spec.I // 32), dtype=np.uint8)
+    y = torch.zeros((R, spec.H), dtype=torch.float32, device=DEV)
+    say("gemm2 tiny")
+    moe.moe_gemm2(shape, dev(codes), dev(scales), d, g["w2"], g["w2_scale"], y)
+    torch.cuda.synchronize()
+    counts, offsets = host(d.counts), host(d.offsets)
+    rows = np.concatenate([np.arange(offsets[e], offsets[e] + counts[e])
+                           for e in range(spec.E_local)])
+    experts = np.concatenate([np.full(counts[e], e) for e in range(spec.E_local)])
+    ref = oracle.gemm2_rows(case, codes[rows], scales[rows], experts)
+    got = host(y)[rows].astype(np.float64)
+    # inside one 32-value K block the scaled MFMA aligns its products to the
+    # largest one and keeps about 14 bits below it (448 + 2^-4 is exact,
+    # 448 + 2^-6 is not); across blocks and into the accumulator it rounds
+    # like float32.  Bound the difference by 2^-12 of the summed magnitudes.
+    from dense_ref import dec_fp4_rows, dec_fp8_rows
+    hq = dec_fp8_rows(codes[rows], scales[rows])
+    mag = np.stack([np.abs(hq[i]) @ np.abs(dec_fp4_rows(case["w2"][e], case["w2_scale"][e])).T
+                    for i, e in enumerate(experts)])
+    ratio = np.abs(got - ref) / mag
+    say("gemm2 max |diff| / sum|terms| = %.3g" % ratio.max())
+    assert ratio.max() <= 2.0 ** -12
+
+
+@pytest.mark.parametrize("name", ["tiny", "v4_decode_t128_fixed"])
+def test_combine_bit_exact_given_y(name):
+    spec, ids, w = synth.make_routing(name)
+    shape = shape_of(spec)
+    d = run_dispatch(spec, dev(ids))
+    R = moe.moe_row_capacity(shape)
+    rng = np.random.default_rng(9)
+    yv = rng.standard_normal((R, spec.H)).astype(np.float32) * 40
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+    say("combine", name)
+    moe.moe_combine(shape, dev(w), d.route_row, dev(yv), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(spec, w, host(d.route_row), yv)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+# --------------------------------------------------------------- the layer ----
+
+def test_forward_tiny_every_token_and_variants():
+    case = cached_case("tiny")
+    say("forward tiny")
+    g = upload(case)
+    out = host(run_forward(case, g))
+    ref = oracle.moe_layer(case)
+    r = assert_layer_close(out, ref, "tiny")
+    say("tiny max|err|/RMS", r)
+    # the four steps called one by one give the same bits
+    steps = run_steps(case, g)
+    np.testing.assert_array_equal(host(steps["out"]), out)
+    # fixed-slot gives the same bits as compact
+    fixed = dict(case)
+    fixed["spec"] = case["spec"].with_(dispatch_mode=1, capacity=16)
+    np.testing.assert_array_equal(host(run_forward(fixed, g)), out)
+    # deterministic
+    np.testing.assert_array_equal(host(run_forward(case, g)), out)
+
+
+def test_forward_tiny_in_a_graph():
+    case = cached_case("tiny")
+    spec = case["spec"]
+    shape = shape_of(spec)
+    g = upload(case)
+    ws = moe.alloc_workspace(shape, DEV)
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+    eager = host(run_forward(case, g, ws))
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture tiny")
+    with torch.cuda.graph(graph, stream=stream):
+        moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
+                        g["w13_scale"], g["w2"], g["w2_scale"], out, ws,
+                        stream=torch.cuda.current_stream())
+    for i in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), eager)
+        _ = host(run_forward(case, g))  # eager work between replays
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_forward_full_size_sampled(name):
+    case = cached_case(name)
+    spec = case["spec"]
+    say("forward", name, "T", spec.T)
+    out = host(run_forward(case))
+    torch.cuda.synchronize()
+    d = run_dispatch(spec, dev(case["topk_ids"]))
+    torch.cuda.synchronize()
+    status = host(d.status)
+    assert status[0] == 0 and status[1] == 0
+    tok = sample_tokens(case)
+    ref = oracle.moe_layer(case, tok)
+    r = assert_layer_close(out[tok], ref, name)
+    say(name, "sampled tokens", tok.size, "max|err|/RMS", r)
+    # tokens with no local route are exactly +0
+    e = case["topk_ids"].astype(np.int64) - spec.expert_begin
+    loc = ((case["topk_ids"] >= 0) & (e >= 0) & (e < spec.E_local)).any(axis=1)
+    assert not out[~loc].any()
+
+
+def test_forward_edges():
+    base = cached_case("tiny")
+    spec = base["spec"]
+    g = upload(base)
+    # every slot -1: exact zeros, whatever the weights
+    c = dict(base)
+    c["topk_ids"] = np.full_like(base["topk_ids"], -1)
+    gg = dict(g, topk_ids=dev(c["topk_ids"]))
+    say("forward all pad")
+    assert not host(run_forward(c, gg)).any()
+    # ids outside [0, E_total), foreign experts and duplicates
+    rng = np.random.default_rng(3)
+    ids = base["topk_ids"].copy()
+    ids[rng.random(ids.shape) < 0.1] = spec.E_total + 7
+    ids[:, 1] = ids[:, 0]
+    c = dict(base, topk_ids=ids)
+    gg = dict(g, topk_ids=dev(ids))
+    say("forward invalid ids")
+    out = host(run_forward(c, gg))
+    assert_layer_close(out, oracle.moe_layer(c), "edges")
+    # a single token
+    c1 = {k: (v[:1] if k in ("x_fp8", "x_scale", "topk_ids", "topk_w") else v)
+          for k, v in base.items()}
+    c1["spec"] = spec.with_(T=1)
+    say("forward T=1")
+    assert_layer_close(host(run_forward(c1)), oracle.moe_layer(c1), "T=1")
+    # T = 0 returns at once
+    c0 = {k: (v[:0] if k in ("x_fp8", "x_scale", "topk_ids", "topk_w") else v)
+          for k, v in base.items()}
+    c0["spec"] = spec.with_(T=0)
+    assert run_forward(c0).numel() == 0
