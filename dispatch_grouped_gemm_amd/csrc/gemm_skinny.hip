@@ -3,6 +3,9 @@
 // weight fragment is applied to all rows of a chunk (up to 16*NMB rows)
 // while it is in registers.
 //
+// The E8M0 exponents of an item's weight and activation rows are copied to
+// LDS once per item (coalesced dword loads); the K loop reads them there.
+//
 // Work items are (row chunk of one expert, N tile); a workgroup of four
 // wavefronts takes items in a grid-stride loop.  The four wavefronts split
 // the K steps of an item (wavefront w takes K steps w, w+4, ...), so their
@@ -37,6 +40,21 @@ __device__ __forceinline__ v8i load_fp8_frag(const uint8_t *p)
     const uint4 hi = *reinterpret_cast<const uint4 *>(p + 64);
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Copy the E8M0 exponent rows of one item into LDS (row stride `stride`
+// bytes, `nbytes` used bytes per row, a multiple of 4): rows [0, nrows)
+// come from src_rows(r); the workgroup shares the copy.
+template <typename RowFn>
+__device__ __forceinline__ void stage_exponents(uint8_t *dst, int stride, int nbytes, int nrows,
+                                                RowFn src_row)
+{
+    const int words = nbytes >> 2;
+    for (int i = threadIdx.x; i < nrows * words; i += kThreads) {
+        const int r = i / words, c = i - r * words;
+        const uint32_t v = reinterpret_cast<const uint32_t *>(src_row(r))[c];
+        *reinterpret_cast<uint32_t *>(dst + r * stride + 4 * c) = v;
+    }
 }
 
 // Sum the four wavefronts' accumulators in LDS: red[(mb*4 + g)*4 + v][lane].
@@ -75,9 +93,12 @@ gemm1_skinny_kernel(Shape s, const uint8_t *__restrict__ x, const uint8_t *__res
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int tok[CH];
     __shared__ float red[NMB * 4 * 4 * 64];
+    extern __shared__ uint8_t exps[]; // [64 weight rows + CH x rows][H/32 + 4]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = H / 128;
+    const int es = H / 32 + 4;
+    uint8_t *wexp = exps, *xexp = exps + 64 * es;
     const int nchunks = plan_chunks(s, counts, CH, prefix);
     const int NT = I / 32;
     const long items = (long)nchunks * NT;
@@ -90,26 +111,36 @@ gemm1_skinny_kernel(Shape s, const uint8_t *__restrict__ x, const uint8_t *__res
         const int row0 = offsets[e] + c * CH;
         const int nrows = min(CH, rows_e - c * CH);
         const int nmb_act = (nrows + 15) >> 4;
+        const int j0 = nt * 32;
         if (tid < CH)
             tok[tid] = tid < nrows ? row_route[row0 + tid] / s.K : 0;
+        // W13 rows of the tile: r in [0, 64) is gate/up group r/16, row r%16
+        stage_exponents(wexp, es, H / 32, 64, [&](int r) {
+            const int g = r >> 4;
+            const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + (r & 15);
+            return w13s + wrow * (size_t)(H / 32);
+        });
+        stage_exponents(xexp, es, H / 32, nrows, [&](int r) {
+            return xs + (size_t)(row_route[row0 + r] / s.K) * (size_t)(H / 32);
+        });
         __syncthreads();
 
-        const int j0 = nt * 32;
         const uint8_t *wp[4];
         const uint8_t *wsp[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + i16;
             wp[g] = w13 + wrow * (size_t)(H / 2) + kq * 16;
-            wsp[g] = w13s + wrow * (size_t)(H / 32) + kq;
+            wsp[g] = wexp + (g * 16 + i16) * es + kq;
         }
         const uint8_t *xp[NMB];
         const uint8_t *xsp[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            const size_t t = (size_t)tok[mb * 16 + i16];
+            const int rloc = min(mb * 16 + i16, nrows - 1);
+            const size_t t = (size_t)tok[rloc];
             xp[mb] = x + t * (size_t)H + kq * 16;
-            xsp[mb] = xs + t * (size_t)(H / 32) + kq;
+            xsp[mb] = xexp + rloc * es + kq;
         }
 
         v4f acc[NMB][4];
@@ -189,9 +220,12 @@ gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__res
     constexpr int CH = 16 * NMB;
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ float red[NMB * 4 * 4 * 64];
+    extern __shared__ uint8_t exps[]; // [64 weight rows + CH h rows][I/32 + 4]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = I / 128;
+    const int es = I / 32 + 4;
+    uint8_t *wexp = exps, *hexp = exps + 64 * es;
     const int nchunks = plan_chunks(s, counts, CH, prefix);
     const int NT = H / 64;
     const long items = (long)nchunks * NT;
@@ -205,6 +239,13 @@ gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__res
         const int nrows = min(CH, rows_e - c * CH);
         const int nmb_act = (nrows + 15) >> 4;
         const int n0 = nt * 64;
+        stage_exponents(wexp, es, I / 32, 64, [&](int r) {
+            return w2s + ((size_t)e * H + n0 + r) * (size_t)(I / 32);
+        });
+        stage_exponents(hexp, es, I / 32, nrows, [&](int r) {
+            return hs + (size_t)(row0 + r) * (size_t)(I / 32);
+        });
+        __syncthreads();
 
         const uint8_t *wp[4];
         const uint8_t *wsp[4];
@@ -212,7 +253,7 @@ gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__res
         for (int g = 0; g < 4; ++g) {
             const size_t wrow = (size_t)e * H + n0 + 16 * g + i16;
             wp[g] = w2 + wrow * (size_t)(I / 2) + kq * 16;
-            wsp[g] = w2s + wrow * (size_t)(I / 32) + kq;
+            wsp[g] = wexp + (16 * g + i16) * es + kq;
         }
         const uint8_t *hp[NMB];
         const uint8_t *hsp[NMB];
@@ -221,7 +262,7 @@ gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__res
             const int rloc = min(mb * 16 + i16, nrows - 1);
             const size_t row = (size_t)(row0 + rloc);
             hp[mb] = h + row * (size_t)I + kq * 16;
-            hsp[mb] = hs + row * (size_t)(I / 32) + kq;
+            hsp[mb] = hexp + rloc * es + kq;
         }
 
         v4f acc[NMB][4];
@@ -272,10 +313,11 @@ gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__res
 int g_cu_count = 0;
 
 template <typename KernelT>
-int grid_for(KernelT kernel, long upper_items)
+int grid_for(KernelT kernel, long upper_items, size_t dyn_lds)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, dyn_lds) !=
+            hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     long g = (long)device_cu_count() * per_cu;
@@ -331,8 +373,9 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
 #define MOE_LAUNCH_G1(N)                                                                          \
     do {                                                                                          \
         auto k = gemm1_skinny_kernel<N>;                                                          \
-        const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt);                         \
-        k<<<grid, kThreads, 0, st>>>(s, x, xs, counts, offsets, row_route, w13, w13s, h, hs);     \
+        const size_t lds = (size_t)(64 + 16 * N) * (sh.H / 32 + 4);                               \
+        const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
+        k<<<grid, kThreads, lds, st>>>(s, x, xs, counts, offsets, row_route, w13, w13s, h, hs);   \
     } while (0)
     if (nmb == 1)
         MOE_LAUNCH_G1(1);
@@ -354,8 +397,9 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
 #define MOE_LAUNCH_G2(N)                                                                          \
     do {                                                                                          \
         auto k = gemm2_skinny_kernel<N>;                                                          \
-        const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt);                         \
-        k<<<grid, kThreads, 0, st>>>(s, h, hs, counts, offsets, w2, w2s, y);                      \
+        const size_t lds = (size_t)(64 + 16 * N) * (sh.I / 32 + 4);                               \
+        const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
+        k<<<grid, kThreads, lds, st>>>(s, h, hs, counts, offsets, w2, w2s, y);                    \
     } while (0)
     if (nmb == 1)
         MOE_LAUNCH_G2(1);
