@@ -335,6 +335,17 @@ long chunk_upper_bound(const moe_shape &s, int ch)
     return rows / ch + s.E_local;
 }
 
+// Expected rows per local expert under uniform routing; the kernel family is
+// chosen from this host-known figure only, never from device data.
+double rows_per_expert(const moe_shape &s)
+{
+    return (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+}
+
+bool use_tiled_gemm1(const moe_shape &s) { return rows_per_expert(s) > 24.0; }
+
+bool use_tiled_gemm2(const moe_shape &s) { return rows_per_expert(s) > 24.0 && s.H % 256 == 0; }
+
 // Rows per chunk: enough for the expected rows of an expert, at most 64.
 int pick_nmb(const moe_shape &s)
 {
@@ -367,6 +378,8 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
                         const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
                         hipStream_t st)
 {
+    if (use_tiled_gemm1(sh))
+        return launch_gemm1_tiled(sh, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
     const Shape s = to_dev(sh);
     const int nmb = pick_nmb(sh);
     const long nt = sh.I / 32;
@@ -391,6 +404,8 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                         const uint8_t *w2s, float *y, hipStream_t st)
 {
+    if (use_tiled_gemm2(sh))
+        return launch_gemm2_tiled(sh, h, hs, counts, offsets, w2, w2s, y, st);
     const Shape s = to_dev(sh);
     const int nmb = pick_nmb(sh);
     const long nt = sh.H / 64;

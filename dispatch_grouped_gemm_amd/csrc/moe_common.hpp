@@ -201,6 +201,14 @@ hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
 hipError_t launch_gemm2(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                         const uint8_t *w2s, float *y, hipStream_t st);
+int tiled_bm(const moe_shape &s);
+hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *row_route, const uint8_t *w13, const uint8_t *w13s,
+                              uint8_t *h, uint8_t *hs, hipStream_t st);
+hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
+                              const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
+                              const uint8_t *w2s, float *y, hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
                           const float *y, uint16_t *out, hipStream_t st);
 
