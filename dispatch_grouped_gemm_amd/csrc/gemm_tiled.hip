@@ -34,6 +34,13 @@ struct TileLds {
     static constexpr int kWE = kBN * 4;   // weight exponents (4 blocks per row)
     static constexpr int kXE = BM * 4;    // activation exponents
     static constexpr int kStage = kW + kX + kWE + kXE;
+    static constexpr int kStages = 3;     // K steps resident in LDS
+    // loads one wavefront issues per stage: 4 weight fragments, BM/32
+    // activation fragment halves, one weight-exponent and one activation-
+    // exponent dword load (wavefront v brings activation exponent rows
+    // 64 (v mod BM/64) + l: when BM < 256 two wavefronts write the same
+    // bytes to the same place)
+    static constexpr int kLoads = 4 + BM / 32 + 2;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -43,96 +50,47 @@ __device__ __forceinline__ u32x4 lds_read16(const uint8_t *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-// Global loads of one K step of the tile into registers.
-template <int WPT, int XPT>
-__device__ __forceinline__ void tile_gload(u32x4 (&wreg)[WPT], u32x4 (&xreg)[XPT], uint32_t &wereg,
-                                           uint32_t &xereg, const uint8_t *w,
-                                           const uint32_t (&woff)[WPT], const uint8_t *x,
-                                           const uint32_t (&xoff)[XPT], const uint8_t *we,
-                                           uint32_t weoff, const uint8_t *xe, uint32_t xeoff,
-                                           int ks, bool has_xe)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
 {
-#pragma unroll
-    for (int i = 0; i < WPT; ++i)
-        wreg[i] = *reinterpret_cast<const u32x4 *>(w + (woff[i] + (uint32_t)ks * 64u));
-#pragma unroll
-    for (int i = 0; i < XPT; ++i)
-        xreg[i] = *reinterpret_cast<const u32x4 *>(x + (xoff[i] + (uint32_t)ks * 128u));
-    wereg = *reinterpret_cast<const uint32_t *>(we + (weoff + (uint32_t)ks * 4u));
-    if (has_xe)
-        xereg = *reinterpret_cast<const uint32_t *>(xe + (xeoff + (uint32_t)ks * 4u));
+    return (uint32_t)(uintptr_t)(lds_u8 *)p;
 }
 
-// The registers of one K step into an LDS stage (fragment order).
-// LDS slot of weight piece p = tid + 256 i (tile row p/4, chunk p%4) and of
-// activation piece p (tile row p/8, chunk p%8), in MFMA fragment order.
-__device__ __forceinline__ int wpiece_slot(int p)
+// global -> LDS without registers: lane l's SIZE bytes from base + voff land
+// at LDS address m0 + SIZE * l (m0 is wavefront-uniform).  Issued as inline
+// assembly so that the waits are exactly the ones this file writes: the
+// loads count in vmcnt like any vector memory load.  An LDS DMA reads m0 one
+// wait state after an SALU write of m0 at the earliest, hence the s_nop.
+template <int SIZE>
+__device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
 {
-    const int r = p >> 2, ch = p & 3;
-    return ((r >> 4) * 64 + (r & 15) + 16 * ch) * 16;
+    static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
+    if (SIZE == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
+                     "v"(voff), "s"(base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0),
+                     "v"(voff), "s"(base)
+                     : "memory", "m0");
 }
 
-__device__ __forceinline__ int xpiece_slot(int p)
+// The workgroup barrier without the memory fence __syncthreads() adds (that
+// fence would wait for every outstanding load, prefetches included).
+__device__ __forceinline__ void raw_barrier()
 {
-    const int r = p >> 3, ch = p & 7;
-    return (((r >> 4) * 2 + (ch >> 2)) * 64 + (r & 15) + 16 * (ch & 3)) * 16;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int WPT, int XPT>
-__device__ __forceinline__ void tile_lstore(uint8_t *st, const u32x4 (&wreg)[WPT],
-                                            const u32x4 (&xreg)[XPT], uint32_t wereg,
-                                            uint32_t xereg, int x_off, int we_off, int xe_off,
-                                            int tid, bool has_xe)
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-#pragma unroll
-    for (int i = 0; i < WPT; ++i)
-        *reinterpret_cast<u32x4 *>(st + wpiece_slot(tid + 256 * i)) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < XPT; ++i)
-        *reinterpret_cast<u32x4 *>(st + x_off + xpiece_slot(tid + 256 * i)) = xreg[i];
-    *reinterpret_cast<uint32_t *>(st + we_off + 4 * tid) = wereg;
-    if (has_xe)
-        *reinterpret_cast<uint32_t *>(st + xe_off + 4 * tid) = xereg;
-}
-
-// One K step from LDS stage BUF: the next step's global loads are issued
-// first, the MFMAs run, then the next step goes to the other stage.
-template <int BUF, int TB, int WPT, int XPT, int STAGE>
-__device__ __forceinline__ void
-tile_step(v4f (&acc)[8][TB], uint8_t *lds, int ks, int KS, int afrag, int bfrag, int wexp,
-          int xexp, u32x4 (&wreg)[WPT], u32x4 (&xreg)[XPT], uint32_t &wereg, uint32_t &xereg,
-          const uint8_t *w, const uint32_t (&woff)[WPT], const uint8_t *x,
-          const uint32_t (&xoff)[XPT], const uint8_t *we, uint32_t weoff, const uint8_t *xe,
-          uint32_t xeoff, int x_off, int we_off, int xe_off, int tid, bool has_xe)
-{
-    const bool more = ks + 1 < KS;
-    if (more)
-        tile_gload<WPT, XPT>(wreg, xreg, wereg, xereg, w, woff, x, xoff, we, weoff, xe, xeoff,
-                             ks + 1, has_xe);
-    const uint8_t *st = lds + BUF * STAGE;
-    v8i b[TB];
-    int sb[TB];
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-        const u32x4 lo = lds_read16(st + bfrag + j * 2048);
-        const u32x4 hi = lds_read16(st + bfrag + j * 2048 + 1024);
-        b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sb[j] = st[xexp + j * 64];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const u32x4 a4 = lds_read16(st + afrag + i * 1024);
-        const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-        const int sa = st[wexp + i * 64];
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-            acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
-    }
-    if (more)
-        tile_lstore<WPT, XPT>(lds + (BUF ^ 1) * STAGE, wreg, xreg, wereg, xereg, x_off, we_off,
-                              xe_off, tid, has_xe);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 template <bool kGemm1, int BM>
@@ -145,9 +103,8 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
 {
     using L = TileLds<BM>;
     constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
-    constexpr int WPT = kBN * 4 / kThreads; // 16-byte weight pieces per thread and K step
-    constexpr int XPT = BM * 8 / kThreads;  // 16-byte activation pieces per thread
-    __shared__ __align__(16) uint8_t lds[2 * L::kStage];
+    constexpr int NS = L::kStages;
+    __shared__ __align__(16) uint8_t lds[NS * L::kStage];
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int arow[BM];                // activation row of each tile row
 
@@ -173,7 +130,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         }
         __syncthreads();
 
-        // byte offsets of this thread's pieces (all buffers are below 4 GiB)
+        // weight row (within the expert's rows of W) of tile row r
         auto wrow_of = [&](int r) -> uint32_t {
             const int grp = r >> 4, rr = r & 15;
             if (kGemm1) {
@@ -183,22 +140,45 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             }
             return (uint32_t)(e * H + nt * kBN + r);
         };
-        uint32_t woff[WPT], xoff[XPT];
+        // This wavefront's loads of one stage.  Weight fragment g = wave + 4i:
+        // lane l brings row 16g + (l & 15), K bytes 16 (l >> 4) .. of the step.
+        // Activation fragment half f = wave + 4i (tile block f/2, half f%2):
+        // lane l = j + 16c brings row 16(f/2) + j, K bytes 16(4(f%2) + c) ..
+        uint32_t woff[4], xoff[TB];
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int p = tid + kThreads * i;
-            woff[i] = wrow_of(p >> 2) * (uint32_t)(KT / 2) + (uint32_t)(p & 3) * 16u;
+        for (int i = 0; i < 4; ++i) {
+            const int g = wave + 4 * i;
+            woff[i] = wrow_of(16 * g + i16) * (uint32_t)(KT / 2) + 16u * kq;
         }
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int p = tid + kThreads * i;
-            xoff[i] = (uint32_t)arow[p >> 3] * (uint32_t)KT + (uint32_t)(p & 7) * 16u;
+        for (int i = 0; i < TB; ++i) {
+            const int f = wave + 4 * i;
+            xoff[i] = (uint32_t)arow[16 * (f >> 1) + i16] * (uint32_t)KT +
+                      16u * (uint32_t)(4 * (f & 1) + kq);
         }
-        const uint32_t weoff = wrow_of(tid) * (uint32_t)(KT / 32);
-        const uint32_t xeoff = (uint32_t)arow[tid < BM ? tid : 0] * (uint32_t)(KT / 32);
+        // exponents: wavefront v brings weight rows 64v + l and activation
+        // rows 64 (v mod BM/64) + l, four bytes (one K step) each
+        const int xe_wave = wave % (BM / 64);
+        const uint32_t weoff = wrow_of(64 * wave + lane) * (uint32_t)(KT / 32);
+        const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
 
-        u32x4 wreg[WPT], xreg[XPT];
-        uint32_t wereg = 0, xereg = 0;
+        const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + 1024u * wave);
+        const uint32_t lds_wexp =
+            __builtin_amdgcn_readfirstlane(lds_addr(lds) + L::kW + L::kX + 256u * wave);
+        const uint32_t lds_xexp = __builtin_amdgcn_readfirstlane(lds_addr(lds) + L::kW + L::kX +
+                                                                 L::kWE + 256u * xe_wave);
+        auto issue = [&](int ks) {
+            const uint32_t st = (uint32_t)((ks % NS) * L::kStage);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_wave + st + 4096u * i);
+#pragma unroll
+            for (int i = 0; i < TB; ++i)
+                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_wave + st + L::kW + 4096u * i);
+            g2lds<4>(ws, weoff + (uint32_t)ks * 4u, lds_wexp + st);
+            g2lds<4>(act_s, xeoff + (uint32_t)ks * 4u, lds_xexp + st);
+        };
+
         v4f acc[8][TB];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -206,29 +186,46 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             for (int j = 0; j < TB; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // per-lane LDS bases: fragment slot of this lane, its exponent bytes
-        const int frag = lane * 16;
+        // per-lane LDS offsets inside a stage
+        const int afrag = lane * 16 + wn * 8 * 1024;
+        const int bfrag = L::kW + lane * 16 + wm * TB * 2048;
         const int wexp = L::kW + L::kX + i16 * 4 + kq + wn * 8 * 64;
         const int xexp = L::kW + L::kX + L::kWE + i16 * 4 + kq + wm * TB * 64;
-        const int afrag = frag + wn * 8 * 1024;
-        const int bfrag = L::kW + frag + wm * TB * 2048;
 
-        tile_gload<WPT, XPT>(wreg, xreg, wereg, xereg, w, woff, act, xoff, ws, weoff, act_s, xeoff,
-                             0, tid < BM);
-        tile_lstore<WPT, XPT>(lds, wreg, xreg, wereg, xereg, L::kW, L::kX + L::kW,
-                              L::kW + L::kX + L::kWE, tid, tid < BM);
-        __syncthreads();
-        for (int ks = 0; ks < KS; ks += 2) {
-            tile_step<0, TB, WPT, XPT, L::kStage>(acc, lds, ks, KS, afrag, bfrag, wexp, xexp, wreg,
-                                                  xreg, wereg, xereg, w, woff, act, xoff, ws,
-                                                  weoff, act_s, xeoff, L::kW, L::kW + L::kX,
-                                                  L::kW + L::kX + L::kWE, tid, tid < BM);
-            if (ks + 1 < KS)
-                tile_step<1, TB, WPT, XPT, L::kStage>(acc, lds, ks + 1, KS, afrag, bfrag, wexp,
-                                                      xexp, wreg, xreg, wereg, xereg, w, woff, act,
-                                                      xoff, ws, weoff, act_s, xeoff, L::kW,
-                                                      L::kW + L::kX, L::kW + L::kX + L::kWE,
-                                                      tid, tid < BM);
+#pragma unroll
+        for (int p = 0; p < NS - 1; ++p)
+            if (p < KS)
+                issue(p);
+        for (int ks = 0; ks < KS; ++ks) {
+            // this wavefront's loads of step ks are done once at most the
+            // later stages' loads are outstanding; then all wavefronts' are
+            if (ks + NS - 2 < KS)
+                wait_vmcnt<(NS - 2) * L::kLoads>();
+            else
+                wait_vmcnt<0>();
+            raw_barrier();
+            if (ks + NS - 1 < KS)
+                issue(ks + NS - 1);
+            const uint8_t *st = lds + (ks % NS) * L::kStage;
+            v8i b[TB];
+            int sb[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const u32x4 lo = lds_read16(st + bfrag + j * 2048);
+                const u32x4 hi = lds_read16(st + bfrag + j * 2048 + 1024);
+                b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                sb[j] = st[xexp + j * 64];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 a4 = lds_read16(st + afrag + i * 1024);
+                const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+                const int sa = st[wexp + i * 64];
+#pragma unroll
+                for (int j = 0; j < TB; ++j)
+                    acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
+            }
         }
 
         // epilogue: lane holds tile row (wm*BM/2 + 16j + i16), weight rows

@@ -148,21 +148,23 @@ def _weights(case):
 
 
 def routes_ffn(case: dict, routes) -> dict:
-    """h codes [n, I], h exponents [n, I/32] and float32 y [n, H] of the
-    route slots r = t*K + k in ``routes``."""
+    """h codes [n, I], h exponents [n, I/32], the SwiGLU output before
+    requantisation hv [n, I] and float32 y [n, H] of the route slots
+    r = t*K + k in ``routes``."""
     spec = case["spec"]
     s = shape_of(spec)
     r = np.ascontiguousarray(np.asarray(routes, dtype=np.int32))
     n = r.size
     hc = np.zeros((max(n, 1), spec.I), np.uint8)
     hs = np.zeros((max(n, 1), spec.I // 32), np.uint8)
+    hv = np.zeros((max(n, 1), spec.I), np.float32)
     y = np.zeros((max(n, 1), spec.H), np.float32)
     w13, w13s, w2, w2s = _weights(case)
-    rc = lib().orc_routes_ffn(ctypes.byref(s), _p(case["x_fp8"]), _p(case["x_scale"]),
-                              _p(case["topk_ids"]), _p(w13), _p(w13s), _p(w2), _p(w2s), _p(r),
-                              ctypes.c_int(n), _p(hc), _p(hs), _p(y))
+    rc = lib().orc_routes_ffn_hv(ctypes.byref(s), _p(case["x_fp8"]), _p(case["x_scale"]),
+                                 _p(case["topk_ids"]), _p(w13), _p(w13s), _p(w2), _p(w2s), _p(r),
+                                 ctypes.c_int(n), _p(hv), _p(hc), _p(hs), _p(y))
     assert rc == 0, "a listed route is not a valid local route"
-    return dict(h_codes=hc[:n], h_scale=hs[:n], y=y[:n])
+    return dict(h_codes=hc[:n], h_scale=hs[:n], hv=hv[:n], y=y[:n])
 
 
 def expert_ffn_gu(case: dict, t: int, e: int) -> np.ndarray:

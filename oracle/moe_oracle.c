@@ -275,10 +275,25 @@ ORC_EXPORT int orc_dispatch(const orc_shape *s, const int32_t *ids, int32_t *cou
  *   (h_codes, h_scale) = MX FP8 of hv, per 32 along I
  *   y[n]  = sum_i hq[i] * W2[e, n, i],  n in [0, H)
  * Any of gu_out / h_codes / h_scale may be NULL. */
+ORC_EXPORT void orc_expert_ffn_hv(const orc_shape *s, const uint8_t *xrow, const uint8_t *xsc,
+                                  int e, const uint8_t *w13, const uint8_t *w13s,
+                                  const uint8_t *w2, const uint8_t *w2s, float *gu_out,
+                                  float *hv_out, uint8_t *h_codes, uint8_t *h_scale, float *y);
+
 ORC_EXPORT void orc_expert_ffn(const orc_shape *s, const uint8_t *xrow, const uint8_t *xsc,
                                int e, const uint8_t *w13, const uint8_t *w13s,
                                const uint8_t *w2, const uint8_t *w2s, float *gu_out,
                                uint8_t *h_codes, uint8_t *h_scale, float *y)
+{
+    orc_expert_ffn_hv(s, xrow, xsc, e, w13, w13s, w2, w2s, gu_out, NULL, h_codes, h_scale, y);
+}
+
+/* As orc_expert_ffn, also returning the SwiGLU output before
+ * requantisation (hv_out[I], may be NULL). */
+ORC_EXPORT void orc_expert_ffn_hv(const orc_shape *s, const uint8_t *xrow, const uint8_t *xsc,
+                                  int e, const uint8_t *w13, const uint8_t *w13s,
+                                  const uint8_t *w2, const uint8_t *w2s, float *gu_out,
+                                  float *hv_out, uint8_t *h_codes, uint8_t *h_scale, float *y)
 {
     const int H = s->H, I = s->I;
     float *xd = (float *)malloc(sizeof(float) * (size_t)H);
@@ -309,6 +324,8 @@ ORC_EXPORT void orc_expert_ffn(const orc_shape *s, const uint8_t *xrow, const ui
 
     for (i = 0; i < I; ++i)
         hv[i] = orc_swiglu(gu[i], gu[I + i], s->gate_limit, s->up_limit);
+    if (hv_out)
+        memcpy(hv_out, hv, sizeof(float) * (size_t)I);
     for (b = 0; b < I / 32; ++b) {
         orc_mx8_quant_block(hv + 32 * b, hc + 32 * b, hs + b);
         for (i = 32 * b; i < 32 * b + 32; ++i)
@@ -383,10 +400,26 @@ ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t
 
 /* Per-route intermediates for step checks: for the routes r_list[0..n),
  * h codes [n, I], h exponents [n, I/32] and y [n, H] in float32. */
+ORC_EXPORT int orc_routes_ffn_hv(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
+                                 const int32_t *ids, const uint8_t *w13, const uint8_t *w13s,
+                                 const uint8_t *w2, const uint8_t *w2s, const int32_t *r_list,
+                                 int n, float *hv, uint8_t *h_codes, uint8_t *h_scale, float *y);
+
 ORC_EXPORT int orc_routes_ffn(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
                               const int32_t *ids, const uint8_t *w13, const uint8_t *w13s,
                               const uint8_t *w2, const uint8_t *w2s, const int32_t *r_list,
                               int n, uint8_t *h_codes, uint8_t *h_scale, float *y)
+{
+    return orc_routes_ffn_hv(s, x, xs, ids, w13, w13s, w2, w2s, r_list, n, NULL, h_codes,
+                             h_scale, y);
+}
+
+/* As orc_routes_ffn, also returning the pre-requantisation SwiGLU output
+ * hv [n, I] (may be NULL). */
+ORC_EXPORT int orc_routes_ffn_hv(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
+                                 const int32_t *ids, const uint8_t *w13, const uint8_t *w13s,
+                                 const uint8_t *w2, const uint8_t *w2s, const int32_t *r_list,
+                                 int n, float *hv, uint8_t *h_codes, uint8_t *h_scale, float *y)
 {
     const int H = s->H, I = s->I, K = s->K;
     int i, bad = 0;
@@ -398,9 +431,9 @@ ORC_EXPORT int orc_routes_ffn(const orc_shape *s, const uint8_t *x, const uint8_
             bad++;
             continue;
         }
-        orc_expert_ffn(s, x + (size_t)t * H, xs + (size_t)t * (H / 32), e, w13, w13s, w2, w2s,
-                       NULL, h_codes + (size_t)i * I, h_scale + (size_t)i * (I / 32),
-                       y + (size_t)i * H);
+        orc_expert_ffn_hv(s, x + (size_t)t * H, xs + (size_t)t * (H / 32), e, w13, w13s, w2,
+                          w2s, NULL, hv ? hv + (size_t)i * I : NULL, h_codes + (size_t)i * I,
+                          h_scale + (size_t)i * (I / 32), y + (size_t)i * H);
     }
     return bad ? -1 : 0;
 }
