@@ -14,7 +14,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Byte layout of the moe_forward workspace.
 struct Layout {
-    size_t counts, offsets, row_route, route_row, status, scratch, h, hs, y, total;
+    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, total;
 };
 
 Layout layout_of(const moe_shape &s)
@@ -33,6 +33,8 @@ Layout layout_of(const moe_shape &s)
     p = align_up(p + sizeof(int32_t) * TK);
     L.status = p;
     p = align_up(p + sizeof(int32_t) * 4);
+    L.sync = p;
+    p = align_up(p + sizeof(int32_t) * (size_t)moe::fused_sync_words(s));
     L.scratch = p;
     p = align_up(p + moe::dispatch_scratch_bytes(s));
     L.h = p;
@@ -190,6 +192,18 @@ int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const i
     uint8_t *hs = base + L.hs;
     float *y = reinterpret_cast<float *>(base + L.y);
     hipStream_t st = as_stream(stream);
+    if (moe::use_fused_decode(*s)) {
+        // dispatch (which also clears the work-queue counters), then one
+        // persistent launch for GEMM1, GEMM2 and the combine
+        int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
+        hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row,
+                                            status, scratch, st, sync,
+                                            moe::fused_sync_words(*s));
+        if (e == hipSuccess)
+            e = moe::launch_fused_decode(*s, x, xs, counts, offsets, row_route, route_row, tw,
+                                         w13, w13s, w2, w2s, h, hs, y, out, sync, st);
+        return hip_status(e);
+    }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st);
     if (e == hipSuccess)

@@ -10,43 +10,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 8; // output columns per thread
 
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict__ route_row,
                const float *__restrict__ y, uint16_t *__restrict__ out)
 {
-    // a rounded product, then a rounded add: no fused multiply-add
-#pragma clang fp contract(off)
-    const int per_token = (s.H + kThreads * kCols - 1) / (kThreads * kCols);
+    const int per_token = (s.H + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
     const int t = blockIdx.x / per_token;
-    const int col = ((blockIdx.x - t * per_token) * kThreads + threadIdx.x) * kCols;
-    if (col >= s.H)
-        return;
-    float acc[kCols];
-#pragma unroll
-    for (int i = 0; i < kCols; ++i)
-        acc[i] = 0.0f;
-    const size_t slot0 = (size_t)t * s.K;
-    for (int k = 0; k < s.K; ++k) {
-        const int row = route_row[slot0 + k];
-        if (row < 0)
-            continue;
-        const float w = tw[slot0 + k];
-        const float4 *yr = reinterpret_cast<const float4 *>(y + (size_t)row * s.H + col);
-        const float4 a = yr[0], b = yr[1];
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < kCols; ++i) {
-            const float p = w * v[i];
-            acc[i] = acc[i] + p;
-        }
-    }
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4 *>(out + (size_t)t * s.H + col) = uint4{o[0], o[1], o[2], o[3]};
+    const int col = ((blockIdx.x - t * per_token) * kThreads + threadIdx.x) * kCombineVec;
+    combine_cols(s, tw, route_row, y, out, t, col);
 }
 
 } // namespace
@@ -55,7 +27,7 @@ hipError_t launch_combine(const moe_shape &sh, const float *tw, const int32_t *r
                           const float *y, uint16_t *out, hipStream_t st)
 {
     const Shape s = to_dev(sh);
-    const int per_block = kThreads * kCols;
+    const int per_block = kThreads * kCombineVec;
     const long grid = (long)((sh.H + per_block - 1) / per_block) * sh.T;
     combine_kernel<<<(unsigned)grid, kThreads, 0, st>>>(s, tw, route_row, y, out);
     return hipGetLastError();

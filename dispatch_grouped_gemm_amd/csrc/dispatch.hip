@@ -136,8 +136,11 @@ __device__ int block_exclusive_scan(int v, int *total)
 __global__ void __launch_bounds__(kThreads)
 compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                      int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
-                     int32_t *__restrict__ route_row, int32_t *__restrict__ status)
+                     int32_t *__restrict__ route_row, int32_t *__restrict__ status,
+                     int32_t *__restrict__ zero, int nzero)
 {
+    for (int i = threadIdx.x; i < nzero; i += kThreads)
+        zero[i] = 0;
     extern __shared__ int hist[]; // [kWaves][E_local]
     __shared__ int invalid_total;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -323,8 +326,11 @@ __device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, lon
 __global__ void __launch_bounds__(kThreads)
 fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                    int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
-                   int32_t *__restrict__ route_row, int32_t *__restrict__ status)
+                   int32_t *__restrict__ route_row, int32_t *__restrict__ status,
+                   int32_t *__restrict__ zero, int nzero)
 {
+    for (int i = threadIdx.x; i < nzero; i += kThreads)
+        zero[i] = 0;
     extern __shared__ int cnt[]; // [E_local]
     __shared__ int inv_total, drop_total;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -405,6 +411,8 @@ int large_blocks(const moe_shape &s)
 
 } // namespace
 
+bool dispatch_is_single_block(const moe_shape &s) { return num_slots(s) <= kSmallSlots; }
+
 size_t dispatch_scratch_bytes(const moe_shape &s)
 {
     if (s.dispatch_mode != MOE_DISPATCH_COMPACT || compact_is_small(s))
@@ -414,14 +422,17 @@ size_t dispatch_scratch_bytes(const moe_shape &s)
 
 hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
-                           int32_t *status, void *scratch, hipStream_t st)
+                           int32_t *status, void *scratch, hipStream_t st, int32_t *zero,
+                           int nzero)
 {
+    if (nzero > 0 && !dispatch_is_single_block(sh))
+        return hipErrorInvalidValue;
     const Shape s = to_dev(sh);
     const size_t E = (size_t)sh.E_local;
     if (sh.dispatch_mode == MOE_DISPATCH_COMPACT) {
         if (compact_is_small(sh)) {
             compact_small_kernel<<<1, kThreads, kWaves * E * sizeof(int), st>>>(
-                s, ids, counts, offsets, row_route, route_row, status);
+                s, ids, counts, offsets, row_route, route_row, status, zero, nzero);
             return hipGetLastError();
         }
         const int nblk = large_blocks(sh);
@@ -434,7 +445,7 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
     }
     if (num_slots(sh) <= kSmallSlots) {
         fixed_small_kernel<<<1, kThreads, E * sizeof(int), st>>>(s, ids, counts, offsets, row_route,
-                                                                  route_row, status);
+                                                                  route_row, status, zero, nzero);
         return hipGetLastError();
     }
     fixed_reset_kernel<<<(int)((E + 256) / 256), 256, 0, st>>>(s, counts, offsets, status);

@@ -81,232 +81,369 @@ __device__ __forceinline__ void reduce_waves(v4f (&acc)[NMB][4], float *red, int
     }
 }
 
+// Pointers of one layer call, shared by the item bodies below.
+struct LayerPtrs {
+    const uint8_t *x, *xs;
+    const int32_t *counts, *offsets, *row_route;
+    const uint8_t *w13, *w13s, *w2, *w2s;
+    uint8_t *h, *hs;
+    float *y;
+    const float *tw;
+    const int32_t *route_row;
+    uint16_t *out;
+};
+
+// Where an item's rows are: expert e, rows [row0, row0 + nrows).
+struct Chunk {
+    int e, row0, nrows;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const Shape &s, const int *prefix,
+                                          const int32_t *__restrict__ counts,
+                                          const int32_t *__restrict__ offsets, int ch, int q)
+{
+    Chunk c;
+    c.e = chunk_expert(prefix, s.E_local, q);
+    const int k = q - prefix[c.e];
+    c.row0 = offsets[c.e] + k * ch;
+    c.nrows = min(ch, used_rows(s, counts[c.e]) - k * ch);
+    return c;
+}
+
+// GEMM1 + SwiGLU + requant of 32 intermediate columns j0 = 32 nt .. of one
+// row chunk.  LDS: tok[16 NMB], red[NMB*4*4*64], exps[(64 + 16 NMB) * es].
 template <int NMB>
-__global__ void __launch_bounds__(kThreads)
-gemm1_skinny_kernel(Shape s, const uint8_t *__restrict__ x, const uint8_t *__restrict__ xs,
-                    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-                    const int32_t *__restrict__ row_route, const uint8_t *__restrict__ w13,
-                    const uint8_t *__restrict__ w13s, uint8_t *__restrict__ h,
-                    uint8_t *__restrict__ hs)
+__device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, const Chunk &c,
+                                           int nt, int *tok, float *red, uint8_t *exps)
 {
     constexpr int CH = 16 * NMB;
-    __shared__ int prefix[kMaxLocalExperts + 1];
-    __shared__ int tok[CH];
-    __shared__ float red[NMB * 4 * 4 * 64];
-    extern __shared__ uint8_t exps[]; // [64 weight rows + CH x rows][H/32 + 4]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = H / 128;
     const int es = H / 32 + 4;
     uint8_t *wexp = exps, *xexp = exps + 64 * es;
-    const int nchunks = plan_chunks(s, counts, CH, prefix);
-    const int NT = I / 32;
-    const long items = (long)nchunks * NT;
+    const int e = c.e, row0 = c.row0, nrows = c.nrows;
+    const int nmb_act = (nrows + 15) >> 4;
+    const int j0 = nt * 32;
+    if (tid < CH)
+        tok[tid] = tid < nrows ? p.row_route[row0 + tid] / s.K : 0;
+    // W13 rows of the tile: r in [0, 64) is gate/up group r/16, row r%16
+    stage_exponents(wexp, es, H / 32, 64, [&](int r) {
+        const int g = r >> 4;
+        const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + (r & 15);
+        return p.w13s + wrow * (size_t)(H / 32);
+    });
+    stage_exponents(xexp, es, H / 32, nrows, [&](int r) {
+        return p.xs + (size_t)(p.row_route[row0 + r] / s.K) * (size_t)(H / 32);
+    });
+    __syncthreads();
 
-    for (long item = blockIdx.x; item < items; item += gridDim.x) {
-        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
-        const int e = chunk_expert(prefix, s.E_local, q);
-        const int c = q - prefix[e];
-        const int rows_e = used_rows(s, counts[e]);
-        const int row0 = offsets[e] + c * CH;
-        const int nrows = min(CH, rows_e - c * CH);
-        const int nmb_act = (nrows + 15) >> 4;
-        const int j0 = nt * 32;
-        if (tid < CH)
-            tok[tid] = tid < nrows ? row_route[row0 + tid] / s.K : 0;
-        // W13 rows of the tile: r in [0, 64) is gate/up group r/16, row r%16
-        stage_exponents(wexp, es, H / 32, 64, [&](int r) {
-            const int g = r >> 4;
-            const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + (r & 15);
-            return w13s + wrow * (size_t)(H / 32);
-        });
-        stage_exponents(xexp, es, H / 32, nrows, [&](int r) {
-            return xs + (size_t)(row_route[row0 + r] / s.K) * (size_t)(H / 32);
-        });
-        __syncthreads();
+    const uint8_t *wp[4];
+    const uint8_t *wsp[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + i16;
+        wp[g] = p.w13 + wrow * (size_t)(H / 2) + kq * 16;
+        wsp[g] = wexp + (g * 16 + i16) * es + kq;
+    }
+    const uint8_t *xp[NMB];
+    const uint8_t *xsp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        const int rloc = min(mb * 16 + i16, nrows - 1);
+        const size_t t = (size_t)tok[rloc];
+        xp[mb] = p.x + t * (size_t)H + kq * 16;
+        xsp[mb] = xexp + rloc * es + kq;
+    }
 
-        const uint8_t *wp[4];
-        const uint8_t *wsp[4];
+    v4f acc[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int ks = wave; ks < KS; ks += 4) {
+        v8i a[4];
+        int sa[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + i16;
-            wp[g] = w13 + wrow * (size_t)(H / 2) + kq * 16;
-            wsp[g] = wexp + (g * 16 + i16) * es + kq;
+            a[g] = load_fp4_frag(wp[g] + ks * 64);
+            sa[g] = wsp[g][ks * 4];
         }
-        const uint8_t *xp[NMB];
-        const uint8_t *xsp[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            const int rloc = min(mb * 16 + i16, nrows - 1);
-            const size_t t = (size_t)tok[rloc];
-            xp[mb] = x + t * (size_t)H + kq * 16;
-            xsp[mb] = xexp + rloc * es + kq;
-        }
-
-        v4f acc[NMB][4];
+            if (mb < nmb_act) {
+                const v8i b = load_fp8_frag(xp[mb] + ks * 128);
+                const int sb = xsp[mb][ks * 4];
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        for (int ks = wave; ks < KS; ks += 4) {
-            v8i a[4];
-            int sa[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                a[g] = load_fp4_frag(wp[g] + ks * 64);
-                sa[g] = wsp[g][ks * 4];
-            }
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                if (mb < nmb_act) {
-                    const v8i b = load_fp8_frag(xp[mb] + ks * 128);
-                    const int sb = xsp[mb][ks * 4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
-                }
+                for (int g = 0; g < 4; ++g)
+                    acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
             }
         }
-        reduce_waves<NMB>(acc, red, nmb_act);
-
-        // epilogue: wavefront w finishes row block w
-        if (wave < nmb_act) {
-            const int mb = wave;
-            const int rloc = mb * 16 + i16;
-            float hv[8];
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float gt = red[((mb * 4 + half) * 4 + v) * 64 + lane];
-                    const float up = red[((mb * 4 + 2 + half) * 4 + v) * 64 + lane];
-                    hv[half * 4 + v] = swiglu_clamped(gt, up, s.gate_limit, s.up_limit);
-                }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                amax = fmaxf(amax, fabsf(hv[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            const int E = mx8_block_exponent(amax);
-            uint32_t pk[2] = {0u, 0u};
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    pk[half] |= f32_to_e4m3(ldexpf(hv[half * 4 + v], -E)) << (8 * v);
-            if (rloc < nrows) {
-                const size_t row = (size_t)(row0 + rloc);
-                uint8_t *hr = h + row * (size_t)I + j0 + 4 * kq;
-                *reinterpret_cast<uint32_t *>(hr) = pk[0];
-                *reinterpret_cast<uint32_t *>(hr + 16) = pk[1];
-                if (kq == 0)
-                    hs[row * (size_t)(I / 32) + nt] = (uint8_t)(E + 127);
-            }
-        }
-        __syncthreads();
     }
+    reduce_waves<NMB>(acc, red, nmb_act);
+
+    // epilogue: wavefront w finishes row block w
+    if (wave < nmb_act) {
+        const int mb = wave;
+        const int rloc = mb * 16 + i16;
+        float hv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float gt = red[((mb * 4 + half) * 4 + v) * 64 + lane];
+                const float up = red[((mb * 4 + 2 + half) * 4 + v) * 64 + lane];
+                hv[half * 4 + v] = swiglu_clamped(gt, up, s.gate_limit, s.up_limit);
+            }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(hv[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int E = mx8_block_exponent(amax);
+        uint32_t pk[2] = {0u, 0u};
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                pk[half] |= f32_to_e4m3(ldexpf(hv[half * 4 + v], -E)) << (8 * v);
+        if (rloc < nrows) {
+            const size_t row = (size_t)(row0 + rloc);
+            uint8_t *hr = p.h + row * (size_t)I + j0 + 4 * kq;
+            *reinterpret_cast<uint32_t *>(hr) = pk[0];
+            *reinterpret_cast<uint32_t *>(hr + 16) = pk[1];
+            if (kq == 0)
+                p.hs[row * (size_t)(I / 32) + nt] = (uint8_t)(E + 127);
+        }
+    }
+    __syncthreads();
 }
 
+// GEMM2 of 64 output columns n0 = 64 nt .. of one row chunk (y in float32).
+// LDS: red[NMB*4*4*64], exps[(64 + 16 NMB) * (I/32 + 4)].
 template <int NMB>
-__global__ void __launch_bounds__(kThreads)
-gemm2_skinny_kernel(Shape s, const uint8_t *__restrict__ h, const uint8_t *__restrict__ hs,
-                    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-                    const uint8_t *__restrict__ w2, const uint8_t *__restrict__ w2s,
-                    float *__restrict__ y)
+__device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, const Chunk &c,
+                                           int nt, float *red, uint8_t *exps)
 {
-    constexpr int CH = 16 * NMB;
-    __shared__ int prefix[kMaxLocalExperts + 1];
-    __shared__ float red[NMB * 4 * 4 * 64];
-    extern __shared__ uint8_t exps[]; // [64 weight rows + CH h rows][I/32 + 4]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = I / 128;
     const int es = I / 32 + 4;
     uint8_t *wexp = exps, *hexp = exps + 64 * es;
-    const int nchunks = plan_chunks(s, counts, CH, prefix);
-    const int NT = H / 64;
-    const long items = (long)nchunks * NT;
+    const int e = c.e, row0 = c.row0, nrows = c.nrows;
+    const int nmb_act = (nrows + 15) >> 4;
+    const int n0 = nt * 64;
+    stage_exponents(wexp, es, I / 32, 64, [&](int r) {
+        return p.w2s + ((size_t)e * H + n0 + r) * (size_t)(I / 32);
+    });
+    stage_exponents(hexp, es, I / 32, nrows, [&](int r) {
+        return p.hs + (size_t)(row0 + r) * (size_t)(I / 32);
+    });
+    __syncthreads();
 
-    for (long item = blockIdx.x; item < items; item += gridDim.x) {
-        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
-        const int e = chunk_expert(prefix, s.E_local, q);
-        const int c = q - prefix[e];
-        const int rows_e = used_rows(s, counts[e]);
-        const int row0 = offsets[e] + c * CH;
-        const int nrows = min(CH, rows_e - c * CH);
-        const int nmb_act = (nrows + 15) >> 4;
-        const int n0 = nt * 64;
-        stage_exponents(wexp, es, I / 32, 64, [&](int r) {
-            return w2s + ((size_t)e * H + n0 + r) * (size_t)(I / 32);
-        });
-        stage_exponents(hexp, es, I / 32, nrows, [&](int r) {
-            return hs + (size_t)(row0 + r) * (size_t)(I / 32);
-        });
-        __syncthreads();
+    const uint8_t *wp[4];
+    const uint8_t *wsp[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const size_t wrow = (size_t)e * H + n0 + 16 * g + i16;
+        wp[g] = p.w2 + wrow * (size_t)(I / 2) + kq * 16;
+        wsp[g] = wexp + (16 * g + i16) * es + kq;
+    }
+    const uint8_t *hp[NMB];
+    const uint8_t *hsp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        const int rloc = min(mb * 16 + i16, nrows - 1);
+        const size_t row = (size_t)(row0 + rloc);
+        hp[mb] = p.h + row * (size_t)I + kq * 16;
+        hsp[mb] = hexp + rloc * es + kq;
+    }
 
-        const uint8_t *wp[4];
-        const uint8_t *wsp[4];
+    v4f acc[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int ks = wave; ks < KS; ks += 4) {
+        v8i a[4];
+        int sa[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const size_t wrow = (size_t)e * H + n0 + 16 * g + i16;
-            wp[g] = w2 + wrow * (size_t)(I / 2) + kq * 16;
-            wsp[g] = wexp + (16 * g + i16) * es + kq;
+            a[g] = load_fp4_frag(wp[g] + ks * 64);
+            sa[g] = wsp[g][ks * 4];
         }
-        const uint8_t *hp[NMB];
-        const uint8_t *hsp[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            const int rloc = min(mb * 16 + i16, nrows - 1);
-            const size_t row = (size_t)(row0 + rloc);
-            hp[mb] = h + row * (size_t)I + kq * 16;
-            hsp[mb] = hexp + rloc * es + kq;
+            if (mb < nmb_act) {
+                const v8i b = load_fp8_frag(hp[mb] + ks * 128);
+                const int sb = hsp[mb][ks * 4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
+            }
         }
+    }
+    reduce_waves<NMB>(acc, red, nmb_act);
 
-        v4f acc[NMB][4];
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        for (int ks = wave; ks < KS; ks += 4) {
-            v8i a[4];
-            int sa[4];
+    if (wave < nmb_act) {
+        const int mb = wave;
+        const int rloc = mb * 16 + i16;
+        if (rloc < nrows) {
+            float *yr = p.y + (size_t)(row0 + rloc) * (size_t)H + n0 + 4 * kq;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                a[g] = load_fp4_frag(wp[g] + ks * 64);
-                sa[g] = wsp[g][ks * 4];
-            }
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                if (mb < nmb_act) {
-                    const v8i b = load_fp8_frag(hp[mb] + ks * 128);
-                    const int sb = hsp[mb][ks * 4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
-                }
+                const float *r = red + (mb * 4 + g) * 4 * 64 + lane;
+                *reinterpret_cast<float4 *>(yr + 16 * g) = float4{r[0], r[64], r[128], r[192]};
             }
         }
-        reduce_waves<NMB>(acc, red, nmb_act);
+    }
+    __syncthreads();
+}
 
-        if (wave < nmb_act) {
-            const int mb = wave;
-            const int rloc = mb * 16 + i16;
-            if (rloc < nrows) {
-                float *yr = y + (size_t)(row0 + rloc) * (size_t)H + n0 + 4 * kq;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float *r = red + (mb * 4 + g) * 4 * 64 + lane;
-                    *reinterpret_cast<float4 *>(yr + 16 * g) =
-                        float4{r[0], r[64], r[128], r[192]};
-                }
-            }
+template <int NMB>
+__global__ void __launch_bounds__(kThreads)
+gemm1_skinny_kernel(Shape s, LayerPtrs p)
+{
+    constexpr int CH = 16 * NMB;
+    __shared__ int prefix[kMaxLocalExperts + 1];
+    __shared__ int tok[CH];
+    __shared__ float red[NMB * 4 * 4 * 64];
+    extern __shared__ uint8_t exps[];
+    const int nchunks = plan_chunks(s, p.counts, CH, prefix);
+    const int NT = s.I / 32;
+    const long items = (long)nchunks * NT;
+    for (long item = blockIdx.x; item < items; item += gridDim.x) {
+        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
+        gemm1_item<NMB>(s, p, chunk_of(s, prefix, p.counts, p.offsets, CH, q), nt, tok, red, exps);
+    }
+}
+
+template <int NMB>
+__global__ void __launch_bounds__(kThreads)
+gemm2_skinny_kernel(Shape s, LayerPtrs p)
+{
+    constexpr int CH = 16 * NMB;
+    __shared__ int prefix[kMaxLocalExperts + 1];
+    __shared__ float red[NMB * 4 * 4 * 64];
+    extern __shared__ uint8_t exps[];
+    const int nchunks = plan_chunks(s, p.counts, CH, prefix);
+    const int NT = s.H / 64;
+    const long items = (long)nchunks * NT;
+    for (long item = blockIdx.x; item < items; item += gridDim.x) {
+        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
+        gemm2_item<NMB>(s, p, chunk_of(s, prefix, p.counts, p.offsets, CH, q), nt, red, exps);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The whole layer after dispatch in one persistent launch.  Workgroups take
+// tickets from one counter: first every GEMM1 item (row chunk, 32
+// intermediate columns), expert by expert, then every GEMM2 item, then the
+// combine items (one token, 2048 output columns).  A GEMM2 item of expert e
+// waits until all GEMM1 items of e have finished (a per-expert counter); a
+// combine item waits until every GEMM2 item has finished.  Tickets are
+// handed out in that order, so a wait only ever concerns items that running
+// workgroups already hold, and every wait ends; a wait that does not end
+// within kMaxSpins polls counts itself in sync[1] and gives up rather than
+// hang.
+//
+// Control flow around the barriers stays wave-uniform: the queue work is done
+// by a whole wavefront (wave 0) whose lanes all run the same atomics and
+// polls, never by one lane behind a per-lane branch.  (Per-lane branches on
+// both sides of the loop's back edge let the compiler join them into a
+// lane-divergent inner loop whose other lanes never take the next ticket.)
+// Every wavefront releases its own stores with its own increment, so a
+// finished item adds kWaves to its counter.
+//
+// sync (zeroed by the dispatch launch): [0] ticket counter, [1] wait
+// timeouts, [2] finished GEMM2 items, [3 + e] finished GEMM1 items of e.
+// Counters are released and acquired at agent scope, so h and y written by
+// one XCD are seen by the others.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxSpins = 1 << 20;
+
+// Whole-wavefront wait until *cnt >= need, then an agent-scope acquire.
+__device__ __forceinline__ void wait_count(int32_t *cnt, int need, int32_t *timeouts, int one)
+{
+    for (int spins = 0;; ++spins) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (v >= need)
+            break;
+        if (spins >= kMaxSpins) {
+            __hip_atomic_fetch_add(timeouts, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int NMB>
+__global__ void __launch_bounds__(kThreads)
+fused_decode_kernel(Shape s, LayerPtrs p, int32_t *sync)
+{
+    constexpr int CH = 16 * NMB;
+    constexpr int kCombineCols = 2048;
+    __shared__ int prefix[kMaxLocalExperts + 1];
+    __shared__ int tok[CH];
+    __shared__ float red[NMB * 4 * 4 * 64];
+    __shared__ int ticket;
+    extern __shared__ uint8_t exps[];
+    const int tid = threadIdx.x;
+    // 1 in lane 0 of each wavefront, 0 elsewhere: a whole-wavefront atomic
+    // add of `one` counts once per wavefront.
+    const int one = (tid & 63) == 0 ? 1 : 0;
+    const bool leader = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
+    const int nchunks = plan_chunks(s, p.counts, CH, prefix);
+    const int NT1 = s.I / 32, NT2 = s.H / 64;
+    const int CB = (s.H + kCombineCols - 1) / kCombineCols;
+    const long items1 = (long)nchunks * NT1, items2 = (long)nchunks * NT2;
+    const long total = items1 + items2 + (long)s.T * CB;
+    int32_t *timeouts = sync + 1, *done2 = sync + 2, *done1 = sync + 3;
+
+    for (;;) {
+        if (leader) {
+            const int mine = __hip_atomic_fetch_add(sync, one, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            ticket = __builtin_amdgcn_readfirstlane(mine);
         }
         __syncthreads();
+        const long t = ticket;
+        __syncthreads();
+        if (t >= total)
+            break;
+        if (t < items1) {
+            const int q = (int)(t / NT1), nt = (int)(t - (long)q * NT1);
+            const Chunk c = chunk_of(s, prefix, p.counts, p.offsets, CH, q);
+            gemm1_item<NMB>(s, p, c, nt, tok, red, exps);
+            __hip_atomic_fetch_add(done1 + c.e, one, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (t < items1 + items2) {
+            const long u = t - items1;
+            const int q = (int)(u / NT2), nt = (int)(u - (long)q * NT2);
+            const Chunk c = chunk_of(s, prefix, p.counts, p.offsets, CH, q);
+            if (leader) {
+                const int chunks_e = prefix[c.e + 1] - prefix[c.e];
+                wait_count(done1 + c.e, kWaves * chunks_e * NT1, timeouts, one);
+            }
+            __syncthreads();
+            gemm2_item<NMB>(s, p, c, nt, red, exps);
+            __hip_atomic_fetch_add(done2, one, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const long u = t - items1 - items2;
+            const int tk = (int)(u / CB), cb = (int)(u - (long)tk * CB);
+            if (leader)
+                wait_count(done2, (int)(kWaves * items2), timeouts, one);
+            __syncthreads();
+            combine_cols(s, p.tw, p.route_row, p.y, p.out, tk,
+                         (cb * kThreads + tid) * kCombineVec);
+        }
     }
 }
 
@@ -381,6 +518,16 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
     if (use_tiled_gemm1(sh))
         return launch_gemm1_tiled(sh, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
     const Shape s = to_dev(sh);
+    LayerPtrs p{};
+    p.x = x;
+    p.xs = xs;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.row_route = row_route;
+    p.w13 = w13;
+    p.w13s = w13s;
+    p.h = h;
+    p.hs = hs;
     const int nmb = pick_nmb(sh);
     const long nt = sh.I / 32;
 #define MOE_LAUNCH_G1(N)                                                                          \
@@ -388,7 +535,7 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
         auto k = gemm1_skinny_kernel<N>;                                                          \
         const size_t lds = (size_t)(64 + 16 * N) * (sh.H / 32 + 4);                               \
         const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
-        k<<<grid, kThreads, lds, st>>>(s, x, xs, counts, offsets, row_route, w13, w13s, h, hs);   \
+        k<<<grid, kThreads, lds, st>>>(s, p);                                                     \
     } while (0)
     if (nmb == 1)
         MOE_LAUNCH_G1(1);
@@ -407,6 +554,14 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
     if (use_tiled_gemm2(sh))
         return launch_gemm2_tiled(sh, h, hs, counts, offsets, w2, w2s, y, st);
     const Shape s = to_dev(sh);
+    LayerPtrs p{};
+    p.h = const_cast<uint8_t *>(h);
+    p.hs = const_cast<uint8_t *>(hs);
+    p.counts = counts;
+    p.offsets = offsets;
+    p.w2 = w2;
+    p.w2s = w2s;
+    p.y = y;
     const int nmb = pick_nmb(sh);
     const long nt = sh.H / 64;
 #define MOE_LAUNCH_G2(N)                                                                          \
@@ -414,7 +569,7 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
         auto k = gemm2_skinny_kernel<N>;                                                          \
         const size_t lds = (size_t)(64 + 16 * N) * (sh.I / 32 + 4);                               \
         const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
-        k<<<grid, kThreads, lds, st>>>(s, h, hs, counts, offsets, w2, w2s, y);                    \
+        k<<<grid, kThreads, lds, st>>>(s, p);                                                     \
     } while (0)
     if (nmb == 1)
         MOE_LAUNCH_G2(1);
@@ -423,6 +578,70 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
     else
         MOE_LAUNCH_G2(4);
 #undef MOE_LAUNCH_G2
+    return hipGetLastError();
+}
+
+} // namespace moe
+
+namespace moe {
+
+// The persistent single-launch layer is correct but slower than the four
+// launches on every decode shape measured (7168 x 3072, 36 experts touched:
+// 1494 us against about 300 us): each item's release writes back the L2 and
+// each GEMM2 item's acquire invalidates it, which costs more than the launch
+// gaps it saves.  It stays off until that synchronisation is cheaper.
+constexpr bool kFusedDecodeEnabled = false;
+
+bool use_fused_decode(const moe_shape &s)
+{
+    return kFusedDecodeEnabled && !use_tiled_gemm1(s) && !use_tiled_gemm2(s) &&
+           dispatch_is_single_block(s);
+}
+
+int fused_sync_words(const moe_shape &s) { return 3 + s.E_local; }
+
+hipError_t launch_fused_decode(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
+                               const int32_t *counts, const int32_t *offsets,
+                               const int32_t *row_route, const int32_t *route_row,
+                               const float *tw, const uint8_t *w13, const uint8_t *w13s,
+                               const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
+                               float *y, uint16_t *out, int32_t *sync, hipStream_t st)
+{
+    const Shape s = to_dev(sh);
+    LayerPtrs p{};
+    p.x = x;
+    p.xs = xs;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.row_route = row_route;
+    p.w13 = w13;
+    p.w13s = w13s;
+    p.w2 = w2;
+    p.w2s = w2s;
+    p.h = h;
+    p.hs = hs;
+    p.y = y;
+    p.tw = tw;
+    p.route_row = route_row;
+    p.out = out;
+    const int nmb = pick_nmb(sh);
+    const long upper = chunk_upper_bound(sh, 16 * nmb) * (sh.I / 32 + sh.H / 64) +
+                       (long)sh.T * ((sh.H + 2047) / 2048);
+#define MOE_LAUNCH_FUSED(N)                                                                       \
+    do {                                                                                          \
+        auto k = fused_decode_kernel<N>;                                                          \
+        const int es = (sh.H > sh.I ? sh.H : sh.I) / 32 + 4;                                      \
+        const size_t lds = (size_t)(64 + 16 * N) * es;                                            \
+        const int grid = grid_for(k, upper, lds);                                                 \
+        k<<<grid, kThreads, lds, st>>>(s, p, sync);                                               \
+    } while (0)
+    if (nmb == 1)
+        MOE_LAUNCH_FUSED(1);
+    else if (nmb == 2)
+        MOE_LAUNCH_FUSED(2);
+    else
+        MOE_LAUNCH_FUSED(4);
+#undef MOE_LAUNCH_FUSED
     return hipGetLastError();
 }
 

@@ -188,12 +188,64 @@ __device__ __forceinline__ int chunk_expert(const int *prefix, int E, int q)
 }
 
 // ---------------------------------------------------------------------------
+// Combine of output columns [col, col + 8) of token t: the kept routes in
+// ascending k, each a rounded product then a rounded add (no fused
+// multiply-add), one bf16 rounding at the end.
+// ---------------------------------------------------------------------------
+constexpr int kCombineVec = 8;
+
+__device__ __forceinline__ void combine_cols(const Shape &s, const float *__restrict__ tw,
+                                             const int32_t *__restrict__ route_row,
+                                             const float *__restrict__ y,
+                                             uint16_t *__restrict__ out, int t, int col)
+{
+#pragma clang fp contract(off)
+    if (col >= s.H)
+        return;
+    float acc[kCombineVec];
+#pragma unroll
+    for (int i = 0; i < kCombineVec; ++i)
+        acc[i] = 0.0f;
+    const size_t slot0 = (size_t)t * s.K;
+    for (int k = 0; k < s.K; ++k) {
+        const int row = route_row[slot0 + k];
+        if (row < 0)
+            continue;
+        const float w = tw[slot0 + k];
+        const float4 *yr = reinterpret_cast<const float4 *>(y + (size_t)row * s.H + col);
+        const float4 a = yr[0], b = yr[1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < kCombineVec; ++i) {
+            const float prod = w * v[i];
+            acc[i] = acc[i] + prod;
+        }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4 *>(out + (size_t)t * s.H + col) = uint4{o[0], o[1], o[2], o[3]};
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (defined in the kernel sources).
 // ---------------------------------------------------------------------------
 size_t dispatch_scratch_bytes(const moe_shape &s);
+bool dispatch_is_single_block(const moe_shape &s);
+// zero[0 .. nzero) is cleared by the dispatch launch (one workgroup paths only)
 hipError_t launch_dispatch(const moe_shape &s, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
-                           int32_t *status, void *scratch, hipStream_t st);
+                           int32_t *status, void *scratch, hipStream_t st,
+                           int32_t *zero = nullptr, int nzero = 0);
+bool use_fused_decode(const moe_shape &s);
+int fused_sync_words(const moe_shape &s);
+hipError_t launch_fused_decode(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
+                               const int32_t *counts, const int32_t *offsets,
+                               const int32_t *row_route, const int32_t *route_row,
+                               const float *tw, const uint8_t *w13, const uint8_t *w13s,
+                               const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
+                               float *y, uint16_t *out, int32_t *sync, hipStream_t st);
 hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
                         const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
