@@ -51,7 +51,64 @@ def parse():
                    help="routes in the oracle's timed sample")
     p.add_argument("--kernel-iters", type=int, default=0,
                    help="launches per kernel for the roofline timing (default: steps)")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="instead of the layer, time a plain device copy of this many MiB "
+                        "(the reference size for the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_reference(args):
+    """A plain copy of known size: N bytes read and N bytes written per launch."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes": n, "read_kib": n // 1024, "write_kib": n // 1024,
+                      "us_per_copy": round(s * 1e6, 2),
+                      "gbs": round(2 * n / s / 1e9, 1)}), flush=True)
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the HIP sources of the library (names and bytes)."""
+    import hashlib
+    d = os.path.join(ROOT, "dispatch_grouped_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the rocprofv3 counter
+    summary of this workload under profiles/, or None when there is none or
+    the kernel sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", workload + ".md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "traffic_bytes_per_launch", "source_sha256", "traffic_kernel"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def gemm1_algorithmic_bytes(spec, work) -> int:
@@ -70,6 +127,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_reference(args)
+        return
 
     import torch
 
@@ -170,7 +230,8 @@ def main():
         "dispatch_status": status.tolist(),
         "roofline": {"bound": "hbm", "kernel": "gemm1_swiglu", "achieved": round(g1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(spec_name),
                      "bytes_per_launch": int(g1_bytes)},
     }
 
