@@ -18,6 +18,8 @@
 // requantises the 32 columns as one MX FP8 block.
 // GEMM2 tile: 64 output columns, four 16-row MFMA groups of W2; y rows are
 // kept in float32 for the combine.
+#include <cmath>
+
 #include "moe_common.hpp"
 
 namespace moe {
@@ -25,6 +27,13 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+// Resident wavefronts per SIMD the skinny GEMM1 is compiled for (register
+// budget 512 / kGemm1Waves per lane): three wavefronts with two K steps in
+// flight each stream W13 faster than four with one (measured on the
+// 7168 x 3072 decode shape: 183 against 199 us; one row block per chunk).
+// GEMM2, whose items are a
+// third as long, is faster with the plain loop at four wavefronts.
+constexpr int kGemm1Waves = 3;
 
 __device__ __forceinline__ v8i load_fp4_frag(const uint8_t *p)
 {
@@ -78,6 +87,94 @@ __device__ __forceinline__ void reduce_waves(v4f (&acc)[NMB][4], float *red, int
             }
         }
         __syncthreads();
+    }
+}
+
+// Operands of one K step (128 K values) of an item: four 16-row FP4 weight
+// fragments and one 16-row FP8 activation fragment per row block, with their
+// exponents.
+template <int NMB>
+struct KStep {
+    v8i a[4];
+    int sa[4];
+    v8i b[NMB];
+    int sb[NMB];
+};
+
+// Where this lane's operands of an item are at K step 0: weight codes at
+// wbase + woff[g] and activation codes at xbase + xoff[mb] (workgroup-uniform
+// bases, 32-bit lane offsets), exponents in LDS at wsp[g] / xsp[mb].
+template <int NMB>
+struct KPtrs {
+    const uint8_t *wbase, *xbase;
+    uint32_t woff[4], xoff[NMB];
+    const uint8_t *wsp[4], *xsp[NMB];
+};
+
+template <int NMB>
+__device__ __forceinline__ void fetch_step(KStep<NMB> &f, const KPtrs<NMB> &p, int ks)
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        f.a[g] = load_fp4_frag(p.wbase + (p.woff[g] + (uint32_t)ks * 64u));
+        f.sa[g] = p.wsp[g][ks * 4];
+    }
+    // every row block is loaded (offsets of missing rows repeat the last
+    // row), so the loads of a step are unconditional
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        f.b[mb] = load_fp8_frag(p.xbase + (p.xoff[mb] + (uint32_t)ks * 128u));
+        f.sb[mb] = p.xsp[mb][ks * 4];
+    }
+}
+
+template <int NMB>
+__device__ __forceinline__ void mma_step(v4f (&acc)[NMB][4], const KStep<NMB> &f, int nmb_act)
+{
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        if (mb < nmb_act) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                acc[mb][g] = mfma_w4a8(f.a[g], f.b[mb], acc[mb][g], f.sa[g], f.sb[mb]);
+        }
+    }
+}
+
+// This wavefront's K steps ks = wave, wave + 4, ... < KS.  With kPrefetch
+// the loads of the next step are in flight while the current step's MFMAs
+// run (twice the bytes in flight per wavefront, at the price of the
+// registers of a second step).
+template <bool kPrefetch, int NMB>
+__device__ __forceinline__ void k_loop(v4f (&acc)[NMB][4], const KPtrs<NMB> &p, int KS, int wave,
+                                       int nmb_act)
+{
+    if (!kPrefetch) {
+        for (int ks = wave; ks < KS; ks += 4) {
+            KStep<NMB> f;
+            fetch_step(f, p, ks);
+            mma_step(acc, f, nmb_act);
+        }
+        return;
+    }
+    const int n = wave < KS ? (KS - wave + 3) / 4 : 0;
+    if (n == 0)
+        return;
+    KStep<NMB> f0, f1;
+    fetch_step(f0, p, wave);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+        fetch_step(f1, p, wave + 4 * (j + 1));
+        mma_step(acc, f0, nmb_act);
+        fetch_step(f0, p, wave + 4 * (j + 2));
+        mma_step(acc, f1, nmb_act);
+    }
+    if (j + 1 < n) {
+        fetch_step(f1, p, wave + 4 * (j + 1));
+        mma_step(acc, f0, nmb_act);
+        mma_step(acc, f1, nmb_act);
+    } else {
+        mma_step(acc, f0, nmb_act);
     }
 }
 
@@ -138,22 +235,20 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
     });
     __syncthreads();
 
-    const uint8_t *wp[4];
-    const uint8_t *wsp[4];
+    KPtrs<NMB> kp;
+    kp.wbase = p.w13 + ((size_t)e * 2 * I + j0) * (size_t)(H / 2);
+    kp.xbase = p.x;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const size_t wrow = (size_t)e * 2 * I + (g >= 2 ? I : 0) + j0 + 16 * (g & 1) + i16;
-        wp[g] = p.w13 + wrow * (size_t)(H / 2) + kq * 16;
-        wsp[g] = wexp + (g * 16 + i16) * es + kq;
+        const uint32_t r = (g >= 2 ? I : 0) + 16 * (g & 1) + i16;
+        kp.woff[g] = r * (uint32_t)(H / 2) + kq * 16;
+        kp.wsp[g] = wexp + (g * 16 + i16) * es + kq;
     }
-    const uint8_t *xp[NMB];
-    const uint8_t *xsp[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
         const int rloc = min(mb * 16 + i16, nrows - 1);
-        const size_t t = (size_t)tok[rloc];
-        xp[mb] = p.x + t * (size_t)H + kq * 16;
-        xsp[mb] = xexp + rloc * es + kq;
+        kp.xoff[mb] = (uint32_t)tok[rloc] * (uint32_t)H + kq * 16;
+        kp.xsp[mb] = xexp + rloc * es + kq;
     }
 
     v4f acc[NMB][4];
@@ -162,26 +257,7 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int ks = wave; ks < KS; ks += 4) {
-        v8i a[4];
-        int sa[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            a[g] = load_fp4_frag(wp[g] + ks * 64);
-            sa[g] = wsp[g][ks * 4];
-        }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-            if (mb < nmb_act) {
-                const v8i b = load_fp8_frag(xp[mb] + ks * 128);
-                const int sb = xsp[mb][ks * 4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
-            }
-        }
-    }
+    k_loop<NMB == 1, NMB>(acc, kp, KS, wave, nmb_act);
     reduce_waves<NMB>(acc, red, nmb_act);
 
     // epilogue: wavefront w finishes row block w
@@ -244,22 +320,19 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
     });
     __syncthreads();
 
-    const uint8_t *wp[4];
-    const uint8_t *wsp[4];
+    KPtrs<NMB> kp;
+    kp.wbase = p.w2 + ((size_t)e * H + n0) * (size_t)(I / 2);
+    kp.xbase = p.h + (size_t)row0 * (size_t)I;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const size_t wrow = (size_t)e * H + n0 + 16 * g + i16;
-        wp[g] = p.w2 + wrow * (size_t)(I / 2) + kq * 16;
-        wsp[g] = wexp + (16 * g + i16) * es + kq;
+        kp.woff[g] = (uint32_t)(16 * g + i16) * (uint32_t)(I / 2) + kq * 16;
+        kp.wsp[g] = wexp + (16 * g + i16) * es + kq;
     }
-    const uint8_t *hp[NMB];
-    const uint8_t *hsp[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
         const int rloc = min(mb * 16 + i16, nrows - 1);
-        const size_t row = (size_t)(row0 + rloc);
-        hp[mb] = p.h + row * (size_t)I + kq * 16;
-        hsp[mb] = hexp + rloc * es + kq;
+        kp.xoff[mb] = (uint32_t)rloc * (uint32_t)I + kq * 16;
+        kp.xsp[mb] = hexp + rloc * es + kq;
     }
 
     v4f acc[NMB][4];
@@ -268,26 +341,7 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             acc[mb][g] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int ks = wave; ks < KS; ks += 4) {
-        v8i a[4];
-        int sa[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            a[g] = load_fp4_frag(wp[g] + ks * 64);
-            sa[g] = wsp[g][ks * 4];
-        }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-            if (mb < nmb_act) {
-                const v8i b = load_fp8_frag(hp[mb] + ks * 128);
-                const int sb = hsp[mb][ks * 4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    acc[mb][g] = mfma_w4a8(a[g], b, acc[mb][g], sa[g], sb);
-            }
-        }
-    }
+    k_loop<false, NMB>(acc, kp, KS, wave, nmb_act);
     reduce_waves<NMB>(acc, red, nmb_act);
 
     if (wave < nmb_act) {
@@ -306,7 +360,7 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
 }
 
 template <int NMB>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMB == 4 ? 2 : kGemm1Waves)))
 gemm1_skinny_kernel(Shape s, LayerPtrs p)
 {
     constexpr int CH = 16 * NMB;
@@ -483,13 +537,16 @@ bool use_tiled_gemm1(const moe_shape &s) { return rows_per_expert(s) > 24.0; }
 
 bool use_tiled_gemm2(const moe_shape &s) { return rows_per_expert(s) > 24.0 && s.H % 256 == 0; }
 
-// Rows per chunk: enough for the expected rows of an expert, at most 64.
+// Rows per chunk: enough for nearly every expert's rows in one pass over its
+// weights (mean + 3 standard deviations of the binomial route count, + 1),
+// at most 64; a second chunk of an expert streams its weights again.
 int pick_nmb(const moe_shape &s)
 {
-    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
-    if (per_expert <= 16.0)
+    const double mu = rows_per_expert(s);
+    const double need = mu + 3.0 * std::sqrt(mu) + 1.0;
+    if (need <= 16.0)
         return 1;
-    if (per_expert <= 32.0)
+    if (need <= 32.0)
         return 2;
     return 4;
 }
