@@ -533,9 +533,13 @@ double rows_per_expert(const moe_shape &s)
     return (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
 }
 
-bool use_tiled_gemm1(const moe_shape &s) { return rows_per_expert(s) > 24.0; }
+// The tiled kernels need a contraction of at least four K steps (512).
+bool use_tiled_gemm1(const moe_shape &s) { return rows_per_expert(s) > 24.0 && s.H >= 512; }
 
-bool use_tiled_gemm2(const moe_shape &s) { return rows_per_expert(s) > 24.0 && s.H % 256 == 0; }
+bool use_tiled_gemm2(const moe_shape &s)
+{
+    return rows_per_expert(s) > 24.0 && s.H % 256 == 0 && s.I >= 512;
+}
 
 // Rows per chunk: enough for nearly every expert's rows in one pass over its
 // weights (mean + 3 standard deviations of the binomial route count, + 1),

@@ -30,17 +30,18 @@ constexpr int kGroups = kBN / 16; // 16-row MFMA groups per tile
 template <int BM>
 struct TileLds {
     static constexpr int kW = kBN * 64;   // FP4 weight tile, one K step
-    static constexpr int kX = BM * 128;   // FP8 activation tile
-    static constexpr int kWE = kBN * 4;   // weight exponents (4 blocks per row)
-    static constexpr int kXE = BM * 4;    // activation exponents
-    static constexpr int kStage = kW + kX + kWE + kXE;
+    static constexpr int kX = BM * 128;   // FP8 activation rows, one K step
+    static constexpr int kStage = kW + kX;
     static constexpr int kStages = 3;     // K steps resident in LDS
-    // loads one wavefront issues per stage: 4 weight fragments, BM/32
-    // activation fragment halves, one weight-exponent and one activation-
-    // exponent dword load (wavefront v brings activation exponent rows
-    // 64 (v mod BM/64) + l: when BM < 256 two wavefronts write the same
-    // bytes to the same place)
-    static constexpr int kLoads = 4 + BM / 32 + 2;
+    static constexpr int kWE = kBN * 16;  // weight exponents of four K steps
+    static constexpr int kXE = BM * 16;   // activation exponents of four K steps
+    static constexpr int kExp = kWE + kXE;
+    static constexpr int kExpSlots = 2;
+    // loads one wavefront issues per K step (4 weight instructions, BM/32
+    // activation instructions) and per four K steps (one weight-exponent and
+    // one activation-exponent instruction)
+    static constexpr int kDataLoads = 4 + BM / 32;
+    static constexpr int kExpLoads = 2;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -104,7 +105,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
     using L = TileLds<BM>;
     constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
     constexpr int NS = L::kStages;
-    __shared__ __align__(16) uint8_t lds[NS * L::kStage];
+    __shared__ __align__(16) uint8_t lds[NS * L::kStage + L::kExpSlots * L::kExp];
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int arow[BM];                // activation row of each tile row
 
@@ -140,43 +141,63 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             }
             return (uint32_t)(e * H + nt * kBN + r);
         };
-        // This wavefront's loads of one stage.  Weight fragment g = wave + 4i:
-        // lane l brings row 16g + (l & 15), K bytes 16 (l >> 4) .. of the step.
-        // Activation fragment half f = wave + 4i (tile block f/2, half f%2):
-        // lane l = j + 16c brings row 16(f/2) + j, K bytes 16(4(f%2) + c) ..
+        // LDS layout of a stage: weight group g (tile rows 16g..16g+15) at
+        // 1024 g as 64-byte rows, activation tile row R at kW + 128 R; the
+        // 16-byte chunk c of a row sits at position c ^ swz(row) with
+        // swz = (row >> 1) & 3 (weights) or (row >> 1) & 7 (activations), so
+        // the MFMA fragment reads below hit every LDS bank once.  Loads are
+        // row-major (four or eight consecutive lanes cover one row), which
+        // the global-to-LDS path moves several times faster than lanes
+        // walking down the rows.
+        //
+        // Weight instruction i brings group g = wave + 4i: lane l -> row
+        // 16g + (l >> 2), chunk (l & 3) ^ swz.  Activation instruction i
+        // brings tile rows 8h.. with h = wave + 4i: lane l -> row
+        // R = 8h + (l >> 3), chunk (l & 7) ^ swz.
         uint32_t woff[4], xoff[TB];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int g = wave + 4 * i;
-            woff[i] = wrow_of(16 * g + i16) * (uint32_t)(KT / 2) + 16u * kq;
+            const int g = wave + 4 * i, rr = lane >> 2;
+            const int c = (lane & 3) ^ ((rr >> 1) & 3);
+            woff[i] = wrow_of(16 * g + rr) * (uint32_t)(KT / 2) + 16u * (uint32_t)c;
         }
 #pragma unroll
         for (int i = 0; i < TB; ++i) {
-            const int f = wave + 4 * i;
-            xoff[i] = (uint32_t)arow[16 * (f >> 1) + i16] * (uint32_t)KT +
-                      16u * (uint32_t)(4 * (f & 1) + kq);
+            const int h = wave + 4 * i, R = 8 * h + (lane >> 3);
+            const int c = (lane & 7) ^ ((R >> 1) & 7);
+            xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)c;
         }
-        // exponents: wavefront v brings weight rows 64v + l and activation
-        // rows 64 (v mod BM/64) + l, four bytes (one K step) each
+        // exponents, four K steps (16 bytes) per row at a time: wavefront v
+        // brings weight rows 64v + l and activation rows 64 (v mod BM/64) + l
+        // (when BM < 256 two wavefronts write the same bytes to the same
+        // place).  The last group of a row is read from 16 bytes before the
+        // row's end, so no read passes it (KS >= 4).
         const int xe_wave = wave % (BM / 64);
         const uint32_t weoff = wrow_of(64 * wave + lane) * (uint32_t)(KT / 32);
         const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
+        auto ebase = [&](int grp) -> int { return min(16 * grp, KT / 32 - 16); };
 
-        const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + 1024u * wave);
-        const uint32_t lds_wexp =
-            __builtin_amdgcn_readfirstlane(lds_addr(lds) + L::kW + L::kX + 256u * wave);
-        const uint32_t lds_xexp = __builtin_amdgcn_readfirstlane(lds_addr(lds) + L::kW + L::kX +
-                                                                 L::kWE + 256u * xe_wave);
+        const uint32_t lds0 = lds_addr(lds);
+        const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds0 + 1024u * wave);
+        const uint32_t lds_x = __builtin_amdgcn_readfirstlane(lds0 + L::kW + 1024u * wave);
+        const uint32_t lds_e = lds0 + NS * L::kStage;
+        const uint32_t lds_we = __builtin_amdgcn_readfirstlane(lds_e + 1024u * wave);
+        const uint32_t lds_xe = __builtin_amdgcn_readfirstlane(lds_e + L::kWE + 1024u * xe_wave);
         auto issue = [&](int ks) {
             const uint32_t st = (uint32_t)((ks % NS) * L::kStage);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_wave + st + 4096u * i);
+                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_w + st + 4096u * i);
 #pragma unroll
             for (int i = 0; i < TB; ++i)
-                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_wave + st + L::kW + 4096u * i);
-            g2lds<4>(ws, weoff + (uint32_t)ks * 4u, lds_wexp + st);
-            g2lds<4>(act_s, xeoff + (uint32_t)ks * 4u, lds_xexp + st);
+                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_x + st + 4096u * i);
+            if ((ks & 3) == 0) {
+                const int grp = ks >> 2;
+                const uint32_t es = (uint32_t)((grp % L::kExpSlots) * L::kExp);
+                const uint32_t eb = (uint32_t)ebase(grp);
+                g2lds<16>(ws, weoff + eb, lds_we + es);
+                g2lds<16>(act_s, xeoff + eb, lds_xe + es);
+            }
         };
 
         v4f acc[8][TB];
@@ -186,11 +207,13 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             for (int j = 0; j < TB; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // per-lane LDS offsets inside a stage
-        const int afrag = lane * 16 + wn * 8 * 1024;
-        const int bfrag = L::kW + lane * 16 + wm * TB * 2048;
-        const int wexp = L::kW + L::kX + i16 * 4 + kq + wn * 8 * 64;
-        const int xexp = L::kW + L::kX + L::kWE + i16 * 4 + kq + wm * TB * 64;
+        // per-lane LDS offsets of the fragment reads (see the layout above)
+        const int afrag = wn * 8 * 1024 + 64 * i16 + 16 * (kq ^ ((i16 >> 1) & 3));
+        const int xrow = wm * (BM / 2) + i16;
+        const int bfrag_lo = L::kW + 128 * xrow + 16 * (kq ^ ((i16 >> 1) & 7));
+        const int bfrag_hi = L::kW + 128 * xrow + 16 * ((kq + 4) ^ ((i16 >> 1) & 7));
+        const int wexp = NS * L::kStage + 16 * (wn * 128 + i16) + kq;
+        const int xexp = NS * L::kStage + L::kWE + 16 * xrow + kq;
 
 #pragma unroll
         for (int p = 0; p < NS - 1; ++p)
@@ -198,30 +221,33 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                 issue(p);
         for (int ks = 0; ks < KS; ++ks) {
             // this wavefront's loads of step ks are done once at most the
-            // later stages' loads are outstanding; then all wavefronts' are
-            if (ks + NS - 2 < KS)
-                wait_vmcnt<(NS - 2) * L::kLoads>();
-            else
+            // loads of step ks+1 are outstanding; then all wavefronts' are
+            if (ks + 1 >= KS)
                 wait_vmcnt<0>();
+            else if (((ks + 1) & 3) == 0)
+                wait_vmcnt<L::kDataLoads + L::kExpLoads>();
+            else
+                wait_vmcnt<L::kDataLoads>();
             raw_barrier();
             if (ks + NS - 1 < KS)
                 issue(ks + NS - 1);
             const uint8_t *st = lds + (ks % NS) * L::kStage;
+            const uint8_t *ex = lds + ((ks >> 2) % L::kExpSlots) * L::kExp + (4 * ks - ebase(ks >> 2));
             v8i b[TB];
             int sb[TB];
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
-                const u32x4 lo = lds_read16(st + bfrag + j * 2048);
-                const u32x4 hi = lds_read16(st + bfrag + j * 2048 + 1024);
+                const u32x4 lo = lds_read16(st + bfrag_lo + j * 2048);
+                const u32x4 hi = lds_read16(st + bfrag_hi + j * 2048);
                 b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                sb[j] = st[xexp + j * 64];
+                sb[j] = ex[xexp + j * 256];
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const u32x4 a4 = lds_read16(st + afrag + i * 1024);
                 const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-                const int sa = st[wexp + i * 64];
+                const int sa = ex[wexp + i * 256];
 #pragma unroll
                 for (int j = 0; j < TB; ++j)
                     acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
