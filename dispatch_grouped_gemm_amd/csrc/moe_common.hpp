@@ -127,11 +127,14 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float gl, floa
 // ---------------------------------------------------------------------------
 // Row chunks of the expert segments: every workgroup derives the same plan
 // from counts.  prefix[e] = first chunk of expert e, prefix[E] = total.
+// NT = threads of the workgroup (a multiple of 64, at most 1024); each
+// thread sums up to 4 experts, which covers E_local <= 512 for NT >= 128.
 // ---------------------------------------------------------------------------
+template <int NT = 256>
 __device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict__ counts, int ch,
                                            int *prefix)
 {
-    // 256 threads, E_local <= 1024: each thread sums up to 4 experts (512 used)
+    static_assert(NT % 64 == 0 && NT >= 128 && NT <= 1024, "plan_chunks: workgroup size");
     const int tid = threadIdx.x;
     const int E = s.E_local;
     int local[4];
@@ -143,7 +146,7 @@ __device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict
         local[i] = n;
         sum += n;
     }
-    // inclusive scan of sum over the 256 threads
+    // inclusive scan of sum over the NT threads
     const int lane = tid & 63, wave = tid >> 6;
     int inc = sum;
 #pragma unroll
@@ -152,7 +155,7 @@ __device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict
         if (lane >= d)
             inc += o;
     }
-    __shared__ int wtot[4];
+    __shared__ int wtot[NT / 64];
     if (lane == 63)
         wtot[wave] = inc;
     __syncthreads();
@@ -167,7 +170,7 @@ __device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict
             prefix[e] = run;
         run += local[i];
     }
-    if (tid == 255)
+    if (tid == NT - 1)
         prefix[E] = base + inc;
     __syncthreads();
     return prefix[E];
