@@ -1,12 +1,15 @@
 // Expert GEMMs for many rows per expert: LDS-tiled scaled FP4 x FP8 MFMA.
 //
 // A workgroup computes a tile of 256 weight rows x BM dispatched rows of one
-// expert.  Its eight wavefronts (two per SIMD) form a 2 x 4 grid: wavefront
-// (wn, wm) owns weight rows [128 wn, 128 wn + 128) of the tile (eight
-// 16-row MFMA groups) and dispatched rows [wm BM/4, (wm+1) BM/4).  Every K
-// step of 128 is brought into LDS with direct global-to-LDS loads, three
-// steps deep, and read from there in MFMA fragment order (see the layout
-// notes in the kernel).
+// expert.  Its four wavefronts form a 2 x 2 grid: wavefront (wn, wm) owns
+// weight rows [128 wn, 128 wn + 128) of the tile (eight 16-row MFMA groups)
+// and dispatched rows [wm BM/2, (wm+1) BM/2).  Every K step of 128 is
+// brought into LDS with direct global-to-LDS loads, double-buffered: the
+// loads of step k+1 are in flight while step k is computed.  Each workgroup
+// fits in half a CU's LDS and registers, so two independent workgroups share
+// every CU: while one waits at its barrier or on LDS, the other's MFMAs run
+// (measured faster than one workgroup of eight wavefronts, whose halves wait
+// at the same barriers, and than three-stage rings at one workgroup per CU).
 //
 // GEMM1 tile: 128 intermediate columns j0..j0+127.  Wavefront wn holds the
 // 64 columns j0+64wn.. as four gate groups and the four matching up groups,
@@ -22,9 +25,7 @@ namespace moe {
 
 namespace {
 
-// Eight wavefronts, two per SIMD: while one waits for LDS or the barrier
-// the other keeps the matrix unit busy.
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kBN = 256;          // weight rows per tile
 constexpr int kGroups = kBN / 16; // 16-row MFMA groups per tile
 
@@ -33,16 +34,16 @@ struct TileLds {
     static constexpr int kW = kBN * 64;   // FP4 weight tile, one K step
     static constexpr int kX = BM * 128;   // FP8 activation rows, one K step
     static constexpr int kStage = kW + kX;
-    static constexpr int kStages = 3;     // K steps resident in LDS (at most 4)
+    static constexpr int kStages = 2;     // K steps resident in LDS (2 to 4)
     static constexpr int kWE = kBN * 16;  // weight exponents of four K steps
     static constexpr int kXE = BM * 16;   // activation exponents of four K steps
     static constexpr int kExp = kWE + kXE;
     static constexpr int kExpSlots = 2;
-    // loads one wavefront issues per K step (2 weight instructions, BM/64
-    // activation instructions) and per four K steps (one exponent
-    // instruction: weight rows on wavefronts 0-3, activation rows on 4-7)
-    static constexpr int kDataLoads = 2 + BM / 64;
-    static constexpr int kExpLoads = 1;
+    // loads one wavefront issues per K step (4 weight instructions, BM/32
+    // activation instructions) and per four K steps (one weight-exponent and
+    // one activation-exponent instruction)
+    static constexpr int kDataLoads = 4 + BM / 32;
+    static constexpr int kExpLoads = 2;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -119,24 +120,20 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                   uint8_t *__restrict__ hs_out, float *__restrict__ y_out)
 {
     using L = TileLds<BM>;
-    constexpr int TB = BM / 64;             // 16-row activation blocks per wavefront
-    constexpr int XI = BM / 64;             // activation load instructions per wavefront
+    constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
     constexpr int NS = L::kStages;
     __shared__ __align__(16) uint8_t lds[NS * L::kStage + L::kExpSlots * L::kExp];
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int arow[BM];                // activation row of each tile row
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
-    // wavefront (wn, wm): weight rows [128 wn, 128 wn + 128) of the tile,
-    // dispatched rows [wm BM/4, (wm+1) BM/4)
     const int wn = wave & 1, wm = wave >> 1;
     const int H = s.H, I = s.I;
     const int KT = kGemm1 ? H : I;          // contraction length
     const int KS = KT / 128;
     const int NT = kGemm1 ? I / 128 : H / kBN;
-    const int nchunks = plan_chunks<kThreads>(s, counts, BM, prefix);
+    const int nchunks = plan_chunks(s, counts, BM, prefix);
     const long items = (long)nchunks * NT;
 
     for (long item = blockIdx.x; item < items; item += gridDim.x) {
@@ -170,53 +167,53 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         // the global-to-LDS path moves several times faster than lanes
         // walking down the rows.
         //
-        // Weight instruction i brings group g = wave + 8i: lane l -> row
+        // Weight instruction i brings group g = wave + 4i: lane l -> row
         // 16g + (l >> 2), chunk (l & 3) ^ swz.  Activation instruction i
-        // brings tile rows 8h.. with h = wave + 8i: lane l -> row
+        // brings tile rows 8h.. with h = wave + 4i: lane l -> row
         // R = 8h + (l >> 3), chunk (l & 7) ^ swz.
-        uint32_t woff[2], xoff[XI];
+        uint32_t woff[4], xoff[TB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = wave + 8 * i, rr = lane >> 2;
+        for (int i = 0; i < 4; ++i) {
+            const int g = wave + 4 * i, rr = lane >> 2;
             const int c = (lane & 3) ^ ((rr >> 1) & 3);
             woff[i] = wrow_of(16 * g + rr) * (uint32_t)(KT / 2) + 16u * (uint32_t)c;
         }
 #pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int h = wave + 8 * i, R = 8 * h + (lane >> 3);
+        for (int i = 0; i < TB; ++i) {
+            const int h = wave + 4 * i, R = 8 * h + (lane >> 3);
             const int c = (lane & 7) ^ ((R >> 1) & 7);
             xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)c;
         }
-        // exponents, four K steps (16 bytes) per row at a time: wavefront
-        // v < 4 brings weight rows 64v + l, wavefront v >= 4 activation rows
-        // 64 ((v-4) mod BM/64) + l (when BM < 256 two wavefronts write the
-        // same bytes to the same place).  The last group of a row is read
-        // from 16 bytes before the row's end, so no read passes it (KS >= 4).
-        const bool wexp_wave = wave < 4;
-        const int xe_blk = (wave - 4) % (BM / 64);
-        const uint32_t eoff = wexp_wave ? wrow_of(64 * wave + lane) * (uint32_t)(KT / 32)
-                                   : (uint32_t)arow[64 * xe_blk + lane] * (uint32_t)(KT / 32);
-        const uint8_t *esrc = wexp_wave ? ws : act_s;
+        // exponents, four K steps (16 bytes) per row at a time: wavefront v
+        // brings weight rows 64v + l and activation rows 64 (v mod BM/64) + l
+        // (when BM < 256 two wavefronts write the same bytes to the same
+        // place).  The last group of a row is read from 16 bytes before the
+        // row's end, so no read passes it (KS >= 4).
+        const int xe_wave = wave % (BM / 64);
+        const uint32_t weoff = wrow_of(64 * wave + lane) * (uint32_t)(KT / 32);
+        const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
         auto ebase = [&](int grp) -> int { return min(16 * grp, KT / 32 - 16); };
 
         const uint32_t lds0 = lds_addr(lds);
         const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds0 + 1024u * wave);
         const uint32_t lds_x = __builtin_amdgcn_readfirstlane(lds0 + L::kW + 1024u * wave);
         const uint32_t lds_e = lds0 + NS * L::kStage;
-        const uint32_t lds_edst = __builtin_amdgcn_readfirstlane(
-            wexp_wave ? lds_e + 1024u * wave : lds_e + L::kWE + 1024u * xe_blk);
+        const uint32_t lds_we = __builtin_amdgcn_readfirstlane(lds_e + 1024u * wave);
+        const uint32_t lds_xe = __builtin_amdgcn_readfirstlane(lds_e + L::kWE + 1024u * xe_wave);
         auto issue = [&](int ks) {
             const uint32_t st = (uint32_t)((ks % NS) * L::kStage);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_w + st + 8192u * i);
+            for (int i = 0; i < 4; ++i)
+                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_w + st + 4096u * i);
 #pragma unroll
-            for (int i = 0; i < XI; ++i)
-                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_x + st + 8192u * i);
+            for (int i = 0; i < TB; ++i)
+                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_x + st + 4096u * i);
             if ((ks & 3) == 0) {
                 const int grp = ks >> 2;
                 const uint32_t es = (uint32_t)((grp % L::kExpSlots) * L::kExp);
-                g2lds<16>(esrc, eoff + (uint32_t)ebase(grp), lds_edst + es);
+                const uint32_t eb = (uint32_t)ebase(grp);
+                g2lds<16>(ws, weoff + eb, lds_we + es);
+                g2lds<16>(act_s, xeoff + eb, lds_xe + es);
             }
         };
 
@@ -229,7 +226,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
 
         // per-lane LDS offsets of the fragment reads (see the layout above)
         const int afrag = wn * 8 * 1024 + 64 * i16 + 16 * (kq ^ ((i16 >> 1) & 3));
-        const int xrow = wm * (BM / 4) + i16;
+        const int xrow = wm * (BM / 2) + i16;
         const int bfrag_lo = L::kW + 128 * xrow + 16 * (kq ^ ((i16 >> 1) & 7));
         const int bfrag_hi = L::kW + 128 * xrow + 16 * ((kq + 4) ^ ((i16 >> 1) & 7));
         const int wexp = NS * L::kStage + 16 * (wn * 128 + i16) + kq;
@@ -281,7 +278,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         if (kGemm1) {
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
-                const int m = wm * (BM / 4) + 16 * j + i16;
+                const int m = wm * (BM / 2) + 16 * j + i16;
                 float hv[4][4];
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
@@ -320,7 +317,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         } else {
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
-                const int m = wm * (BM / 4) + 16 * j + i16;
+                const int m = wm * (BM / 2) + 16 * j + i16;
                 if (m < nrows) {
                     float *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * kBN +
                                 128 * wn + 4 * kq;
