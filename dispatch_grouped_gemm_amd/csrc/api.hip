@@ -12,6 +12,15 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// The kernels move codes, exponents and rows in 16-byte pieces.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename... P>
+bool all_aligned16(const P *...p)
+{
+    return (aligned16(p) && ...);
+}
+
 // Byte layout of the moe_forward workspace.
 struct Layout {
     size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, total;
@@ -135,6 +144,8 @@ int moe_gemm1_swiglu(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
         return MOE_OK;
     if (!x || !xs || !counts || !offsets || !row_route || !w13 || !w13s || !h || !hs)
         return MOE_EINVAL;
+    if (!all_aligned16(x, xs, w13, w13s, h, hs))
+        return MOE_EINVAL;
     return hip_status(moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
                                         as_stream(stream)));
 }
@@ -150,6 +161,8 @@ int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int
         return MOE_OK;
     if (!h || !hs || !counts || !offsets || !w2 || !w2s || !y)
         return MOE_EINVAL;
+    if (!all_aligned16(h, hs, w2, w2s, y))
+        return MOE_EINVAL;
     return hip_status(
         moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, as_stream(stream)));
 }
@@ -164,6 +177,8 @@ int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, c
         return MOE_OK;
     if (!tw || !route_row || !y || !out)
         return MOE_EINVAL;
+    if (!all_aligned16(y, out))
+        return MOE_EINVAL;
     return hip_status(moe::launch_combine(*s, tw, route_row, y, out, as_stream(stream)));
 }
 
@@ -177,6 +192,8 @@ int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const i
     if (s->T == 0)
         return MOE_OK;
     if (!x || !xs || !ids || !tw || !w13 || !w13s || !w2 || !w2s || !out)
+        return MOE_EINVAL;
+    if (!all_aligned16(x, xs, w13, w13s, w2, w2s, out))
         return MOE_EINVAL;
     const Layout L = layout_of(*s);
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)

@@ -51,13 +51,32 @@ __device__ __forceinline__ v8i load_fp8_frag(const uint8_t *p)
                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// LDS row stride of staged exponent rows of a contraction of length k:
+// 16-byte aligned when the row (k/32 bytes) is a whole number of 16-byte
+// chunks, with 16 bytes of padding so the K loop's byte reads of sixteen
+// consecutive rows fall in different LDS banks; 4 bytes of padding else.
+__host__ __device__ constexpr int exp_stride(int k)
+{
+    return (k / 32) % 16 == 0 ? k / 32 + 16 : k / 32 + 4;
+}
+
 // Copy the E8M0 exponent rows of one item into LDS (row stride `stride`
 // bytes, `nbytes` used bytes per row, a multiple of 4): rows [0, nrows)
-// come from src_rows(r); the workgroup shares the copy.
+// come from src_row(r); the workgroup shares the copy, in 16-byte pieces
+// when the rows allow (a quarter of the load instructions), else in dwords.
 template <typename RowFn>
 __device__ __forceinline__ void stage_exponents(uint8_t *dst, int stride, int nbytes, int nrows,
                                                 RowFn src_row)
 {
+    if (nbytes % 16 == 0) {
+        const int pieces = nbytes >> 4;
+        for (int i = threadIdx.x; i < nrows * pieces; i += kThreads) {
+            const int r = i / pieces, c = i - r * pieces;
+            const uint4 v = reinterpret_cast<const uint4 *>(src_row(r))[c];
+            *reinterpret_cast<uint4 *>(dst + r * stride + 16 * c) = v;
+        }
+        return;
+    }
     const int words = nbytes >> 2;
     for (int i = threadIdx.x; i < nrows * words; i += kThreads) {
         const int r = i / words, c = i - r * words;
@@ -217,7 +236,7 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = H / 128;
-    const int es = H / 32 + 4;
+    const int es = exp_stride(H);
     uint8_t *wexp = exps, *xexp = exps + 64 * es;
     const int e = c.e, row0 = c.row0, nrows = c.nrows;
     const int nmb_act = (nrows + 15) >> 4;
@@ -299,7 +318,7 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
 }
 
 // GEMM2 of 64 output columns n0 = 64 nt .. of one row chunk (y in float32).
-// LDS: red[NMB*4*4*64], exps[(64 + 16 NMB) * (I/32 + 4)].
+// LDS: red[NMB*4*4*64], exps[(64 + 16 NMB) * exp_stride(I)].
 template <int NMB>
 __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, const Chunk &c,
                                            int nt, float *red, uint8_t *exps)
@@ -307,7 +326,7 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int H = s.H, I = s.I, KS = I / 128;
-    const int es = I / 32 + 4;
+    const int es = exp_stride(I);
     uint8_t *wexp = exps, *hexp = exps + 64 * es;
     const int e = c.e, row0 = c.row0, nrows = c.nrows;
     const int nmb_act = (nrows + 15) >> 4;
@@ -367,7 +386,7 @@ gemm1_skinny_kernel(Shape s, LayerPtrs p)
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int tok[CH];
     __shared__ float red[NMB * 4 * 4 * 64];
-    extern __shared__ uint8_t exps[];
+    extern __shared__ __align__(16) uint8_t exps[];
     const int nchunks = plan_chunks(s, p.counts, CH, prefix);
     const int NT = s.I / 32;
     const long items = (long)nchunks * NT;
@@ -384,7 +403,7 @@ gemm2_skinny_kernel(Shape s, LayerPtrs p)
     constexpr int CH = 16 * NMB;
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ float red[NMB * 4 * 4 * 64];
-    extern __shared__ uint8_t exps[];
+    extern __shared__ __align__(16) uint8_t exps[];
     const int nchunks = plan_chunks(s, p.counts, CH, prefix);
     const int NT = s.H / 64;
     const long items = (long)nchunks * NT;
@@ -449,7 +468,7 @@ fused_decode_kernel(Shape s, LayerPtrs p, int32_t *sync)
     __shared__ int tok[CH];
     __shared__ float red[NMB * 4 * 4 * 64];
     __shared__ int ticket;
-    extern __shared__ uint8_t exps[];
+    extern __shared__ __align__(16) uint8_t exps[];
     const int tid = threadIdx.x;
     // 1 in lane 0 of each wavefront, 0 elsewhere: a whole-wavefront atomic
     // add of `one` counts once per wavefront.
@@ -594,7 +613,7 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
 #define MOE_LAUNCH_G1(N)                                                                          \
     do {                                                                                          \
         auto k = gemm1_skinny_kernel<N>;                                                          \
-        const size_t lds = (size_t)(64 + 16 * N) * (sh.H / 32 + 4);                               \
+        const size_t lds = (size_t)(64 + 16 * N) * exp_stride(sh.H);                              \
         const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
         k<<<grid, kThreads, lds, st>>>(s, p);                                                     \
     } while (0)
@@ -628,7 +647,7 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
 #define MOE_LAUNCH_G2(N)                                                                          \
     do {                                                                                          \
         auto k = gemm2_skinny_kernel<N>;                                                          \
-        const size_t lds = (size_t)(64 + 16 * N) * (sh.I / 32 + 4);                               \
+        const size_t lds = (size_t)(64 + 16 * N) * exp_stride(sh.I);                              \
         const int grid = grid_for(k, chunk_upper_bound(sh, 16 * N) * nt, lds);                    \
         k<<<grid, kThreads, lds, st>>>(s, p);                                                     \
     } while (0)
@@ -691,7 +710,7 @@ hipError_t launch_fused_decode(const moe_shape &sh, const uint8_t *x, const uint
 #define MOE_LAUNCH_FUSED(N)                                                                       \
     do {                                                                                          \
         auto k = fused_decode_kernel<N>;                                                          \
-        const int es = (sh.H > sh.I ? sh.H : sh.I) / 32 + 4;                                      \
+        const int es = exp_stride(sh.H) > exp_stride(sh.I) ? exp_stride(sh.H) : exp_stride(sh.I); \
         const size_t lds = (size_t)(64 + 16 * N) * es;                                            \
         const int grid = grid_for(k, upper, lds);                                                 \
         k<<<grid, kThreads, lds, st>>>(s, p, sync);                                               \

@@ -46,6 +46,11 @@
  * Rows inside a compact segment are in ascending r (a stable scatter);
  * inside a fixed-slot segment their order is unspecified.
  *
+ * Alignment: the FP8, MXFP4 and E8M0 arrays (x_fp8, x_scale, w13,
+ * w13_scale, w2, w2_scale, h_fp8, h_scale), y_f32 and out_bf16 must start on
+ * a 16-byte boundary (PyTorch allocations do); a misaligned one is refused
+ * with MOE_EINVAL.
+ *
  * Ownership: the caller owns every buffer; pointers are device pointers
  * unless stated.  The library allocates nothing in these calls and keeps no
  * pointer after a call returns.  All calls are asynchronous on `stream`
@@ -68,7 +73,7 @@ extern "C" {
 #endif
 
 #define MOE_OK 0
-#define MOE_EINVAL (-1)     /* null pointer, negative size, bad enum */
+#define MOE_EINVAL (-1)     /* null or misaligned pointer, negative size, bad enum */
 #define MOE_ENOTSUP (-2)    /* shape outside what the kernels support */
 #define MOE_EWORKSPACE (-3) /* workspace missing or too small */
 #define MOE_EHIP (-4)       /* a HIP launch or query failed */

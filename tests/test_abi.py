@@ -82,6 +82,13 @@ def test_refusals_return_before_any_launch(lib):
     fake = ctypes.c_void_p(256)
     args = [fake] * 9
     assert lib.moe_forward(ctypes.byref(c), *args, fake, 16, null) == -3
+    # a pointer off a 16-byte boundary is refused before the workspace check
+    odd = ctypes.c_void_p(256 + 4)
+    assert lib.moe_forward(ctypes.byref(c), *([fake] * 8), odd, fake, 1 << 40, null) == -1
+    assert lib.moe_forward(ctypes.byref(c), odd, *([fake] * 8), fake, 1 << 40, null) == -1
+    assert lib.moe_gemm1_swiglu(ctypes.byref(c), *([fake] * 6), odd, fake, fake, null) == -1
+    assert lib.moe_gemm2(ctypes.byref(c), *([fake] * 6), odd, null) == -1
+    assert lib.moe_combine(ctypes.byref(c), fake, fake, odd, fake, null) == -1
     # T = 0 is a no-op for the steps that have nothing to do
     z = moe.MoeShape(**{**V4, "T": 0}).c()
     assert lib.moe_forward(ctypes.byref(z), *([null] * 10), 0, null) == 0
