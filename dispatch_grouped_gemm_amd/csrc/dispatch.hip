@@ -226,16 +226,29 @@ compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restric
 
 // Pass 2 (one workgroup): counts, offsets, status, and every workgroup's
 // first row per expert, written back over its histogram.
+template <bool kStaged>
 __global__ void __launch_bounds__(kThreads)
 compact_scan_kernel(Shape s, int nblk, int32_t *__restrict__ scratch, int32_t *__restrict__ counts,
                     int32_t *__restrict__ offsets, int32_t *__restrict__ status)
 {
+    // kStaged: the [nblk][E+1] table is copied to LDS first (coalesced), so
+    // the per-expert walk over the blocks runs at LDS rather than global
+    // memory latency, and copied back at the end
+    extern __shared__ int staged[];
     const int tid = threadIdx.x;
     const int E = s.E_local;
+    const int nval = nblk * (E + 1);
+    int32_t *tab = scratch;
+    if (kStaged) {
+        for (int i = tid; i < nval; i += kThreads)
+            staged[i] = scratch[i];
+        __syncthreads();
+        tab = staged;
+    }
     int cnt = 0;
     if (tid < E) {
         for (int b = 0; b < nblk; ++b) {
-            int32_t *p = scratch + (size_t)b * (E + 1) + tid;
+            int32_t *p = tab + (size_t)b * (E + 1) + tid;
             const int c = *p;
             *p = cnt;
             cnt += c;
@@ -247,15 +260,20 @@ compact_scan_kernel(Shape s, int nblk, int32_t *__restrict__ scratch, int32_t *_
         counts[tid] = cnt;
         offsets[tid] = off;
         for (int b = 0; b < nblk; ++b)
-            scratch[(size_t)b * (E + 1) + tid] += off;
+            tab[(size_t)b * (E + 1) + tid] += off;
     }
     if (tid == 0) {
         offsets[E] = total;
         int inv = 0;
         for (int b = 0; b < nblk; ++b)
-            inv += scratch[(size_t)b * (E + 1) + E];
+            inv += tab[(size_t)b * (E + 1) + E];
         status[0] = inv;
         status[1] = status[2] = status[3] = 0;
+    }
+    if (kStaged) {
+        __syncthreads();
+        for (int i = tid; i < nval; i += kThreads)
+            scratch[i] = staged[i];
     }
 }
 
@@ -438,7 +456,13 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
         const int nblk = large_blocks(sh);
         int32_t *blk = static_cast<int32_t *>(scratch);
         compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk);
-        compact_scan_kernel<<<1, kThreads, 0, st>>>(s, nblk, blk, counts, offsets, status);
+        const size_t table = (size_t)nblk * (E + 1) * sizeof(int);
+        if (table <= 64 * 1024)
+            compact_scan_kernel<true><<<1, kThreads, table, st>>>(s, nblk, blk, counts, offsets,
+                                                                   status);
+        else
+            compact_scan_kernel<false><<<1, kThreads, 0, st>>>(s, nblk, blk, counts, offsets,
+                                                                status);
         compact_scatter_kernel<<<nblk, kThreads, kWaves * E * sizeof(int), st>>>(
             s, ids, blk, row_route, route_row);
         return hipGetLastError();

@@ -125,24 +125,22 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float gl, floa
 }
 
 // ---------------------------------------------------------------------------
-// Row chunks of the expert segments: every workgroup derives the same plan
-// from counts.  prefix[e] = first chunk of expert e, prefix[E] = total.
+// Exclusive prefix over the local experts of f(e) >= 0, shared by the
+// workgroup: out[e] = sum of f over experts < e, out[E] = total (returned).
 // NT = threads of the workgroup (a multiple of 64, at most 1024); each
 // thread sums up to 4 experts, which covers E_local <= 512 for NT >= 128.
 // ---------------------------------------------------------------------------
-template <int NT = 256>
-__device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict__ counts, int ch,
-                                           int *prefix)
+template <int NT, typename F>
+__device__ __forceinline__ int scan_experts(int E, F f, int *out)
 {
-    static_assert(NT % 64 == 0 && NT >= 128 && NT <= 1024, "plan_chunks: workgroup size");
+    static_assert(NT % 64 == 0 && NT >= 128 && NT <= 1024, "scan_experts: workgroup size");
     const int tid = threadIdx.x;
-    const int E = s.E_local;
     int local[4];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = tid * 4 + i;
-        const int n = e < E ? (used_rows(s, counts[e]) + ch - 1) / ch : 0;
+        const int n = e < E ? f(e) : 0;
         local[i] = n;
         sum += n;
     }
@@ -167,13 +165,23 @@ __device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict
     for (int i = 0; i < 4; ++i) {
         const int e = tid * 4 + i;
         if (e < E)
-            prefix[e] = run;
+            out[e] = run;
         run += local[i];
     }
     if (tid == NT - 1)
-        prefix[E] = base + inc;
+        out[E] = base + inc;
     __syncthreads();
-    return prefix[E];
+    return out[E];
+}
+
+// Row chunks of the expert segments: every workgroup derives the same plan
+// from counts.  prefix[e] = first chunk of expert e, prefix[E] = total.
+template <int NT = 256>
+__device__ __forceinline__ int plan_chunks(const Shape &s, const int *__restrict__ counts, int ch,
+                                           int *prefix)
+{
+    return scan_experts<NT>(
+        s.E_local, [&](int e) { return (used_rows(s, counts[e]) + ch - 1) / ch; }, prefix);
 }
 
 // Expert owning chunk q: the last e with prefix[e] <= q.
