@@ -18,10 +18,10 @@ namespace {
 
 constexpr int kThreads = 1024; // 16 wavefronts
 constexpr int kWaves = kThreads / 64;
-constexpr int kSlotsPerWaveLarge = 256;
+constexpr int kSlotsPerWaveLarge = 128;
 constexpr int kSlotsPerBlockLarge = kWaves * kSlotsPerWaveLarge;
 // compact dispatch of at most this many slots runs in one workgroup
-constexpr long kSmallSlots = 16384;
+constexpr long kSmallSlots = 8192;
 
 struct Match {
     int rank;                 // lanes below with the same key
@@ -457,7 +457,7 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
         int32_t *blk = static_cast<int32_t *>(scratch);
         compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk);
         const size_t table = (size_t)nblk * (E + 1) * sizeof(int);
-        if (table <= 64 * 1024)
+        if (table <= 128 * 1024)
             compact_scan_kernel<true><<<1, kThreads, table, st>>>(s, nblk, blk, counts, offsets,
                                                                    status);
         else

@@ -26,23 +26,21 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 256;          // weight rows per tile
-constexpr int kGroups = kBN / 16; // 16-row MFMA groups per tile
-
-template <int BM>
+// Tile of BN weight rows (256 or 128) x BM dispatched rows (64 or 128).
+template <int BM, int BN>
 struct TileLds {
-    static constexpr int kW = kBN * 64;   // FP4 weight tile, one K step
+    static constexpr int kW = BN * 64;    // FP4 weight tile, one K step
     static constexpr int kX = BM * 128;   // FP8 activation rows, one K step
     static constexpr int kStage = kW + kX;
     static constexpr int kStages = 2;     // K steps resident in LDS (2 to 4)
-    static constexpr int kWE = kBN * 16;  // weight exponents of four K steps
+    static constexpr int kWE = BN * 16;   // weight exponents of four K steps
     static constexpr int kXE = BM * 16;   // activation exponents of four K steps
     static constexpr int kExp = kWE + kXE;
     static constexpr int kExpSlots = 2;
-    // loads one wavefront issues per K step (4 weight instructions, BM/32
+    // loads one wavefront issues per K step (BN/64 weight instructions, BM/32
     // activation instructions) and per four K steps (one weight-exponent and
     // one activation-exponent instruction)
-    static constexpr int kDataLoads = 4 + BM / 32;
+    static constexpr int kDataLoads = BN / 64 + BM / 32;
     static constexpr int kExpLoads = 2;
 };
 
@@ -111,7 +109,7 @@ __device__ __forceinline__ void wait_loads(int steps, int exps)
     }
 }
 
-template <bool kGemm1, int BM>
+template <bool kGemm1, int BM, int BN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__restrict__ act_s,
                   const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
@@ -119,7 +117,9 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                   const uint8_t *__restrict__ ws, uint8_t *__restrict__ h_out,
                   uint8_t *__restrict__ hs_out, float *__restrict__ y_out)
 {
-    using L = TileLds<BM>;
+    using L = TileLds<BM, BN>;
+    constexpr int GW = BN / 32;             // 16-row weight groups per wavefront
+    constexpr int WI = BN / 64;             // weight load instructions per wavefront
     constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
     constexpr int NS = L::kStages;
     __shared__ __align__(16) uint8_t lds[NS * L::kStage + L::kExpSlots * L::kExp];
@@ -132,7 +132,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
     const int H = s.H, I = s.I;
     const int KT = kGemm1 ? H : I;          // contraction length
     const int KS = KT / 128;
-    const int NT = kGemm1 ? I / 128 : H / kBN;
+    const int NT = kGemm1 ? I / (BN / 2) : H / BN;
     const int nchunks = plan_chunks(s, counts, BM, prefix);
     const long items = (long)nchunks * NT;
 
@@ -152,11 +152,13 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         auto wrow_of = [&](int r) -> uint32_t {
             const int grp = r >> 4, rr = r & 15;
             if (kGemm1) {
-                // group grp: wavefront half grp/8, up if (grp/4)&1, column block grp%4
-                const int half = grp >> 3, up = (grp >> 2) & 1, cb = grp & 3;
-                return (uint32_t)(e * 2 * I + (up ? I : 0) + nt * 128 + 64 * half + 16 * cb + rr);
+                // group grp: wavefront half grp / GW; within it GW/2 gate
+                // groups, then the GW/2 matching up groups
+                const int half = grp / GW, up = (grp % GW) >= GW / 2, cb = grp % (GW / 2);
+                return (uint32_t)(e * 2 * I + (up ? I : 0) + nt * (BN / 2) + (BN / 4) * half +
+                                  16 * cb + rr);
             }
-            return (uint32_t)(e * H + nt * kBN + r);
+            return (uint32_t)(e * H + nt * BN + r);
         };
         // LDS layout of a stage: weight group g (tile rows 16g..16g+15) at
         // 1024 g as 64-byte rows, activation tile row R at kW + 128 R; the
@@ -167,13 +169,13 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         // the global-to-LDS path moves several times faster than lanes
         // walking down the rows.
         //
-        // Weight instruction i brings group g = wave + 4i: lane l -> row
+        // Weight instruction i (< BN/64) brings group g = wave + 4i: lane l -> row
         // 16g + (l >> 2), chunk (l & 3) ^ swz.  Activation instruction i
         // brings tile rows 8h.. with h = wave + 4i: lane l -> row
         // R = 8h + (l >> 3), chunk (l & 7) ^ swz.
-        uint32_t woff[4], xoff[TB];
+        uint32_t woff[WI], xoff[TB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < WI; ++i) {
             const int g = wave + 4 * i, rr = lane >> 2;
             const int c = (lane & 3) ^ ((rr >> 1) & 3);
             woff[i] = wrow_of(16 * g + rr) * (uint32_t)(KT / 2) + 16u * (uint32_t)c;
@@ -185,12 +187,14 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)c;
         }
         // exponents, four K steps (16 bytes) per row at a time: wavefront v
-        // brings weight rows 64v + l and activation rows 64 (v mod BM/64) + l
-        // (when BM < 256 two wavefronts write the same bytes to the same
-        // place).  The last group of a row is read from 16 bytes before the
-        // row's end, so no read passes it (KS >= 4).
+        // brings weight rows 64 (v mod BN/64) + l and activation rows
+        // 64 (v mod BM/64) + l (where there are fewer than four such row
+        // blocks, two wavefronts write the same bytes to the same place).
+        // The last group of a row is read from 16 bytes before the row's
+        // end, so no read passes it (KS >= 4).
+        const int we_wave = wave % (BN / 64);
         const int xe_wave = wave % (BM / 64);
-        const uint32_t weoff = wrow_of(64 * wave + lane) * (uint32_t)(KT / 32);
+        const uint32_t weoff = wrow_of(64 * we_wave + lane) * (uint32_t)(KT / 32);
         const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
         auto ebase = [&](int grp) -> int { return min(16 * grp, KT / 32 - 16); };
 
@@ -198,12 +202,12 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds0 + 1024u * wave);
         const uint32_t lds_x = __builtin_amdgcn_readfirstlane(lds0 + L::kW + 1024u * wave);
         const uint32_t lds_e = lds0 + NS * L::kStage;
-        const uint32_t lds_we = __builtin_amdgcn_readfirstlane(lds_e + 1024u * wave);
+        const uint32_t lds_we = __builtin_amdgcn_readfirstlane(lds_e + 1024u * we_wave);
         const uint32_t lds_xe = __builtin_amdgcn_readfirstlane(lds_e + L::kWE + 1024u * xe_wave);
         auto issue = [&](int ks) {
             const uint32_t st = (uint32_t)((ks % NS) * L::kStage);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < WI; ++i)
                 g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_w + st + 4096u * i);
 #pragma unroll
             for (int i = 0; i < TB; ++i)
@@ -217,19 +221,19 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             }
         };
 
-        v4f acc[8][TB];
+        v4f acc[GW][TB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < GW; ++i)
 #pragma unroll
             for (int j = 0; j < TB; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
         // per-lane LDS offsets of the fragment reads (see the layout above)
-        const int afrag = wn * 8 * 1024 + 64 * i16 + 16 * (kq ^ ((i16 >> 1) & 3));
+        const int afrag = wn * GW * 1024 + 64 * i16 + 16 * (kq ^ ((i16 >> 1) & 3));
         const int xrow = wm * (BM / 2) + i16;
         const int bfrag_lo = L::kW + 128 * xrow + 16 * (kq ^ ((i16 >> 1) & 7));
         const int bfrag_hi = L::kW + 128 * xrow + 16 * ((kq + 4) ^ ((i16 >> 1) & 7));
-        const int wexp = NS * L::kStage + 16 * (wn * 128 + i16) + kq;
+        const int wexp = NS * L::kStage + 16 * (wn * (BN / 2) + i16) + kq;
         const int xexp = NS * L::kStage + L::kWE + 16 * xrow + kq;
 
 #pragma unroll
@@ -263,7 +267,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                 sb[j] = ex[xexp + j * 256];
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < GW; ++i) {
                 const u32x4 a4 = lds_read16(st + afrag + i * 1024);
                 const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
                 const int sa = ex[wexp + i * 256];
@@ -274,20 +278,21 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         }
 
         // epilogue: lane holds tile row (wm*BM/2 + 16j + i16), weight rows
-        // 4kq..4kq+3 of each of its eight groups
+        // 4kq..4kq+3 of each of its GW groups
         if (kGemm1) {
+            constexpr int CB = GW / 2;   // 16-column blocks of h per wavefront
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 const int m = wm * (BM / 2) + 16 * j + i16;
-                float hv[4][4];
+                float hv[CB][4];
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        hv[cb][v] = swiglu_clamped(acc[cb][j][v], acc[cb + 4][j][v], s.gate_limit,
-                                                   s.up_limit);
+                        hv[cb][v] = swiglu_clamped(acc[cb][j][v], acc[cb + CB][j][v],
+                                                   s.gate_limit, s.up_limit);
 #pragma unroll
-                for (int blk = 0; blk < 2; ++blk) {
+                for (int blk = 0; blk < CB / 2; ++blk) {
                     float amax = 0.0f;
 #pragma unroll
                     for (int cb = 2 * blk; cb < 2 * blk + 2; ++cb)
@@ -299,15 +304,15 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                     const int E = mx8_block_exponent(amax);
                     if (m < nrows) {
                         const size_t row = (size_t)(row0 + m);
-                        const int col0 = nt * 128 + 64 * wn + 32 * blk;
+                        const int col0 = nt * (BN / 2) + (BN / 4) * wn + 32 * blk;
 #pragma unroll
                         for (int cb = 2 * blk; cb < 2 * blk + 2; ++cb) {
                             uint32_t pk = 0;
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
                                 pk |= f32_to_e4m3(ldexpf(hv[cb][v], -E)) << (8 * v);
-                            *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + nt * 128 +
-                                                          64 * wn + 16 * cb + 4 * kq) = pk;
+                            *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + col0 +
+                                                          16 * (cb - 2 * blk) + 4 * kq) = pk;
                         }
                         if (kq == 0)
                             hs_out[row * (size_t)(I / 32) + col0 / 32] = (uint8_t)(E + 127);
@@ -319,10 +324,10 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             for (int j = 0; j < TB; ++j) {
                 const int m = wm * (BM / 2) + 16 * j + i16;
                 if (m < nrows) {
-                    float *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * kBN +
-                                128 * wn + 4 * kq;
+                    float *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * BN +
+                                (BN / 2) * wn + 4 * kq;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
+                    for (int i = 0; i < GW; ++i)
                         *reinterpret_cast<float4 *>(yr + 16 * i) =
                             float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                 }
@@ -362,45 +367,74 @@ int tiled_bm(const moe_shape &s)
     return per_expert <= 96.0 ? 64 : 128;
 }
 
+namespace {
+
+// Weight rows per tile: 256, or 128 when the expected number of items with
+// 256 would leave fewer than three rounds for the resident workgroups (two
+// per CU), so the last, partly filled round costs little.
+int tiled_bn(const moe_shape &s, bool gemm1)
+{
+    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+    const int bm = tiled_bm(s);
+    const double tiles = (double)s.E_local * (double)(long)((per_expert + bm - 1) / bm);
+    const double nt256 = gemm1 ? s.I / 128 : s.H / 256;
+    const bool fits256 = gemm1 ? s.I % 128 == 0 : s.H % 256 == 0;
+    if (!fits256)
+        return 128;
+    return tiles * nt256 < 3.0 * 2 * device_cu_count() ? 128 : 256;
+}
+
+template <bool kGemm1, int BM, int BN>
+hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
+                        const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
+                        const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, float *y,
+                        hipStream_t st)
+{
+    auto k = gemm_tiled_kernel<kGemm1, BM, BN>;
+    const long nt = kGemm1 ? sh.I / (BN / 2) : sh.H / BN;
+    const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt);
+    k<<<grid, kThreads, 0, st>>>(to_dev(sh), act, act_s, counts, offsets, row_route, w, ws, h, hs,
+                                 y);
+    return hipGetLastError();
+}
+
+template <bool kGemm1>
+hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
+                            const int32_t *counts, const int32_t *offsets,
+                            const int32_t *row_route, const uint8_t *w, const uint8_t *ws,
+                            uint8_t *h, uint8_t *hs, float *y, hipStream_t st)
+{
+    const int bm = tiled_bm(sh), bn = tiled_bn(sh, kGemm1);
+    if (bm == 64 && bn == 128)
+        return launch_tiled<kGemm1, 64, 128>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
+                                             hs, y, st);
+    if (bm == 64)
+        return launch_tiled<kGemm1, 64, 256>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
+                                             hs, y, st);
+    if (bn == 128)
+        return launch_tiled<kGemm1, 128, 128>(sh, act, act_s, counts, offsets, row_route, w, ws,
+                                              h, hs, y, st);
+    return launch_tiled<kGemm1, 128, 256>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
+                                          hs, y, st);
+}
+
+} // namespace
+
 hipError_t launch_gemm1_tiled(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
                               const int32_t *counts, const int32_t *offsets,
                               const int32_t *row_route, const uint8_t *w13, const uint8_t *w13s,
                               uint8_t *h, uint8_t *hs, hipStream_t st)
 {
-    const Shape s = to_dev(sh);
-    const long nt = sh.I / 128;
-    if (tiled_bm(sh) == 64) {
-        auto k = gemm_tiled_kernel<true, 64>;
-        const int grid = tiled_grid(k, tile_upper_bound(sh, 64) * nt);
-        k<<<grid, kThreads, 0, st>>>(s, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
-                                     nullptr);
-    } else {
-        auto k = gemm_tiled_kernel<true, 128>;
-        const int grid = tiled_grid(k, tile_upper_bound(sh, 128) * nt);
-        k<<<grid, kThreads, 0, st>>>(s, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
-                                     nullptr);
-    }
-    return hipGetLastError();
+    return launch_tiled_any<true>(sh, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
+                                  nullptr, st);
 }
 
 hipError_t launch_gemm2_tiled(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                               const uint8_t *w2s, float *y, hipStream_t st)
 {
-    const Shape s = to_dev(sh);
-    const long nt = sh.H / kBN;
-    if (tiled_bm(sh) == 64) {
-        auto k = gemm_tiled_kernel<false, 64>;
-        const int grid = tiled_grid(k, tile_upper_bound(sh, 64) * nt);
-        k<<<grid, kThreads, 0, st>>>(s, h, hs, counts, offsets, nullptr, w2, w2s, nullptr,
-                                     nullptr, y);
-    } else {
-        auto k = gemm_tiled_kernel<false, 128>;
-        const int grid = tiled_grid(k, tile_upper_bound(sh, 128) * nt);
-        k<<<grid, kThreads, 0, st>>>(s, h, hs, counts, offsets, nullptr, w2, w2s, nullptr,
-                                     nullptr, y);
-    }
-    return hipGetLastError();
+    return launch_tiled_any<false>(sh, h, hs, counts, offsets, nullptr, w2, w2s, nullptr,
+                                   nullptr, y, st);
 }
 
 } // namespace moe
