@@ -12,9 +12,11 @@ Reported (one JSON line):
   us_per_layer, routed_tflops, hbm_frac (all algorithmic bytes / 8 TB/s),
   mfma_frac (routed FLOP / 5.0 PFLOP/s dense FP8)
   roofline     the dominant kernel (GEMM1 + SwiGLU + requant): its
-               algorithmic bytes per launch / its mean launch time, the time
-               taken with HIP events on the launch stream over K back-to-back
-               launches of the four steps
+               algorithmic bytes (HBM-bound workloads) or FLOP (MFMA-bound,
+               above the ridge point) per launch / its mean launch time, the
+               time taken with HIP events on the launch stream over K
+               back-to-back launches of the four steps; traffic = its HBM
+               bytes per launch from the rocprofv3 counter summary
   cpu_baseline the CPU oracle timed on a bounded sample of the same batch
                (whole tokens), scaled to the full batch by its routes
 """
@@ -202,7 +204,21 @@ def main():
     weight_gbs = work["weight_bytes"] / t_s / 1e9
     tflops = work["flop"] / t_s / 1e12
     g1_bytes = gemm1_algorithmic_bytes(spec, work)
-    g1_gbs = g1_bytes / (kern_us["gemm1_swiglu"] * 1e-6) / 1e9
+    g1_flop = 4.0 * spec.H * spec.I * work["routes"]
+    g1_s = kern_us["gemm1_swiglu"] * 1e-6
+    # GEMM1 is bound by HBM below the ridge point of the FP8 MFMA peak and
+    # HBM bandwidth (625 FLOP/byte), by the MFMA above it
+    if g1_flop / g1_bytes > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "kernel": "gemm1_swiglu",
+                "achieved": round(g1_flop / g1_s / 1e12, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g1_flop / g1_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+                "flop_per_launch": int(g1_flop)}
+    else:
+        roof = {"bound": "hbm", "kernel": "gemm1_swiglu",
+                "achieved": round(g1_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(g1_bytes / g1_s / 1e9 / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = recorded_traffic(spec_name)
+    roof["bytes_per_launch"] = int(g1_bytes)
     result = {
         "metric": METRIC,
         "value": round(weight_gbs, 2),
@@ -228,11 +244,7 @@ def main():
         "mfma_frac": round(tflops / FP8_PEAK_TFLOPS, 5),
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "dispatch_status": status.tolist(),
-        "roofline": {"bound": "hbm", "kernel": "gemm1_swiglu", "achieved": round(g1_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(spec_name),
-                     "bytes_per_launch": int(g1_bytes)},
+        "roofline": roof,
     }
 
     if not args.no_cpu_baseline:
