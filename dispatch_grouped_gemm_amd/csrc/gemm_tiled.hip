@@ -1,20 +1,26 @@
 // Expert GEMMs for many rows per expert: LDS-tiled scaled FP4 x FP8 MFMA.
 //
-// A workgroup computes a tile of 256 weight rows x BM dispatched rows of one
+// A workgroup computes a tile of BN weight rows x BM dispatched rows of one
 // expert.  Its four wavefronts form a 2 x 2 grid: wavefront (wn, wm) owns
-// weight rows [128 wn, 128 wn + 128) of the tile (eight 16-row MFMA groups)
-// and dispatched rows [wm BM/2, (wm+1) BM/2).  Every K step of 128 is
-// brought into LDS with direct global-to-LDS loads, double-buffered: the
-// loads of step k+1 are in flight while step k is computed.  Each workgroup
-// fits in half a CU's LDS and registers, so two independent workgroups share
-// every CU: while one waits at its barrier or on LDS, the other's MFMAs run
-// (measured faster than one workgroup of eight wavefronts, whose halves wait
-// at the same barriers, and than three-stage rings at one workgroup per CU).
+// weight rows [wn BN/2, (wn+1) BN/2) of the tile (BN/32 16-row MFMA groups)
+// and dispatched rows [wm BM/2, (wm+1) BM/2).  The operands of KU K steps of
+// 128 (one stage) are brought into LDS with direct global-to-LDS loads,
+// double-buffered: the loads of stage u+1 are in flight while stage u is
+// computed.  Each workgroup fits in half a CU's LDS and registers, so two
+// independent workgroups share every CU: while one waits at its barrier or
+// on memory, the other's MFMAs run (measured faster than one workgroup of
+// eight wavefronts, whose halves wait at the same barriers, and than
+// three-stage rings at one workgroup per CU).
 //
-// GEMM1 tile: 128 intermediate columns j0..j0+127.  Wavefront wn holds the
-// 64 columns j0+64wn.. as four gate groups and the four matching up groups,
-// so the clamped SwiGLU and the MX FP8 requant (two 32-column blocks) happen
-// in registers.  GEMM2 tile: 256 output columns, y kept in float32.
+// Tiles: 128-row tiles (MFMA-bound prefill sizes) take 256 weight rows (or
+// 128 when 256 would leave fewer than three rounds of items) and one K step
+// per stage; 64-row tiles (HBM-bound) take 128 weight rows and two K steps
+// per stage, so every weight row is read 128 contiguous bytes at a time.
+//
+// GEMM1 tile: BN/2 intermediate columns.  Each wavefront holds BN/4 of them
+// as BN/64 gate groups and the matching up groups, so the clamped SwiGLU and
+// the MX FP8 requant (32-column blocks) happen in registers.  GEMM2 tile: BN
+// output columns, y kept in float32.
 //
 // Work items are (row tile of one expert, N tile), derived on every
 // workgroup from counts as in the skinny kernels, and taken in a grid-stride
@@ -26,22 +32,19 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-// Tile of BN weight rows (256 or 128) x BM dispatched rows (64 or 128).
-template <int BM, int BN>
+// Tile of BN weight rows (256 or 128) x BM dispatched rows (64 or 128); one
+// LDS stage holds KU K steps of 128 (1 or 2).
+template <int BM, int BN, int KU>
 struct TileLds {
-    static constexpr int kW = BN * 64;    // FP4 weight tile, one K step
-    static constexpr int kX = BM * 128;   // FP8 activation rows, one K step
+    static_assert(KU == 1 || KU == 2, "one or two K steps per stage");
+    static constexpr int kW = BN * 64 * KU;    // FP4 weight tile, one stage
+    static constexpr int kX = BM * 128 * KU;   // FP8 activation rows, one stage
     static constexpr int kStage = kW + kX;
-    static constexpr int kStages = 2;     // K steps resident in LDS (2 to 4)
-    static constexpr int kWE = BN * 16;   // weight exponents of four K steps
-    static constexpr int kXE = BM * 16;   // activation exponents of four K steps
+    static constexpr int kStages = 2;          // stages resident in LDS
+    static constexpr int kWE = BN * 16;        // weight exponents of four K steps
+    static constexpr int kXE = BM * 16;        // activation exponents of four K steps
     static constexpr int kExp = kWE + kXE;
     static constexpr int kExpSlots = 2;
-    // loads one wavefront issues per K step (BN/64 weight instructions, BM/32
-    // activation instructions) and per four K steps (one weight-exponent and
-    // one activation-exponent instruction)
-    static constexpr int kDataLoads = BN / 64 + BM / 32;
-    static constexpr int kExpLoads = 2;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -94,22 +97,7 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until at most `steps` K steps' loads (of which `exps` start an
-// exponent group) are outstanding; steps <= 2, exps <= 1.
-template <typename L>
-__device__ __forceinline__ void wait_loads(int steps, int exps)
-{
-    constexpr int D = L::kDataLoads, E = L::kExpLoads;
-    switch (steps * 2 + exps) {
-    case 2: wait_vmcnt<D>(); break;
-    case 3: wait_vmcnt<D + E>(); break;
-    case 4: wait_vmcnt<2 * D>(); break;
-    case 5: wait_vmcnt<2 * D + E>(); break;
-    default: wait_vmcnt<0>(); break;
-    }
-}
-
-template <bool kGemm1, int BM, int BN>
+template <bool kGemm1, int BM, int BN, int KU>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__restrict__ act_s,
                   const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
@@ -117,11 +105,13 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                   const uint8_t *__restrict__ ws, uint8_t *__restrict__ h_out,
                   uint8_t *__restrict__ hs_out, float *__restrict__ y_out)
 {
-    using L = TileLds<BM, BN>;
+    using L = TileLds<BM, BN, KU>;
     constexpr int GW = BN / 32;             // 16-row weight groups per wavefront
-    constexpr int WI = BN / 64;             // weight load instructions per wavefront
+    constexpr int WI = BN * KU / 64;        // weight load instructions per wavefront and stage
     constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
     constexpr int NS = L::kStages;
+    constexpr int WROW = 64 * KU;           // LDS bytes of one weight row in a stage
+    constexpr int WSWZ = 4 * KU - 1;        // chunk swizzle mask of the weight rows
     __shared__ __align__(16) uint8_t lds[NS * L::kStage + L::kExpSlots * L::kExp];
     __shared__ int prefix[kMaxLocalExperts + 1];
     __shared__ int arow[BM];                // activation row of each tile row
@@ -131,9 +121,11 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
     const int wn = wave & 1, wm = wave >> 1;
     const int H = s.H, I = s.I;
     const int KT = kGemm1 ? H : I;          // contraction length
-    const int KS = KT / 128;
+    const int KS = KT / 128;                // K steps
+    const int U = (KS + KU - 1) / KU;       // stages
     const int NT = kGemm1 ? I / (BN / 2) : H / BN;
     const int nchunks = plan_chunks(s, counts, BM, prefix);
+
     const long items = (long)nchunks * NT;
 
     for (long item = blockIdx.x; item < items; item += gridDim.x) {
@@ -160,31 +152,38 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             }
             return (uint32_t)(e * H + nt * BN + r);
         };
-        // LDS layout of a stage: weight group g (tile rows 16g..16g+15) at
-        // 1024 g as 64-byte rows, activation tile row R at kW + 128 R; the
-        // 16-byte chunk c of a row sits at position c ^ swz(row) with
-        // swz = (row >> 1) & 3 (weights) or (row >> 1) & 7 (activations), so
-        // the MFMA fragment reads below hit every LDS bank once.  Loads are
-        // row-major (four or eight consecutive lanes cover one row), which
-        // the global-to-LDS path moves several times faster than lanes
-        // walking down the rows.
+        // LDS layout of a stage: weight tile row r at WROW r (64 bytes of
+        // each row per K step, so WROW = 64 or 128), then activation rows:
+        // K step kk of the stage at kW + BM 128 kk, tile row R at 128 R of
+        // it.  The 16-byte chunk c of a row sits at position c ^ swz(row),
+        // swz = (row >> 1) & (WROW/16 - 1) (weights) or (row >> 1) & 7
+        // (activations), so the MFMA fragment reads below hit every LDS bank
+        // once.  Loads are row-major (WROW/16 or eight consecutive lanes
+        // cover one row): the global-to-LDS path moves that several times
+        // faster than lanes walking down the rows, and HBM serves whole
+        // 128-byte row pieces (two K steps per stage) markedly faster than
+        // 64-byte ones.
         //
-        // Weight instruction i (< BN/64) brings group g = wave + 4i: lane l -> row
-        // 16g + (l >> 2), chunk (l & 3) ^ swz.  Activation instruction i
-        // brings tile rows 8h.. with h = wave + 4i: lane l -> row
-        // R = 8h + (l >> 3), chunk (l & 7) ^ swz.
+        // Weight instruction i brings tile rows rpi h .. rpi h + rpi - 1 with
+        // rpi = 1024 / WROW and h = wave + 4i: lane l -> row
+        // rpi h + l / (WROW/16), chunk (l mod WROW/16) ^ swz.  Activation
+        // instruction i of a K step brings tile rows 8h.., h = wave + 4i:
+        // lane l -> row R = 8h + (l >> 3), chunk (l & 7) ^ swz.
+        constexpr int LPR = WROW / 16;      // lanes per weight row
         uint32_t woff[WI], xoff[TB];
+        bool xrow_used[TB];   // activation rows past nrows are not loaded
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
-            const int g = wave + 4 * i, rr = lane >> 2;
-            const int c = (lane & 3) ^ ((rr >> 1) & 3);
-            woff[i] = wrow_of(16 * g + rr) * (uint32_t)(KT / 2) + 16u * (uint32_t)c;
+            const int r = (64 / LPR) * (wave + 4 * i) + lane / LPR;
+            const int cc = (lane % LPR) ^ ((r >> 1) & WSWZ);
+            woff[i] = wrow_of(r) * (uint32_t)(KT / 2) + 16u * (uint32_t)cc;
         }
 #pragma unroll
         for (int i = 0; i < TB; ++i) {
             const int h = wave + 4 * i, R = 8 * h + (lane >> 3);
-            const int c = (lane & 7) ^ ((R >> 1) & 7);
-            xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)c;
+            const int cc = (lane & 7) ^ ((R >> 1) & 7);
+            xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)cc;
+            xrow_used[i] = R < nrows;
         }
         // exponents, four K steps (16 bytes) per row at a time: wavefront v
         // brings weight rows 64 (v mod BN/64) + l and activation rows
@@ -196,6 +195,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         const int xe_wave = wave % (BM / 64);
         const uint32_t weoff = wrow_of(64 * we_wave + lane) * (uint32_t)(KT / 32);
         const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
+        const bool xe_used = 64 * xe_wave + lane < nrows;
         auto ebase = [&](int grp) -> int { return min(16 * grp, KT / 32 - 16); };
 
         const uint32_t lds0 = lds_addr(lds);
@@ -204,20 +204,40 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
         const uint32_t lds_e = lds0 + NS * L::kStage;
         const uint32_t lds_we = __builtin_amdgcn_readfirstlane(lds_e + 1024u * we_wave);
         const uint32_t lds_xe = __builtin_amdgcn_readfirstlane(lds_e + L::kWE + 1024u * xe_wave);
-        auto issue = [&](int ks) {
-            const uint32_t st = (uint32_t)((ks % NS) * L::kStage);
+        // stage u: K steps KU u .. (the last stage of an odd KS with KU = 2
+        // holds one step; its other half is neither loaded nor read)
+        auto issue = [&](int u) {
+            const uint32_t st = (uint32_t)((u % NS) * L::kStage);
+            const int ks0 = KU * u;
+            const int nk = min(KU, KS - ks0);
+            if (nk == KU) {
 #pragma unroll
-            for (int i = 0; i < WI; ++i)
-                g2lds<16>(w, woff[i] + (uint32_t)ks * 64u, lds_w + st + 4096u * i);
+                for (int i = 0; i < WI; ++i)
+                    g2lds<16>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+            } else {
+                // one K step of a 128-byte row layout: only chunks 0..3
+                // (positions c ^ swz) are read; load them, skip the rest
 #pragma unroll
-            for (int i = 0; i < TB; ++i)
-                g2lds<16>(act, xoff[i] + (uint32_t)ks * 128u, lds_x + st + 4096u * i);
-            if ((ks & 3) == 0) {
-                const int grp = ks >> 2;
+                for (int i = 0; i < WI; ++i)
+                    if (((lane % LPR) ^ ((((64 / LPR) * (wave + 4 * i) + lane / LPR) >> 1) & WSWZ)) < 4)
+                        g2lds<16>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+            }
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk)
+                if (kk < nk) {
+#pragma unroll
+                    for (int i = 0; i < TB; ++i)
+                        if (xrow_used[i])
+                            g2lds<16>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
+                                      lds_x + st + (uint32_t)(kk * BM * 128) + 4096u * i);
+                }
+            if ((ks0 & 3) == 0) {
+                const int grp = ks0 >> 2;
                 const uint32_t es = (uint32_t)((grp % L::kExpSlots) * L::kExp);
                 const uint32_t eb = (uint32_t)ebase(grp);
                 g2lds<16>(ws, weoff + eb, lds_we + es);
-                g2lds<16>(act_s, xeoff + eb, lds_xe + es);
+                if (xe_used)
+                    g2lds<16>(act_s, xeoff + eb, lds_xe + es);
             }
         };
 
@@ -228,52 +248,59 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             for (int j = 0; j < TB; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // per-lane LDS offsets of the fragment reads (see the layout above)
-        const int afrag = wn * GW * 1024 + 64 * i16 + 16 * (kq ^ ((i16 >> 1) & 3));
+        // per-lane LDS offsets of the fragment reads (see the layout above);
+        // K step kk of a stage reads chunks 4 kk + kq of the weight rows
+        const int arow0 = wn * GW * 16 * WROW + WROW * i16;
         const int xrow = wm * (BM / 2) + i16;
         const int bfrag_lo = L::kW + 128 * xrow + 16 * (kq ^ ((i16 >> 1) & 7));
         const int bfrag_hi = L::kW + 128 * xrow + 16 * ((kq + 4) ^ ((i16 >> 1) & 7));
         const int wexp = NS * L::kStage + 16 * (wn * (BN / 2) + i16) + kq;
         const int xexp = NS * L::kStage + L::kWE + 16 * xrow + kq;
 
-#pragma unroll
-        for (int p = 0; p < NS - 1; ++p)
-            if (p < KS)
-                issue(p);
-        for (int ks = 0; ks < KS; ++ks) {
-            // this wavefront's loads of step ks are done once at most the
-            // loads of the later steps already issued (up to NS-2 of them)
-            // are outstanding; then all wavefronts' are
-            {
-                const int later = min(NS - 2, KS - 1 - ks);
-                int exps = 0;
-                for (int t = ks + 1; t <= ks + later; ++t)
-                    exps += (t & 3) == 0;
-                wait_loads<L>(later, exps);
-            }
+        // 16-row activation blocks of this wavefront that hold dispatched
+        // rows (the MFMAs of the others would only feed discarded columns)
+        const int nlive = min(TB, max(0, (nrows - wm * (BM / 2) + 15) >> 4));
+
+        issue(0);
+        for (int u = 0; u < U; ++u) {
+            // this wavefront's loads of stage u are the only ones outstanding;
+            // after the barrier every wavefront's are done and nobody reads
+            // the other stage any more, so the next stage's loads go there
+            wait_vmcnt<0>();
             raw_barrier();
-            if (ks + NS - 1 < KS)
-                issue(ks + NS - 1);
-            const uint8_t *st = lds + (ks % NS) * L::kStage;
-            const uint8_t *ex = lds + ((ks >> 2) % L::kExpSlots) * L::kExp + (4 * ks - ebase(ks >> 2));
-            v8i b[TB];
-            int sb[TB];
+            if (u + 1 < U)
+                issue(u + 1);
+            const uint8_t *st = lds + (u % NS) * L::kStage;
 #pragma unroll
-            for (int j = 0; j < TB; ++j) {
-                const u32x4 lo = lds_read16(st + bfrag_lo + j * 2048);
-                const u32x4 hi = lds_read16(st + bfrag_hi + j * 2048);
-                b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                sb[j] = ex[xexp + j * 256];
-            }
+            for (int kk = 0; kk < KU; ++kk) {
+                const int ks = KU * u + kk;
+                if (ks >= KS)
+                    break;
+                const uint8_t *ex = lds + ((ks >> 2) % L::kExpSlots) * L::kExp + (4 * ks - ebase(ks >> 2));
+                const uint8_t *sx = st + kk * (BM * 128);
+                const int afrag = arow0 + 16 * ((4 * kk + kq) ^ ((i16 >> 1) & WSWZ));
+                v8i b[TB];
+                int sb[TB];
 #pragma unroll
-            for (int i = 0; i < GW; ++i) {
-                const u32x4 a4 = lds_read16(st + afrag + i * 1024);
-                const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-                const int sa = ex[wexp + i * 256];
+                for (int j = 0; j < TB; ++j) {
+                    if (j >= nlive)
+                        break;
+                    const u32x4 lo = lds_read16(sx + bfrag_lo + j * 2048);
+                    const u32x4 hi = lds_read16(sx + bfrag_hi + j * 2048);
+                    b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    sb[j] = ex[xexp + j * 256];
+                }
 #pragma unroll
-                for (int j = 0; j < TB; ++j)
-                    acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
+                for (int i = 0; i < GW; ++i) {
+                    const u32x4 a4 = lds_read16(st + afrag + i * 16 * WROW);
+                    const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+                    const int sa = ex[wexp + i * 256];
+#pragma unroll
+                    for (int j = 0; j < TB; ++j)
+                        if (j < nlive)
+                            acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
+                }
             }
         }
 
@@ -384,13 +411,29 @@ int tiled_bn(const moe_shape &s, bool gemm1)
     return tiles * nt256 < 3.0 * 2 * device_cu_count() ? 128 : 256;
 }
 
-template <bool kGemm1, int BM, int BN>
+// Tile shape and K steps per LDS stage.  Two steps per stage (128 bytes of
+// every weight row per load) stream HBM faster; they double the stage, so
+// they are used where two workgroups per CU still fit: 64-row tiles, which
+// are HBM-bound, take 128 weight rows and two steps.
+struct TiledConfig {
+    int bm, bn, ku;
+};
+
+TiledConfig tiled_config(const moe_shape &s, bool gemm1)
+{
+    const int bm = tiled_bm(s), bn = tiled_bn(s, gemm1);
+    if (bm == 64)
+        return {64, 128, 2};
+    return {bm, bn, 1};
+}
+
+template <bool kGemm1, int BM, int BN, int KU>
 hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
                         const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, float *y,
                         hipStream_t st)
 {
-    auto k = gemm_tiled_kernel<kGemm1, BM, BN>;
+    auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU>;
     const long nt = kGemm1 ? sh.I / (BN / 2) : sh.H / BN;
     const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt);
     k<<<grid, kThreads, 0, st>>>(to_dev(sh), act, act_s, counts, offsets, row_route, w, ws, h, hs,
@@ -404,18 +447,16 @@ hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8
                             const int32_t *row_route, const uint8_t *w, const uint8_t *ws,
                             uint8_t *h, uint8_t *hs, float *y, hipStream_t st)
 {
-    const int bm = tiled_bm(sh), bn = tiled_bn(sh, kGemm1);
-    if (bm == 64 && bn == 128)
-        return launch_tiled<kGemm1, 64, 128>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
+    const TiledConfig c = tiled_config(sh, kGemm1);
+#define MOE_TILED_CASE(BM, BN, KU)                                                                \
+    if (c.bm == BM && c.bn == BN && c.ku == KU)                                                   \
+        return launch_tiled<kGemm1, BM, BN, KU>(sh, act, act_s, counts, offsets, row_route, w, ws, \
+                                                h, hs, y, st);
+    MOE_TILED_CASE(64, 128, 2)
+    MOE_TILED_CASE(128, 128, 1)
+#undef MOE_TILED_CASE
+    return launch_tiled<kGemm1, 128, 256, 1>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
                                              hs, y, st);
-    if (bm == 64)
-        return launch_tiled<kGemm1, 64, 256>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
-                                             hs, y, st);
-    if (bn == 128)
-        return launch_tiled<kGemm1, 128, 128>(sh, act, act_s, counts, offsets, row_route, w, ws,
-                                              h, hs, y, st);
-    return launch_tiled<kGemm1, 128, 256>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
-                                          hs, y, st);
 }
 
 } // namespace
