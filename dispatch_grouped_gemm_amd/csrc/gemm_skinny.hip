@@ -1,7 +1,8 @@
-// Expert GEMMs for few rows per expert (decode-sized batches): the weights
-// are streamed once from HBM straight into scaled FP4 x FP8 MFMAs and every
-// weight fragment is applied to all rows of a chunk (up to 16*NMB rows)
-// while it is in registers.
+// Expert GEMMs without LDS tiles, for contractions shorter than four K steps
+// of 128 (the LDS-tiled kernels take all others): the weights are streamed
+// from HBM straight into scaled FP4 x FP8 MFMAs and every weight fragment is
+// applied to all rows of a chunk (up to 16*NMB rows) while it is in
+// registers.
 //
 // The E8M0 exponents of an item's weight and activation rows are copied to
 // LDS once per item (coalesced dword loads); the K loop reads them there.
@@ -552,13 +553,15 @@ double rows_per_expert(const moe_shape &s)
     return (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
 }
 
-// The tiled kernels need a contraction of at least four K steps (512).
-bool use_tiled_gemm1(const moe_shape &s) { return rows_per_expert(s) > 24.0 && s.H >= 512; }
+// The tiled kernels need a contraction of at least four K steps (512); where
+// they have it they are faster at every row count (measured on the V4 and
+// Flash shapes from 2.7 to 1000 rows per expert: their 64-row tiles read
+// each weight row 128 contiguous bytes at a time, which HBM serves faster
+// than the 64-byte fragments these kernels stream), so the kernels here
+// serve the shorter contractions.
+bool use_tiled_gemm1(const moe_shape &s) { return s.H >= 512; }
 
-bool use_tiled_gemm2(const moe_shape &s)
-{
-    return rows_per_expert(s) > 24.0 && s.H % 256 == 0 && s.I >= 512;
-}
+bool use_tiled_gemm2(const moe_shape &s) { return s.I >= 512; }
 
 // Rows per chunk: enough for nearly every expert's rows in one pass over its
 // weights (mean + 3 standard deviations of the binomial route count, + 1),

@@ -67,11 +67,17 @@ __device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
 // assembly so that the waits are exactly the ones this file writes: the
 // loads count in vmcnt like any vector memory load.  An LDS DMA reads m0 one
 // wait state after an SALU write of m0 at the earliest, hence the s_nop.
-template <int SIZE>
+// kStream marks data read once (non-temporal: the L2 evicts it first, so it
+// does not push out the activation rows that other tiles read again).
+template <int SIZE, bool kStream = false>
 __device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
 {
     static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
-    if (SIZE == 16)
+    if (SIZE == 16 && kStream)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0),
+                     "v"(voff), "s"(base)
+                     : "memory", "m0");
+    else if (SIZE == 16)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
                      "v"(voff), "s"(base)
                      : "memory", "m0");
@@ -106,6 +112,10 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                   uint8_t *__restrict__ hs_out, float *__restrict__ y_out)
 {
     using L = TileLds<BM, BN, KU>;
+    // 64-row tiles: an expert's weights are read by one row chunk (as a
+    // rule), so they stream through the L2 without displacing the
+    // activation rows; 128-row tiles reuse each weight tile across row chunks
+    constexpr bool kStreamW = BM == 64;
     constexpr int GW = BN / 32;             // 16-row weight groups per wavefront
     constexpr int WI = BN * KU / 64;        // weight load instructions per wavefront and stage
     constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
@@ -213,14 +223,14 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             if (nk == KU) {
 #pragma unroll
                 for (int i = 0; i < WI; ++i)
-                    g2lds<16>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+                    g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
             } else {
                 // one K step of a 128-byte row layout: only chunks 0..3
                 // (positions c ^ swz) are read; load them, skip the rest
 #pragma unroll
                 for (int i = 0; i < WI; ++i)
                     if (((lane % LPR) ^ ((((64 / LPR) * (wave + 4 * i) + lane / LPR) >> 1) & WSWZ)) < 4)
-                        g2lds<16>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+                        g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
             }
 #pragma unroll
             for (int kk = 0; kk < KU; ++kk)

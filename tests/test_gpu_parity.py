@@ -248,22 +248,37 @@ def test_forward_tiny_every_token_and_variants():
     np.testing.assert_array_equal(host(run_forward(case, g)), out)
 
 
-@pytest.mark.parametrize("T,H,I", [(512, 512, 256), (1200, 512, 256), (600, 512, 640),
-                                   (400, 640, 512)])
-def test_tiled_path_small(T, H, I):
-    """Enough rows per expert for the LDS-tiled GEMMs (64- and 128-row tiles)
-    on small shapes: GEMM1 codes, then the whole layer on every token.  The
-    contraction lengths 640 cover a last exponent group of fewer than four
-    K steps; I = 256 leaves GEMM2 to the skinny kernel (the tiled kernels
-    need K >= 512), H = 640 too (its tiles are 256 columns wide)."""
-    case = synth.make_case("tiny", T=T, H=H, I=I, seed=1100 + T)
-    say("tiled path small T H I", T, H, I)
+def _small_layer(T, H, I, label):
+    case = synth.make_case("tiny", T=T, H=H, I=I, seed=1100 + T + H)
+    say(label, "T H I", T, H, I)
     steps = run_steps(case)
     torch.cuda.synchronize()
     _gemm1_compare(case, steps)
     out = host(run_forward(case))
     np.testing.assert_array_equal(host(steps["out"]), out)
-    check_layer(case, np.arange(T), out, steps, "tiled T=%d H=%d I=%d" % (T, H, I))
+    check_layer(case, np.arange(T), out, steps, "%s T=%d H=%d I=%d" % (label, T, H, I))
+
+
+@pytest.mark.parametrize("T,H,I", [(512, 512, 256), (1200, 512, 256), (600, 512, 640),
+                                   (400, 640, 512), (40, 640, 512)])
+def test_tiled_path_small(T, H, I):
+    """The LDS-tiled GEMMs (every contraction of 512 or more) on small
+    shapes, 128-row tiles (1200, 600 tokens) and 64-row tiles with two K
+    steps per stage (the others; 40 tokens leave most tile rows empty):
+    GEMM1 codes, then the whole layer on every token.  The contraction
+    lengths 640 cover a last exponent group of fewer than four K steps and,
+    with two steps per stage, a last stage of one step; H = 640 also gives
+    GEMM2 128-column tiles.  I = 256 leaves GEMM2 to the register-streaming
+    kernel."""
+    _small_layer(T, H, I, "tiled path small")
+
+
+@pytest.mark.parametrize("T,H,I", [(64, 256, 256), (400, 384, 256)])
+def test_short_contraction_path(T, H, I):
+    """Contractions shorter than 512 (H for GEMM1, I for GEMM2) take the
+    register-streaming kernels; 400 tokens (about 75 rows per expert) give
+    them 64-row chunks, 64 tokens 16-row chunks."""
+    _small_layer(T, H, I, "short contraction")
 
 
 def test_forward_tiny_in_a_graph():
