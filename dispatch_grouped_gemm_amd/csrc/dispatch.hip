@@ -19,6 +19,7 @@ namespace {
 constexpr int kThreads = 1024; // 16 wavefronts
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlotsPerWaveLarge = 128;
+constexpr int kLargeBatch = kSlotsPerWaveLarge / 64;
 constexpr int kSlotsPerBlockLarge = kWaves * kSlotsPerWaveLarge;
 // compact dispatch of at most this many slots runs in one workgroup
 constexpr long kSmallSlots = 8192;
@@ -58,47 +59,81 @@ __device__ __forceinline__ int wave_sum(int v)
     return v;
 }
 
+// Slots a wavefront reads per batch: the id loads of a batch are all in
+// flight together, so a wavefront waits for memory once per 64 * P slots
+// rather than once per 64.
+constexpr int kBatch = 8;
+
+// Local expert (route_local) of the slots base + 64 p + lane, p < P; -1 past e.
+template <int P>
+__device__ __forceinline__ void load_keys(const Shape &s, const int32_t *__restrict__ ids,
+                                          long base, long e, int (&ex)[P])
+{
+    const int lane = threadIdx.x & 63;
+    int raw[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const long r = base + 64 * p + lane;
+        raw[p] = r < e ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        ex[p] = route_local(s, raw[p]);
+}
+
 // Per-wavefront histogram of the slots [b, e) into hist_row (LDS); returns
 // the wavefront's count of invalid ids (in every lane).
+template <int P>
 __device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
                               int *hist_row)
 {
-    const int lane = threadIdx.x & 63;
     int invalid = 0;
-    for (long base = b; base < e; base += 64) {
-        const long r = base + lane;
-        const int ex = r < e ? route_local(s, ids[r]) : -1;
-        const Match m = wave_match(ex, ex >= 0);
-        if (ex >= 0 && m.rank == 0)
-            hist_row[ex] += m.count; // one leader per expert: no two lanes collide
-        invalid += ex == -2;
+    for (long base = b; base < e; base += 64 * P) {
+        int ex[P];
+        load_keys<P>(s, ids, base, e, ex);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (base + 64 * p >= e)
+                break;
+            const Match m = wave_match(ex[p], ex[p] >= 0);
+            if (ex[p] >= 0 && m.rank == 0)
+                hist_row[ex[p]] += m.count; // one leader per expert: no two lanes collide
+            invalid += ex[p] == -2;
+        }
     }
     return wave_sum(invalid);
 }
 
 // Stable scatter of the slots [b, e): base_row[ex] (LDS, this wavefront's
 // own row) is the next row of expert ex for this wavefront.
+template <int P>
 __device__ void wave_scatter(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
                              int *base_row, int32_t *__restrict__ row_route,
                              int32_t *__restrict__ route_row)
 {
     const int lane = threadIdx.x & 63;
-    for (long base = b; base < e; base += 64) {
-        const long r = base + lane;
-        const int ex = r < e ? route_local(s, ids[r]) : -1;
-        const Match m = wave_match(ex, ex >= 0);
-        int row = -1;
-        if (ex >= 0)
-            row = base_row[ex] + m.rank;
-        // every lane has read its base before a leader moves it on
-        __builtin_amdgcn_wave_barrier();
-        if (ex >= 0 && m.rank == 0)
-            base_row[ex] += m.count;
-        __builtin_amdgcn_wave_barrier();
-        if (r < e) {
-            route_row[r] = row;
-            if (row >= 0)
-                row_route[row] = (int32_t)r;
+    for (long base = b; base < e; base += 64 * P) {
+        int ex[P];
+        load_keys<P>(s, ids, base, e, ex);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (base + 64 * p >= e)
+                break;
+            const long r = base + 64 * p + lane;
+            const Match m = wave_match(ex[p], ex[p] >= 0);
+            int row = -1;
+            if (ex[p] >= 0)
+                row = base_row[ex[p]] + m.rank;
+            // every lane has read its base before a leader moves it on
+            __builtin_amdgcn_wave_barrier();
+            if (ex[p] >= 0 && m.rank == 0)
+                base_row[ex[p]] += m.count;
+            __builtin_amdgcn_wave_barrier();
+            if (r < e) {
+                route_row[r] = row;
+                if (row >= 0)
+                    row_route[row] = (int32_t)r;
+            }
         }
     }
 }
@@ -154,7 +189,7 @@ compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restri
     if (tid == 0)
         invalid_total = 0;
     __syncthreads();
-    const int inv = wave_histogram(s, ids, b, e, hist + wave * E);
+    const int inv = wave_histogram<kBatch>(s, ids, b, e, hist + wave * E);
     if (lane == 0 && inv)
         atomicAdd(&invalid_total, inv);
     __syncthreads();
@@ -182,7 +217,7 @@ compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restri
         status[1] = status[2] = status[3] = 0;
     }
     __syncthreads();
-    wave_scatter(s, ids, b, e, hist + wave * E, row_route, route_row);
+    wave_scatter<kBatch>(s, ids, b, e, hist + wave * E, row_route, route_row);
 }
 
 // ---- compact, many workgroups ------------------------------------------------
@@ -205,13 +240,16 @@ compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restric
     const long e = min(n, b + kSlotsPerWaveLarge);
     // wavefronts share the workgroup histogram: add with LDS atomics
     int inv = 0;
-    for (long base = b; base < e; base += 64) {
-        const long r = base + lane;
-        const int ex = r < e ? route_local(s, ids[r]) : -1;
-        const Match m = wave_match(ex, ex >= 0);
-        if (ex >= 0 && m.rank == 0)
-            atomicAdd(&hist[ex], m.count);
-        inv += ex == -2;
+    for (long base = b; base < e; base += 64 * kLargeBatch) {
+        int ex[kLargeBatch];
+        load_keys<kLargeBatch>(s, ids, base, e, ex);
+#pragma unroll
+        for (int p = 0; p < kLargeBatch; ++p) {
+            const Match m = wave_match(ex[p], ex[p] >= 0);
+            if (ex[p] >= 0 && m.rank == 0)
+                atomicAdd(&hist[ex[p]], m.count);
+            inv += ex[p] == -2;
+        }
     }
     inv = wave_sum(inv);
     if (lane == 0 && inv)
@@ -291,7 +329,7 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
     __syncthreads();
     const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
     const long e = min(n, b + kSlotsPerWaveLarge);
-    (void)wave_histogram(s, ids, b, e, hist + wave * E);
+    (void)wave_histogram<kLargeBatch>(s, ids, b, e, hist + wave * E);
     __syncthreads();
     if (tid < E) {
         int run = scratch[(size_t)blockIdx.x * (E + 1) + tid];
@@ -302,41 +340,48 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
         }
     }
     __syncthreads();
-    wave_scatter(s, ids, b, e, hist + wave * E, row_route, route_row);
+    wave_scatter<kLargeBatch>(s, ids, b, e, hist + wave * E, row_route, route_row);
 }
 
 // ---- fixed-slot ----------------------------------------------------------------
 
 // Claim one slot per kept route: the leader of each expert group adds the
 // group's size to the expert's counter and hands out consecutive slots.
-template <bool kLds>
+template <int P>
 __device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
                             int32_t *cnt, int32_t *__restrict__ row_route,
                             int32_t *__restrict__ route_row, int &invalid, int &dropped)
 {
     const int lane = threadIdx.x & 63;
-    for (long base = b; base < e; base += 64) {
-        const long r = base + lane;
-        const int ex = r < e ? route_local(s, ids[r]) : -1;
-        const Match m = wave_match(ex, ex >= 0);
-        int first = 0;
-        if (ex >= 0 && m.rank == 0)
-            first = atomicAdd(&cnt[ex], m.count);
-        const int leader = ex >= 0 ? __ffsll((long long)m.mask) - 1 : lane;
-        first = __shfl(first, leader);
-        int row = -1;
-        if (ex >= 0) {
-            const int slot = first + m.rank;
-            if (slot < s.capacity)
-                row = ex * s.capacity + slot;
-            else
-                ++dropped;
-        }
-        invalid += ex == -2;
-        if (r < e) {
-            route_row[r] = row;
-            if (row >= 0)
-                row_route[row] = (int32_t)r;
+    for (long base = b; base < e; base += 64 * P) {
+        int exs[P];
+        load_keys<P>(s, ids, base, e, exs);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (base + 64 * p >= e)
+                break;
+            const long r = base + 64 * p + lane;
+            const int ex = exs[p];
+            const Match m = wave_match(ex, ex >= 0);
+            int first = 0;
+            if (ex >= 0 && m.rank == 0)
+                first = atomicAdd(&cnt[ex], m.count);
+            const int leader = ex >= 0 ? __ffsll((long long)m.mask) - 1 : lane;
+            first = __shfl(first, leader);
+            int row = -1;
+            if (ex >= 0) {
+                const int slot = first + m.rank;
+                if (slot < s.capacity)
+                    row = ex * s.capacity + slot;
+                else
+                    ++dropped;
+            }
+            invalid += ex == -2;
+            if (r < e) {
+                route_row[r] = row;
+                if (row >= 0)
+                    row_route[row] = (int32_t)r;
+            }
         }
     }
 }
@@ -362,7 +407,7 @@ fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
     const long per_wave = (n + kWaves - 1) / kWaves;
     const long b = min(n, per_wave * wave), e = min(n, b + per_wave);
     int invalid = 0, dropped = 0;
-    claim_slots<true>(s, ids, b, e, cnt, row_route, route_row, invalid, dropped);
+    claim_slots<kBatch>(s, ids, b, e, cnt, row_route, route_row, invalid, dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
@@ -407,7 +452,7 @@ fixed_claim_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
     const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
     const long e = min(n, b + kSlotsPerWaveLarge);
     int invalid = 0, dropped = 0;
-    claim_slots<false>(s, ids, b, e, counts, row_route, route_row, invalid, dropped);
+    claim_slots<kLargeBatch>(s, ids, b, e, counts, row_route, route_row, invalid, dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
