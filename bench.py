@@ -175,7 +175,7 @@ def main():
     R = max(moe.moe_row_capacity(shape), 1)
     h = torch.empty((R, spec.I), dtype=torch.uint8, device=dev)
     hs = torch.empty((R, spec.I // 32), dtype=torch.uint8, device=dev)
-    y = torch.empty((R, spec.H), dtype=torch.float32, device=dev)
+    y = torch.empty((R, spec.H), dtype=torch.uint16, device=dev)
     st = torch.cuda.current_stream()
     iters = args.kernel_iters or args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]

@@ -261,7 +261,7 @@ def moe_gemm1_swiglu(shape: MoeShape, x_fp8, x_scale, d: DispatchBuffers, w13, w
            "moe_gemm1_swiglu")
 
 
-def moe_gemm2(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_scale, y_f32,
+def moe_gemm2(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_scale, y_bf16,
               stream=None):
     dev = h_fp8.device
     H, I, E = shape.H, shape.I, shape.E_local
@@ -273,19 +273,19 @@ def moe_gemm2(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_scale,
             _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
             _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
             _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
-            _ptr(y_f32, "y_f32", (R, H), {torch.float32}, dev)]
+            _ptr(y_bf16, "y_bf16", (R, H), {torch.bfloat16, torch.uint16, torch.int16}, dev)]
     c = shape.c()
     _check(lib().moe_gemm2(ctypes.byref(c), *args, _stream(stream, dev)), "moe_gemm2")
 
 
-def moe_combine(shape: MoeShape, topk_w, route_row, y_f32, out_bf16, stream=None):
+def moe_combine(shape: MoeShape, topk_w, route_row, y_bf16, out_bf16, stream=None):
     dev = topk_w.device
     T, K, H = shape.T, shape.K, shape.H
     R = max(moe_row_capacity(shape), 1)
     bf = {torch.bfloat16, torch.uint16, torch.int16}
     args = [_ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
             _ptr(route_row, "route_row", (max(T * K, 1),), {torch.int32}, dev),
-            _ptr(y_f32, "y_f32", (R, H), {torch.float32}, dev),
+            _ptr(y_bf16, "y_bf16", (R, H), bf, dev),
             _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
     c = shape.c()
     _check(lib().moe_combine(ctypes.byref(c), *args, _stream(stream, dev)), "moe_combine")

@@ -51,7 +51,7 @@ Layout layout_of(const moe_shape &s)
     L.hs = p;
     p = align_up(p + R * (size_t)(s.I / 32));
     L.y = p;
-    p = align_up(p + R * (size_t)s.H * sizeof(float));
+    p = align_up(p + R * (size_t)s.H * sizeof(uint16_t));
     L.total = p;
     return L;
 }
@@ -151,7 +151,7 @@ int moe_gemm1_swiglu(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
 }
 
 int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int32_t *counts,
-              const int32_t *offsets, const uint8_t *w2, const uint8_t *w2s, float *y,
+              const int32_t *offsets, const uint8_t *w2, const uint8_t *w2s, uint16_t *y,
               void *stream)
 {
     int rc = moe_check_shape(s);
@@ -167,7 +167,7 @@ int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int
         moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, as_stream(stream)));
 }
 
-int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, const float *y,
+int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, const uint16_t *y,
                 uint16_t *out, void *stream)
 {
     int rc = moe_check_shape(s);
@@ -207,7 +207,7 @@ int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const i
     void *scratch = base + L.scratch;
     uint8_t *h = base + L.h;
     uint8_t *hs = base + L.hs;
-    float *y = reinterpret_cast<float *>(base + L.y);
+    uint16_t *y = reinterpret_cast<uint16_t *>(base + L.y);
     hipStream_t st = as_stream(stream);
     if (moe::use_fused_decode(*s)) {
         // dispatch (which also clears the work-queue counters), then one

@@ -1,5 +1,5 @@
-// Combine: each token's kept routes, weighted by their routing weights and
-// summed in float32 in ascending k, rounded to bf16 once.  Slots whose
+// Combine: each token's kept routes (bf16 y rows), weighted by their routing
+// weights and summed in float32 in ascending k, rounded to bf16 once.  Slots whose
 // route_row is -1 (pad, foreign, invalid or dropped) contribute nothing, so
 // the result does not depend on their weights.  No atomics: a thread owns 8
 // output columns of one token, which makes the sum order fixed.
@@ -13,7 +13,7 @@ constexpr int kThreads = 256;
 
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict__ route_row,
-               const float *__restrict__ y, uint16_t *__restrict__ out)
+               const uint16_t *__restrict__ y, uint16_t *__restrict__ out)
 {
     const int per_token = (s.H + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
     const int t = blockIdx.x / per_token;
@@ -24,7 +24,7 @@ combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict_
 } // namespace
 
 hipError_t launch_combine(const moe_shape &sh, const float *tw, const int32_t *route_row,
-                          const float *y, uint16_t *out, hipStream_t st)
+                          const uint16_t *y, uint16_t *out, hipStream_t st)
 {
     const Shape s = to_dev(sh);
     const int per_block = kThreads * kCombineVec;

@@ -18,7 +18,7 @@
 // epilogue applies the clamped SwiGLU to matching gate/up accumulators and
 // requantises the 32 columns as one MX FP8 block.
 // GEMM2 tile: 64 output columns, four 16-row MFMA groups of W2; y rows are
-// kept in float32 for the combine.
+// rounded to bf16 for the combine.
 #include <cmath>
 
 #include "moe_common.hpp"
@@ -204,7 +204,7 @@ struct LayerPtrs {
     const int32_t *counts, *offsets, *row_route;
     const uint8_t *w13, *w13s, *w2, *w2s;
     uint8_t *h, *hs;
-    float *y;
+    uint16_t *y;
     const float *tw;
     const int32_t *route_row;
     uint16_t *out;
@@ -318,7 +318,7 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
     __syncthreads();
 }
 
-// GEMM2 of 64 output columns n0 = 64 nt .. of one row chunk (y in float32).
+// GEMM2 of 64 output columns n0 = 64 nt .. of one row chunk (y in bf16).
 // LDS: red[NMB*4*4*64], exps[(64 + 16 NMB) * exp_stride(I)].
 template <int NMB>
 __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, const Chunk &c,
@@ -368,11 +368,13 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
         const int mb = wave;
         const int rloc = mb * 16 + i16;
         if (rloc < nrows) {
-            float *yr = p.y + (size_t)(row0 + rloc) * (size_t)H + n0 + 4 * kq;
+            uint16_t *yr = p.y + (size_t)(row0 + rloc) * (size_t)H + n0 + 4 * kq;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float *r = red + (mb * 4 + g) * 4 * 64 + lane;
-                *reinterpret_cast<float4 *>(yr + 16 * g) = float4{r[0], r[64], r[128], r[192]};
+                *reinterpret_cast<uint2 *>(yr + 16 * g) =
+                    uint2{f32_to_bf16(r[0]) | (f32_to_bf16(r[64]) << 16),
+                          f32_to_bf16(r[128]) | (f32_to_bf16(r[192]) << 16)};
             }
         }
     }
@@ -632,7 +634,7 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
 
 hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                        const uint8_t *w2s, float *y, hipStream_t st)
+                        const uint8_t *w2s, uint16_t *y, hipStream_t st)
 {
     if (use_tiled_gemm2(sh))
         return launch_gemm2_tiled(sh, h, hs, counts, offsets, w2, w2s, y, st);
@@ -688,7 +690,7 @@ hipError_t launch_fused_decode(const moe_shape &sh, const uint8_t *x, const uint
                                const int32_t *row_route, const int32_t *route_row,
                                const float *tw, const uint8_t *w13, const uint8_t *w13s,
                                const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
-                               float *y, uint16_t *out, int32_t *sync, hipStream_t st)
+                               uint16_t *y, uint16_t *out, int32_t *sync, hipStream_t st)
 {
     const Shape s = to_dev(sh);
     LayerPtrs p{};

@@ -20,7 +20,7 @@
 // GEMM1 tile: BN/2 intermediate columns.  Each wavefront holds BN/4 of them
 // as BN/64 gate groups and the matching up groups, so the clamped SwiGLU and
 // the MX FP8 requant (32-column blocks) happen in registers.  GEMM2 tile: BN
-// output columns, y kept in float32.
+// output columns, y rounded to bf16 (the combine's input).
 //
 // Work items are (row tile of one expert, N tile), derived on every
 // workgroup from counts as in the skinny kernels, and taken in a grid-stride
@@ -109,7 +109,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                   const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
                   const int32_t *__restrict__ row_route, const uint8_t *__restrict__ w,
                   const uint8_t *__restrict__ ws, uint8_t *__restrict__ h_out,
-                  uint8_t *__restrict__ hs_out, float *__restrict__ y_out)
+                  uint8_t *__restrict__ hs_out, uint16_t *__restrict__ y_out)
 {
     using L = TileLds<BM, BN, KU>;
     // 64-row tiles: an expert's weights are read by one row chunk (as a
@@ -361,12 +361,13 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
             for (int j = 0; j < TB; ++j) {
                 const int m = wm * (BM / 2) + 16 * j + i16;
                 if (m < nrows) {
-                    float *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * BN +
-                                (BN / 2) * wn + 4 * kq;
+                    uint16_t *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * BN +
+                                   (BN / 2) * wn + 4 * kq;
 #pragma unroll
                     for (int i = 0; i < GW; ++i)
-                        *reinterpret_cast<float4 *>(yr + 16 * i) =
-                            float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                        *reinterpret_cast<uint2 *>(yr + 16 * i) =
+                            uint2{f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16),
+                                  f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16)};
                 }
             }
         }
@@ -440,7 +441,7 @@ TiledConfig tiled_config(const moe_shape &s, bool gemm1)
 template <bool kGemm1, int BM, int BN, int KU>
 hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
-                        const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, float *y,
+                        const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, uint16_t *y,
                         hipStream_t st)
 {
     auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU>;
@@ -455,7 +456,7 @@ template <bool kGemm1>
 hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
                             const int32_t *counts, const int32_t *offsets,
                             const int32_t *row_route, const uint8_t *w, const uint8_t *ws,
-                            uint8_t *h, uint8_t *hs, float *y, hipStream_t st)
+                            uint8_t *h, uint8_t *hs, uint16_t *y, hipStream_t st)
 {
     const TiledConfig c = tiled_config(sh, kGemm1);
 #define MOE_TILED_CASE(BM, BN, KU)                                                                \
@@ -482,7 +483,7 @@ hipError_t launch_gemm1_tiled(const moe_shape &sh, const uint8_t *x, const uint8
 
 hipError_t launch_gemm2_tiled(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                              const uint8_t *w2s, float *y, hipStream_t st)
+                              const uint8_t *w2s, uint16_t *y, hipStream_t st)
 {
     return launch_tiled_any<false>(sh, h, hs, counts, offsets, nullptr, w2, w2s, nullptr,
                                    nullptr, y, st);

@@ -201,13 +201,14 @@ __device__ __forceinline__ int chunk_expert(const int *prefix, int E, int q)
 // ---------------------------------------------------------------------------
 // Combine of output columns [col, col + 8) of token t: the kept routes in
 // ascending k, each a rounded product then a rounded add (no fused
-// multiply-add), one bf16 rounding at the end.
+// multiply-add) on the bf16 y values widened to float32, one bf16 rounding
+// at the end.
 // ---------------------------------------------------------------------------
 constexpr int kCombineVec = 8;
 
 __device__ __forceinline__ void combine_cols(const Shape &s, const float *__restrict__ tw,
                                              const int32_t *__restrict__ route_row,
-                                             const float *__restrict__ y,
+                                             const uint16_t *__restrict__ y,
                                              uint16_t *__restrict__ out, int t, int col)
 {
 #pragma clang fp contract(off)
@@ -223,9 +224,14 @@ __device__ __forceinline__ void combine_cols(const Shape &s, const float *__rest
         if (row < 0)
             continue;
         const float w = tw[slot0 + k];
-        const float4 *yr = reinterpret_cast<const float4 *>(y + (size_t)row * s.H + col);
-        const float4 a = yr[0], b = yr[1];
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint4 q = *reinterpret_cast<const uint4 *>(y + (size_t)row * s.H + col);
+        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(wd[i] << 16);
+            v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+        }
 #pragma unroll
         for (int i = 0; i < kCombineVec; ++i) {
             const float prod = w * v[i];
@@ -256,14 +262,14 @@ hipError_t launch_fused_decode(const moe_shape &s, const uint8_t *x, const uint8
                                const int32_t *row_route, const int32_t *route_row,
                                const float *tw, const uint8_t *w13, const uint8_t *w13s,
                                const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
-                               float *y, uint16_t *out, int32_t *sync, hipStream_t st);
+                               uint16_t *y, uint16_t *out, int32_t *sync, hipStream_t st);
 hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
                         const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
                         hipStream_t st);
 hipError_t launch_gemm2(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                        const uint8_t *w2s, float *y, hipStream_t st);
+                        const uint8_t *w2s, uint16_t *y, hipStream_t st);
 int tiled_bm(const moe_shape &s);
 hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                               const int32_t *counts, const int32_t *offsets,
@@ -271,9 +277,9 @@ hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_
                               uint8_t *h, uint8_t *hs, hipStream_t st);
 hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                              const uint8_t *w2s, float *y, hipStream_t st);
+                              const uint8_t *w2s, uint16_t *y, hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
-                          const float *y, uint16_t *out, hipStream_t st);
+                          const uint16_t *y, uint16_t *out, hipStream_t st);
 
 int device_cu_count();
 

@@ -136,25 +136,26 @@ int moe_gemm1_swiglu(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t
                      uint8_t *h_scale, void *stream);
 
 /*
- * GEMM2 (MXFP4 W2): y[row, n] = sum_i h[row,i] * W2[e,n,i] in float32 for
- * every used row.  Writes y rows of used rows only.  y stays float32: the
- * combine rounds to bf16 once, after the weighted sum.
+ * GEMM2 (MXFP4 W2; "MegaMoEV2 ...", Technical Details: the expert output
+ * rows are BF16): y[row, n] = bf16(sum_i h[row,i] * W2[e,n,i]), the sum in
+ * float32, rounded to nearest even, for every used row (y_bf16 is
+ * [row capacity, H] bf16 bit patterns).  Writes y rows of used rows only.
  */
 int moe_gemm2(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_scale,
               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-              const uint8_t *w2_scale, float *y_f32, void *stream);
+              const uint8_t *w2_scale, uint16_t *y_bf16, void *stream);
 
 /*
  * Combine ("MegaMoEV2 ...": the combine skips invalid (-1) top-k slots;
  * "route before the rows move": routed contributions summed in f32 and
  * rounded once).  For every token t:
  *   out[t,:] = bf16( sum over k = 0..K-1 with route_row[t*K+k] >= 0 of
- *                    topk_w[t,k] * y_f32[route_row[t*K+k], :] )
- * in float32, k ascending, each term a product then an add; a token with no
- * kept route gets +0.
+ *                    topk_w[t,k] * y_bf16[route_row[t*K+k], :] )
+ * in float32 (each y value widened exactly), k ascending, each term a
+ * product then an add; a token with no kept route gets +0.
  */
 int moe_combine(const moe_shape *shape, const float *topk_w, const int32_t *route_row,
-                const float *y_f32, uint16_t *out_bf16, void *stream);
+                const uint16_t *y_bf16, uint16_t *out_bf16, void *stream);
 
 /*
  * The whole layer: dispatch, GEMM1 + SwiGLU + requant, GEMM2, combine, with
