@@ -53,6 +53,9 @@ def parse():
                    help="routes in the oracle's timed sample")
     p.add_argument("--kernel-iters", type=int, default=0,
                    help="launches per kernel for the roofline timing (default: steps)")
+    p.add_argument("--persistent", action="store_true",
+                   help="time moe_forward_persistent (GEMM1 and GEMM2 in one persistent "
+                        "launch; 128-row tile sizes only)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the layer, time a plain device copy of this many MiB "
                         "(the reference size for the HBM byte counters)")
@@ -151,7 +154,8 @@ def main():
 
     def forward(stream=None):
         moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
-                        g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream)
+                        g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream,
+                        persistent=args.persistent)
 
     # ---- whole layer: graph replays ---------------------------------------------
     forward()
@@ -236,7 +240,8 @@ def main():
                    "K": spec.K, "E_total": spec.E_total, "E_local": spec.E_local,
                    "dispatch": "fixed-slot" if spec.dispatch_mode else "compact",
                    "capacity": spec.capacity, "routes": work["routes"],
-                   "touched_experts": work["touched"]},
+                   "touched_experts": work["touched"],
+                   "forward": "persistent" if args.persistent else "four launches"},
         "us_per_layer": round(us, 2),
         "routed_tflops": round(tflops, 3),
         "weight_gbps": round(weight_gbs, 2),

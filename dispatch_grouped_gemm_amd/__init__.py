@@ -7,6 +7,7 @@ of any entry point raises.
 
 Entry points (same names as the C ABI):
     moe_dispatch, moe_gemm1_swiglu, moe_gemm2, moe_combine, moe_forward,
+    moe_forward_persistent,
     moe_workspace_size, moe_dispatch_workspace_size, moe_row_capacity,
     moe_check_shape, moe_strerror
 """
@@ -23,7 +24,8 @@ import torch
 __all__ = [
     "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
     "moe_dispatch_workspace_size", "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu",
-    "moe_gemm2", "moe_combine", "moe_forward", "moe_strerror", "DispatchBuffers",
+    "moe_gemm2", "moe_combine", "moe_forward", "moe_forward_persistent", "moe_strerror",
+    "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT",
 ]
 
@@ -35,7 +37,7 @@ library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
             "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
-            "moe_combine", "moe_forward", "moe_strerror"]
+            "moe_combine", "moe_forward", "moe_forward_persistent", "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -111,6 +113,8 @@ def lib() -> ctypes.CDLL:
         h.moe_combine.restype = ctypes.c_int
         h.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         h.moe_forward.restype = ctypes.c_int
+        h.moe_forward_persistent.argtypes = h.moe_forward.argtypes
+        h.moe_forward_persistent.restype = ctypes.c_int
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -292,7 +296,8 @@ def moe_combine(shape: MoeShape, topk_w, route_row, y_bf16, out_bf16, stream=Non
 
 
 def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2,
-                w2_scale, out_bf16, workspace, stream=None):
+                w2_scale, out_bf16, workspace, stream=None, persistent=False):
+    """The layer; persistent=True calls moe_forward_persistent."""
     dev = x_fp8.device
     T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
     bf = {torch.bfloat16, torch.uint16, torch.int16}
@@ -307,5 +312,12 @@ def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scal
             _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
     ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
     c = shape.c()
-    _check(lib().moe_forward(ctypes.byref(c), *args, ws, workspace.numel(),
-                             _stream(stream, dev)), "moe_forward")
+    fn, name = ((lib().moe_forward_persistent, "moe_forward_persistent") if persistent
+                else (lib().moe_forward, "moe_forward"))
+    _check(fn(ctypes.byref(c), *args, ws, workspace.numel(), _stream(stream, dev)), name)
+
+
+def moe_forward_persistent(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale,
+                           w2, w2_scale, out_bf16, workspace, stream=None):
+    moe_forward(shape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2, w2_scale,
+                out_bf16, workspace, stream=stream, persistent=True)

@@ -43,7 +43,10 @@ Layout layout_of(const moe_shape &s)
     L.status = p;
     p = align_up(p + sizeof(int32_t) * 4);
     L.sync = p;
-    p = align_up(p + sizeof(int32_t) * (size_t)moe::fused_sync_words(s));
+    const int sync_words = moe::fused_sync_words(s) > moe::persistent_sync_words(s)
+                               ? moe::fused_sync_words(s)
+                               : moe::persistent_sync_words(s);
+    p = align_up(p + sizeof(int32_t) * (size_t)sync_words);
     L.scratch = p;
     p = align_up(p + moe::dispatch_scratch_bytes(s));
     L.h = p;
@@ -182,13 +185,21 @@ int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, c
     return hip_status(moe::launch_combine(*s, tw, route_row, y, out, as_stream(stream)));
 }
 
-int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
-                const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
-                const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+// The layer; `persistent` runs GEMM1 and GEMM2 in one persistent launch.
+int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
+                 const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                 const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
+                 bool persistent)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
         return rc;
+    if (persistent && !moe::persistent_supported(*s))
+        return MOE_ENOTSUP;
     if (s->T == 0)
         return MOE_OK;
     if (!x || !xs || !ids || !tw || !w13 || !w13s || !w2 || !w2s || !out)
@@ -223,13 +234,39 @@ int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const i
     }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st);
-    if (e == hipSuccess)
-        e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
-    if (e == hipSuccess)
-        e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
+    if (persistent) {
+        int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
+        if (e == hipSuccess)
+            e = moe::launch_layer_persistent(*s, x, xs, counts, offsets, row_route, w13, w13s, w2,
+                                             w2s, h, hs, y, sync, st);
+    } else {
+        if (e == hipSuccess)
+            e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
+        if (e == hipSuccess)
+            e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
+    }
     if (e == hipSuccess)
         e = moe::launch_combine(*s, tw, route_row, y, out, st);
     return hip_status(e);
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
+                const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(s, x, xs, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes, stream, false);
+}
+
+int moe_forward_persistent(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
+                           const int32_t *ids, const float *tw, const uint8_t *w13,
+                           const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                           uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(s, x, xs, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes, stream, true);
 }
 
 const char *moe_strerror(int code)

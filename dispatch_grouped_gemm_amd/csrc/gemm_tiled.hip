@@ -69,11 +69,18 @@ __device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
 // wait state after an SALU write of m0 at the earliest, hence the s_nop.
 // kStream marks data read once (non-temporal: the L2 evicts it first, so it
 // does not push out the activation rows that other tiles read again).
-template <int SIZE, bool kStream = false>
+// kDevice reads at device scope (sc1): data another XCD wrote in the same
+// launch with device-scope stores, which this XCD's L2 may hold stale.
+template <int SIZE, bool kStream = false, bool kDevice = false>
 __device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
 {
     static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
-    if (SIZE == 16 && kStream)
+    static_assert(!(kStream && kDevice), "one cache policy");
+    if (SIZE == 16 && kDevice)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc1" ::"s"(m0),
+                     "v"(voff), "s"(base)
+                     : "memory", "m0");
+    else if (SIZE == 16 && kStream)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0),
                      "v"(voff), "s"(base)
                      : "memory", "m0");
@@ -103,14 +110,36 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <bool kGemm1, int BM, int BN, int KU>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__restrict__ act_s,
-                  const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-                  const int32_t *__restrict__ row_route, const uint8_t *__restrict__ w,
-                  const uint8_t *__restrict__ ws, uint8_t *__restrict__ h_out,
-                  uint8_t *__restrict__ hs_out, uint16_t *__restrict__ y_out)
+// Operands of one GEMM launch.
+struct TiledArgs {
+    const uint8_t *act, *act_s;             // FP8 activation rows (x or h) and exponents
+    const int32_t *counts, *offsets, *row_route;
+    const uint8_t *w, *ws;                  // W13 or W2 codes and exponents
+    uint8_t *h_out, *hs_out;                // GEMM1 output
+    uint16_t *y_out;                        // GEMM2 output
+};
+
+// One work item: N tile nt of row chunk q.  prefix holds the chunk plan,
+// arow (BM ints) and lds (the stage ring) are the workgroup's.  kDevice:
+// GEMM1 stores h at device scope and GEMM2 reads it at device scope (the
+// persistent layer, where GEMM1 and GEMM2 items of one launch meet on
+// different XCDs).  Ends with the workgroup's LDS still in use: the caller
+// synchronises before the next item.
+template <bool kGemm1, int BM, int BN, int KU, bool kDevice>
+__device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
+                                           const int *prefix, int *arow, uint8_t *lds, int q,
+                                           int nt)
 {
+    const uint8_t *__restrict__ act = g.act;
+    const uint8_t *__restrict__ act_s = g.act_s;
+    const int32_t *__restrict__ counts = g.counts;
+    const int32_t *__restrict__ offsets = g.offsets;
+    const int32_t *__restrict__ row_route = g.row_route;
+    const uint8_t *__restrict__ w = g.w;
+    const uint8_t *__restrict__ ws = g.ws;
+    uint8_t *__restrict__ h_out = g.h_out;
+    uint8_t *__restrict__ hs_out = g.hs_out;
+    uint16_t *__restrict__ y_out = g.y_out;
     using L = TileLds<BM, BN, KU>;
     // 64-row tiles: an expert's weights are read by one row chunk (as a
     // rule), so they stream through the L2 without displacing the
@@ -122,10 +151,6 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
     constexpr int NS = L::kStages;
     constexpr int WROW = 64 * KU;           // LDS bytes of one weight row in a stage
     constexpr int WSWZ = 4 * KU - 1;        // chunk swizzle mask of the weight rows
-    __shared__ __align__(16) uint8_t lds[NS * L::kStage + L::kExpSlots * L::kExp];
-    __shared__ int prefix[kMaxLocalExperts + 1];
-    __shared__ int arow[BM];                // activation row of each tile row
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, kq = lane >> 4;
     const int wn = wave & 1, wm = wave >> 1;
@@ -133,13 +158,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
     const int KT = kGemm1 ? H : I;          // contraction length
     const int KS = KT / 128;                // K steps
     const int U = (KS + KU - 1) / KU;       // stages
-    const int NT = kGemm1 ? I / (BN / 2) : H / BN;
-    const int nchunks = plan_chunks(s, counts, BM, prefix);
-
-    const long items = (long)nchunks * NT;
-
-    for (long item = blockIdx.x; item < items; item += gridDim.x) {
-        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
+    {
         const int e = chunk_expert(prefix, s.E_local, q);
         const int c = q - prefix[e];
         const int row0 = offsets[e] + c * BM;
@@ -238,7 +257,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
 #pragma unroll
                     for (int i = 0; i < TB; ++i)
                         if (xrow_used[i])
-                            g2lds<16>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
+                            g2lds<16, false, kDevice>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
                                       lds_x + st + (uint32_t)(kk * BM * 128) + 4096u * i);
                 }
             if ((ks0 & 3) == 0) {
@@ -247,7 +266,7 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                 const uint32_t eb = (uint32_t)ebase(grp);
                 g2lds<16>(ws, weoff + eb, lds_we + es);
                 if (xe_used)
-                    g2lds<16>(act_s, xeoff + eb, lds_xe + es);
+                    g2lds<16, false, kDevice>(act_s, xeoff + eb, lds_xe + es);
             }
         };
 
@@ -348,11 +367,22 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
                                 pk |= f32_to_e4m3(ldexpf(hv[cb][v], -E)) << (8 * v);
-                            *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + col0 +
-                                                          16 * (cb - 2 * blk) + 4 * kq) = pk;
+                            uint32_t *hp = reinterpret_cast<uint32_t *>(
+                                h_out + row * (size_t)I + col0 + 16 * (cb - 2 * blk) + 4 * kq);
+                            if (kDevice)
+                                __hip_atomic_store(hp, pk, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                *hp = pk;
                         }
-                        if (kq == 0)
-                            hs_out[row * (size_t)(I / 32) + col0 / 32] = (uint8_t)(E + 127);
+                        if (kq == 0) {
+                            uint8_t *sp = hs_out + row * (size_t)(I / 32) + col0 / 32;
+                            if (kDevice)
+                                __hip_atomic_store(sp, (uint8_t)(E + 127), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                *sp = (uint8_t)(E + 127);
+                        }
                     }
                 }
             }
@@ -371,6 +401,97 @@ gemm_tiled_kernel(Shape s, const uint8_t *__restrict__ act, const uint8_t *__res
                 }
             }
         }
+    }
+}
+
+// LDS of a workgroup running BM-row tiles with the given stage ring.
+template <int BM, int BN, int KU>
+struct TileShared {
+    using L = TileLds<BM, BN, KU>;
+    __align__(16) uint8_t ring[L::kStages * L::kStage + L::kExpSlots * L::kExp];
+    int prefix[kMaxLocalExperts + 1];
+    int arow[BM];
+};
+
+// ---------------------------------------------------------------------------
+// The persistent layer for 128-row tiles: GEMM1 + SwiGLU + requant and GEMM2
+// in one launch.  Workgroups take tickets from one counter, first every
+// GEMM1 item (row chunk by row chunk), then every GEMM2 item; a GEMM2 item
+// of chunk q waits until ready[q] counts all NT1 GEMM1 items of q, so GEMM2
+// starts on the first chunks while GEMM1 finishes the last ones.  Tickets
+// go out in dependency order, so every wait is on items that running
+// workgroups hold.  h crosses XCDs: GEMM1 stores it at device scope and
+// counts an item only once its stores are done; GEMM2 reads it at device
+// scope.  sync[0] is the ticket counter, sync[1 + q] = ready[q], all zero at
+// launch.  Every wait is bounded: past the bound a workgroup goes on (wrong
+// numbers, which the tests would catch, rather than a GPU that never
+// finishes).
+template <int BM, int BN1, int BN2>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync)
+{
+    // one stage ring, sized for the wider of the two weight tiles
+    __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), 1> sh;
+    __shared__ int ticket_sh;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int NT1 = s.I / (BN1 / 2), NT2 = s.H / BN2;
+    const int nchunks = plan_chunks(s, g1.counts, BM, sh.prefix);
+    const int n1 = nchunks * NT1, n2 = nchunks * NT2;
+    int32_t *ticket = sync, *ready = sync + 1;
+    for (;;) {
+        // wavefront 0 takes the ticket (whole-wavefront atomic, value 1 in
+        // lane 0: control flow stays uniform) and hands it to the others
+        if (wave == 0) {
+            const int t0 = atomicAdd(ticket, lane == 0 ? 1 : 0);
+            ticket_sh = __builtin_amdgcn_readfirstlane(t0);
+        }
+        __syncthreads();
+        const int t = ticket_sh;
+        __syncthreads();
+        if (t >= n1 + n2)
+            break;
+        if (t < n1) {
+            const int q = t / NT1, nt = t - q * NT1;
+            tiled_item<true, BM, BN1, 1, true>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
+            wait_vmcnt<0>();   // this thread's h stores have reached device scope
+            __syncthreads();   // ... and every thread's
+            if (wave == 0)
+                atomicAdd(&ready[q], lane == 0 ? 1 : 0);
+        } else {
+            const int q = (t - n1) / NT2, nt = (t - n1) - q * NT2;
+            if (wave == 0) {
+                for (int it = 0; it < (1 << 22); ++it) {
+                    const int v = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(&ready[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    if (v >= NT1)
+                        break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+            tiled_item<false, BM, BN2, 1, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
+            __syncthreads();
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(int32_t *p, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+        p[i] = 0;
+}
+
+template <bool kGemm1, int BM, int BN, int KU>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_tiled_kernel(Shape s, TiledArgs g)
+{
+    __shared__ TileShared<BM, BN, KU> sh;
+    const int NT = kGemm1 ? s.I / (BN / 2) : s.H / BN;
+    const int nchunks = plan_chunks(s, g.counts, BM, sh.prefix);
+    const long items = (long)nchunks * NT;
+    for (long item = blockIdx.x; item < items; item += gridDim.x) {
+        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
+        tiled_item<kGemm1, BM, BN, KU, false>(s, g, sh.prefix, sh.arow, sh.ring, q, nt);
         __syncthreads();
     }
 }
@@ -447,8 +568,8 @@ hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *
     auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU>;
     const long nt = kGemm1 ? sh.I / (BN / 2) : sh.H / BN;
     const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt);
-    k<<<grid, kThreads, 0, st>>>(to_dev(sh), act, act_s, counts, offsets, row_route, w, ws, h, hs,
-                                 y);
+    k<<<grid, kThreads, 0, st>>>(to_dev(sh),
+                                 TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs, y});
     return hipGetLastError();
 }
 
@@ -479,6 +600,45 @@ hipError_t launch_gemm1_tiled(const moe_shape &sh, const uint8_t *x, const uint8
 {
     return launch_tiled_any<true>(sh, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
                                   nullptr, st);
+}
+
+// The persistent layer takes the 128-row tiles (the prefill sizes) of both
+// GEMMs.
+bool persistent_supported(const moe_shape &sh)
+{
+    if (sh.H < 512 || sh.I < 512)
+        return false;
+    const TiledConfig a = tiled_config(sh, true), b = tiled_config(sh, false);
+    return a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1;
+}
+
+int persistent_sync_words(const moe_shape &sh) { return 1 + (int)tile_upper_bound(sh, 128); }
+
+hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
+                                   const int32_t *counts, const int32_t *offsets,
+                                   const int32_t *row_route, const uint8_t *w13,
+                                   const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                                   uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
+                                   hipStream_t st)
+{
+    const int nsync = persistent_sync_words(sh);
+    fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
+    const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr};
+    const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y};
+    const int bn1 = tiled_config(sh, true).bn, bn2 = tiled_config(sh, false).bn;
+    auto go = [&](auto k, int b1, int b2) {
+        const long items = tile_upper_bound(sh, 128) * (long)(sh.I / (b1 / 2) + sh.H / b2);
+        k<<<tiled_grid(k, items), kThreads, 0, st>>>(to_dev(sh), g1, g2, sync);
+    };
+    if (bn1 == 256 && bn2 == 256)
+        go(layer_persistent_kernel<128, 256, 256>, 256, 256);
+    else if (bn1 == 256)
+        go(layer_persistent_kernel<128, 256, 128>, 256, 128);
+    else if (bn2 == 256)
+        go(layer_persistent_kernel<128, 128, 256>, 128, 256);
+    else
+        go(layer_persistent_kernel<128, 128, 128>, 128, 128);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,

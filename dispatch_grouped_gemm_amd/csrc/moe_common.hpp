@@ -278,6 +278,16 @@ hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_
 hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                               const uint8_t *w2s, uint16_t *y, hipStream_t st);
+bool persistent_supported(const moe_shape &s);
+int persistent_sync_words(const moe_shape &s);
+// GEMM1 + SwiGLU + requant and GEMM2 in one persistent launch (after a
+// zero-fill of sync[0 .. persistent_sync_words)).
+hipError_t launch_layer_persistent(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
+                                   const int32_t *counts, const int32_t *offsets,
+                                   const int32_t *row_route, const uint8_t *w13,
+                                   const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                                   uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
+                                   hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
                           const uint16_t *y, uint16_t *out, hipStream_t st);
 

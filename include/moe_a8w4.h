@@ -168,6 +168,23 @@ int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_s
                 const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
                 uint16_t *out_bf16, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The same layer with GEMM1 + SwiGLU + requant and GEMM2 in one persistent
+ * launch ("MegaMoEV2 ...", Technical Details: the large-M path is a
+ * persistent kernel that overlaps the stages): workgroups take tickets from
+ * one counter, every GEMM1 item first, then every GEMM2 item, and a GEMM2
+ * item of a row chunk waits until all GEMM1 items of that chunk are done.
+ * Same arguments, workspace and result as moe_forward (the output bits are
+ * identical); MOE_ENOTSUP for shapes it does not cover (it takes the
+ * 128-row, 256-column tiles of the prefill sizes: H and I >= 512 and
+ * enough rows per expert).
+ */
+int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
+                           const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,
+                           const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
+                           uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

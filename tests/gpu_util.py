@@ -65,7 +65,8 @@ def run_steps(case: dict, g: dict | None = None) -> dict:
     return dict(d=d, h=h, hs=hs, y=y, out=out)
 
 
-def run_forward(case: dict, g: dict | None = None, ws: torch.Tensor | None = None):
+def run_forward(case: dict, g: dict | None = None, ws: torch.Tensor | None = None,
+                persistent: bool = False):
     spec = case["spec"]
     shape = shape_of(spec)
     g = g or upload(case)
@@ -73,7 +74,7 @@ def run_forward(case: dict, g: dict | None = None, ws: torch.Tensor | None = Non
         ws = moe.alloc_workspace(shape, DEV)
     out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
     moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
-                    g["w13_scale"], g["w2"], g["w2_scale"], out, ws)
+                    g["w13_scale"], g["w2"], g["w2_scale"], out, ws, persistent=persistent)
     return out
 
 
@@ -141,6 +142,38 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return e4m3_values()[codes] * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=1))
 
 
+def gemm1_mfma_bound(case: dict, routes: np.ndarray) -> np.ndarray:
+    """How far the GPU's pre-quantisation value of h may lie from the
+    oracle's, per route slot and column [n, I]: inside one 32-value K block
+    the scaled MFMA aligns the products to the largest and keeps about 14
+    bits below it, so a block sum is off by at most 32 * 2^-14 of its largest
+    term, in total at most 2^-9 * sum|x * w| for the gate sum g and the up
+    sum u; carried through the clamped SwiGLU (|d silu / dg| <= 1.1).  The
+    bound matters only where the sums cancel."""
+    from dense_ref import dec_fp4_rows, dec_fp8_rows
+    spec = case["spec"]
+    routes = np.asarray(routes, dtype=np.int64)
+    I = spec.I
+    toks = routes // spec.K
+    eids = case["topk_ids"].reshape(-1)[routes].astype(np.int64) - spec.expert_begin
+    x = dec_fp8_rows(case["x_fp8"][toks], case["x_scale"][toks])
+    g = np.zeros((routes.size, I))
+    u = np.zeros((routes.size, I))
+    ag = np.zeros((routes.size, I))
+    au = np.zeros((routes.size, I))
+    for e in np.unique(eids):
+        sel = eids == e
+        W = dec_fp4_rows(case["w13"][e], case["w13_scale"][e])
+        g[sel] = x[sel] @ W[:I].T
+        u[sel] = x[sel] @ W[I:].T
+        ag[sel] = np.abs(x[sel]) @ np.abs(W[:I]).T
+        au[sel] = np.abs(x[sel]) @ np.abs(W[I:]).T
+    gc = np.minimum(g, spec.gate_limit)
+    uc = np.clip(u, -spec.up_limit, spec.up_limit)
+    silu = gc / (1.0 + np.exp(-gc))
+    return 1.1 * np.abs(uc) * 2.0 ** -9 * ag + np.abs(silu) * 2.0 ** -9 * au
+
+
 def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dict,
                 what: str = "", max_flip_rate: float = 1e-3):
     """The layer output of `tokens` against the oracle.
@@ -150,8 +183,8 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
     (about 14 bits below its largest product), the oracle sums sequentially,
     so a value that sits at an e4m3 rounding boundary may round the other
     way.  Such a flip is accepted when the GPU code is a valid rounding of
-    the oracle's own pre-quantisation value (within one e4m3 step of it) and
-    flips are rare; its effect on the output, |w| * |W2[:, i]| * |step|
+    the oracle's own pre-quantisation value (within one e4m3 step of it, plus
+    the MFMA summation bound where the GEMM1 sums cancel) and flips are rare; its effect on the output, |w| * |W2[:, i]| * |step|
     (float64, oracle-decoded W2), is added to that token's allowance.
 
     The GPU keeps y in bf16 (the pages' expert output rows) where the oracle
@@ -182,7 +215,12 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
         # or a subnormal step of the block) of the oracle's own value
         blk = np.repeat(orc["h_scale"].astype(np.float64) - 127, 32, axis=1)
         step = np.maximum(np.abs(hq_gpu), np.abs(hq_ref)) / 8 + np.exp2(blk - 9)
-        assert (np.abs(hq_gpu - hv)[flips] <= step[flips] * 1.0001).all(), what + ": invalid code"
+        far = flips & (np.abs(hq_gpu - hv) > step * 1.0001)
+        if far.any():
+            sel = np.nonzero(far.any(axis=1))[0]
+            dh = gemm1_mfma_bound(case, routes[sel])
+            ok = np.abs(hq_gpu[sel] - hv[sel]) <= (step[sel] + dh) * 1.0001
+            assert ok[far[sel]].all(), what + ": invalid code"
         ids = case["topk_ids"].reshape(-1)
         w = case["topk_w"].reshape(-1)
         for j, (i, r) in enumerate(slots):

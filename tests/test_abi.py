@@ -89,6 +89,10 @@ def test_refusals_return_before_any_launch(lib):
     assert lib.moe_gemm1_swiglu(ctypes.byref(c), *([fake] * 6), odd, fake, fake, null) == -1
     assert lib.moe_gemm2(ctypes.byref(c), *([fake] * 6), odd, null) == -1
     assert lib.moe_combine(ctypes.byref(c), fake, fake, odd, fake, null) == -1
+    # the persistent variant takes 128-row tiles only: refused at decode sizes
+    assert lib.moe_forward_persistent(ctypes.byref(c), *([fake] * 9), fake, 1 << 40, null) == -2
+    pre = moe.MoeShape(**{**V4, "T": 65536}).c()
+    assert lib.moe_forward_persistent(ctypes.byref(pre), *([null] * 10), 0, null) == -1
     # T = 0 is a no-op for the steps that have nothing to do
     z = moe.MoeShape(**{**V4, "T": 0}).c()
     assert lib.moe_forward(ctypes.byref(z), *([null] * 10), 0, null) == 0

@@ -20,8 +20,9 @@ import torch
 import dispatch_grouped_gemm_amd as moe
 import oracle
 import synth
-from gpu_util import (DEV, bf16_f64, bf16_ulp, cached_case, check_layer, dev, host, run_dispatch,
-                      run_forward, run_steps, say, sample_tokens, shape_of, upload)
+from gpu_util import (DEV, bf16_f64, bf16_ulp, cached_case, check_layer, dev, gemm1_mfma_bound,
+                      host, run_dispatch, run_forward, run_steps, say, sample_tokens, shape_of,
+                      upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,7 +121,6 @@ def _gemm1_compare(case, steps, rows_to_check=None):
     32 * 2^-14 of its largest term: in total at most 2^-9 * sum|x * w| for
     the gate sum g and the up sum u.  That bound matters only where the sums
     cancel; differing codes must still be rare."""
-    from dense_ref import dec_fp4_rows, dec_fp8_rows
     spec = case["spec"]
     d = steps["d"]
     rr = host(d.route_row)
@@ -139,27 +139,7 @@ def _gemm1_compare(case, steps, rows_to_check=None):
     hv = ref["hv"].astype(np.float64)
     diff = got != want
     n = diff.sum()
-    # float64 gate / up sums and the sums of absolute terms, per route
-    I = spec.I
-    toks = routes // spec.K
-    eids = case["topk_ids"].reshape(-1)[routes].astype(np.int64) - spec.expert_begin
-    x = dec_fp8_rows(case["x_fp8"][toks], case["x_scale"][toks])
-    g = np.zeros((routes.size, I))
-    u = np.zeros((routes.size, I))
-    ag = np.zeros((routes.size, I))
-    au = np.zeros((routes.size, I))
-    for e in np.unique(eids):
-        sel = eids == e
-        W = dec_fp4_rows(case["w13"][e], case["w13_scale"][e])
-        g[sel] = x[sel] @ W[:I].T
-        u[sel] = x[sel] @ W[I:].T
-        ag[sel] = np.abs(x[sel]) @ np.abs(W[:I]).T
-        au[sel] = np.abs(x[sel]) @ np.abs(W[I:]).T
-    gc = np.minimum(g, spec.gate_limit)
-    uc = np.clip(u, -spec.up_limit, spec.up_limit)
-    silu = gc / (1.0 + np.exp(-gc))
-    # |d silu / dg| <= 1.1 everywhere
-    dh = 1.1 * np.abs(uc) * 2.0 ** -9 * ag + np.abs(silu) * 2.0 ** -9 * au
+    dh = gemm1_mfma_bound(case, routes)
     # one e4m3 step: 1/8 of the larger magnitude, or a subnormal step of the block
     step = np.maximum(np.abs(got), np.abs(hv)) / 8 + np.exp2(
         np.repeat(hs.astype(np.float64) - 127 - 9, 32, axis=1))
@@ -287,6 +267,37 @@ def test_short_contraction_path(T, H, I):
     register-streaming kernels; 400 tokens (about 75 rows per expert) give
     them 64-row chunks, 64 tokens 16-row chunks."""
     _small_layer(T, H, I, "short contraction")
+
+
+@pytest.mark.parametrize("T,H,I", [(1200, 512, 512), (600, 640, 512)])
+def test_persistent_layer_small(T, H, I):
+    """moe_forward_persistent (GEMM1 and GEMM2 in one persistent launch,
+    128-row tiles) gives the bits of moe_forward, twice in a row on one
+    workspace (each call clears its ticket and ready counters), and the
+    layer matches the oracle on every token."""
+    case = synth.make_case("tiny", T=T, H=H, I=I, seed=1300 + T + H)
+    shape = shape_of(case["spec"])
+    say("persistent small T H I", T, H, I)
+    g = upload(case)
+    ws = moe.alloc_workspace(shape, DEV)
+    ref = host(run_forward(case, g, ws))
+    for _ in range(2):
+        np.testing.assert_array_equal(host(run_forward(case, g, ws, persistent=True)), ref)
+    steps = run_steps(case, g)
+    torch.cuda.synchronize()
+    check_layer(case, np.arange(T), ref, steps, "persistent T=%d H=%d I=%d" % (T, H, I))
+
+
+@pytest.mark.parametrize("name", ["v4_prefill_t65536_uniform", "v4_prefill_t65536_hot30"])
+def test_persistent_layer_full_size(name):
+    """The persistent layer on the prefill workloads: every output element
+    equals moe_forward's (which the sampled oracle checks cover)."""
+    case = cached_case(name)
+    say("persistent", name)
+    g = upload(case)
+    ref = host(run_forward(case, g))
+    got = host(run_forward(case, g, persistent=True))
+    np.testing.assert_array_equal(got, ref)
 
 
 def test_forward_tiny_in_a_graph():
