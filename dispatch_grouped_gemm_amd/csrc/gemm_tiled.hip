@@ -69,15 +69,16 @@ __device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
 // wait state after an SALU write of m0 at the earliest, hence the s_nop.
 // kStream marks data read once (non-temporal: the L2 evicts it first, so it
 // does not push out the activation rows that other tiles read again).
-// kDevice reads at device scope (sc1): data another XCD wrote in the same
-// launch with device-scope stores, which this XCD's L2 may hold stale.
-template <int SIZE, bool kStream = false, bool kDevice = false>
+// kL2 reads data that another CU of the same XCD wrote earlier in the same
+// launch: sc0 makes the load miss the CU's own L1, which may hold the line
+// from before the write, and take it from the XCD's L2, where the write is.
+template <int SIZE, bool kStream = false, bool kL2 = false>
 __device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
 {
     static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
-    static_assert(!(kStream && kDevice), "one cache policy");
-    if (SIZE == 16 && kDevice)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc1" ::"s"(m0),
+    static_assert(!(kStream && kL2), "one cache policy");
+    if (SIZE == 16 && kL2)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc0" ::"s"(m0),
                      "v"(voff), "s"(base)
                      : "memory", "m0");
     else if (SIZE == 16 && kStream)
@@ -120,12 +121,11 @@ struct TiledArgs {
 };
 
 // One work item: N tile nt of row chunk q.  prefix holds the chunk plan,
-// arow (BM ints) and lds (the stage ring) are the workgroup's.  kDevice:
-// GEMM1 stores h at device scope and GEMM2 reads it at device scope (the
-// persistent layer, where GEMM1 and GEMM2 items of one launch meet on
-// different XCDs).  Ends with the workgroup's LDS still in use: the caller
-// synchronises before the next item.
-template <bool kGemm1, int BM, int BN, int KU, bool kDevice>
+// arow (BM ints) and lds (the stage ring) are the workgroup's.  kL2: GEMM2
+// reads h through the XCD's L2, past the CU's L1 (the persistent layer,
+// where GEMM1 items of the same launch and XCD wrote it).  Ends with the
+// workgroup's LDS still in use: the caller synchronises before the next item.
+template <bool kGemm1, int BM, int BN, int KU, bool kL2>
 __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                                            const int *prefix, int *arow, uint8_t *lds, int q,
                                            int nt)
@@ -257,7 +257,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
 #pragma unroll
                     for (int i = 0; i < TB; ++i)
                         if (xrow_used[i])
-                            g2lds<16, false, kDevice>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
+                            g2lds<16, false, kL2>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
                                       lds_x + st + (uint32_t)(kk * BM * 128) + 4096u * i);
                 }
             if ((ks0 & 3) == 0) {
@@ -266,7 +266,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                 const uint32_t eb = (uint32_t)ebase(grp);
                 g2lds<16>(ws, weoff + eb, lds_we + es);
                 if (xe_used)
-                    g2lds<16, false, kDevice>(act_s, xeoff + eb, lds_xe + es);
+                    g2lds<16, false, kL2>(act_s, xeoff + eb, lds_xe + es);
             }
         };
 
@@ -367,22 +367,11 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
                                 pk |= f32_to_e4m3(ldexpf(hv[cb][v], -E)) << (8 * v);
-                            uint32_t *hp = reinterpret_cast<uint32_t *>(
-                                h_out + row * (size_t)I + col0 + 16 * (cb - 2 * blk) + 4 * kq);
-                            if (kDevice)
-                                __hip_atomic_store(hp, pk, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                            else
-                                *hp = pk;
+                            *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + col0 +
+                                                          16 * (cb - 2 * blk) + 4 * kq) = pk;
                         }
-                        if (kq == 0) {
-                            uint8_t *sp = hs_out + row * (size_t)(I / 32) + col0 / 32;
-                            if (kDevice)
-                                __hip_atomic_store(sp, (uint8_t)(E + 127), __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                            else
-                                *sp = (uint8_t)(E + 127);
-                        }
+                        if (kq == 0)
+                            hs_out[row * (size_t)(I / 32) + col0 / 32] = (uint8_t)(E + 127);
                     }
                 }
             }
@@ -415,20 +404,25 @@ struct TileShared {
 
 // ---------------------------------------------------------------------------
 // The persistent layer for 128-row tiles: GEMM1 + SwiGLU + requant and GEMM2
-// in one launch.  Workgroups take tickets from one counter, first every
-// GEMM1 item (row chunk by row chunk), then every GEMM2 item; a GEMM2 item
-// of chunk q waits until ready[q] counts all NT1 GEMM1 items of q, so GEMM2
-// starts on the first chunks while GEMM1 finishes the last ones.  Tickets
-// go out in dependency order, so every wait is on items that running
-// workgroups hold.  h crosses XCDs: GEMM1 stores it at device scope and
-// counts an item only once its stores are done; GEMM2 reads it at device
-// scope.  sync[0] is the ticket counter, sync[1 + q] = ready[q], all zero at
-// launch.  Every wait is bounded: past the bound a workgroup goes on (wrong
-// numbers, which the tests would catch, rather than a GPU that never
-// finishes).
+// in one launch, one work queue per XCD.  Row chunk q belongs to queue
+// q mod nq; a workgroup serves the queue of the XCD it runs on (hardware
+// XCC id mod nq, nq = the device's XCD count), so the h rows of a chunk are
+// written and read through one L2.  A queue hands out tickets for first
+// every GEMM1 item of its chunks, then every GEMM2 item; a GEMM2 item of
+// chunk q waits until ready[q] counts all NT1 GEMM1 items of q, so GEMM2
+// starts on the first chunks while GEMM1 finishes the last ones.  A
+// workgroup takes its next ticket when it starts an item (the atomic's
+// round trip hides behind the item); tickets go out in dependency order
+// and a workgroup's tickets rise, so every wait is on items that running
+// workgroups hold and reach first.  A GEMM1 item counts in ready[q] once
+// its h stores are in the L2; GEMM2 reads h past the CU's L1.
+// sync[32 x] is queue x's ticket counter (one 128-byte line each),
+// sync[256 + q] = ready[q], all zero at launch.  Every wait is bounded:
+// past the bound a workgroup goes on (wrong numbers, which the tests would
+// catch, rather than a GPU that never finishes).
 template <int BM, int BN1, int BN2>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync)
+layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int nq)
 {
     // one stage ring, sized for the wider of the two weight tiles
     __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), 1> sh;
@@ -436,29 +430,36 @@ layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int NT1 = s.I / (BN1 / 2), NT2 = s.H / BN2;
     const int nchunks = plan_chunks(s, g1.counts, BM, sh.prefix);
-    const int n1 = nchunks * NT1, n2 = nchunks * NT2;
-    int32_t *ticket = sync, *ready = sync + 1;
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const int x = (int)(xcc & 7u) % nq;
+    const int mine = nchunks > x ? (nchunks - x + nq - 1) / nq : 0;
+    const int n1 = mine * NT1, n2 = mine * NT2;
+    int32_t *ticket = sync + 32 * x, *ready = sync + 256;
+    // wavefront 0 takes tickets (whole-wavefront atomic, value 1 in lane 0:
+    // control flow stays uniform) and hands them to the others through LDS
+    if (wave == 0) {
+        const int t0 = atomicAdd(ticket, lane == 0 ? 1 : 0);
+        ticket_sh = __builtin_amdgcn_readfirstlane(t0);
+    }
+    __syncthreads();
     for (;;) {
-        // wavefront 0 takes the ticket (whole-wavefront atomic, value 1 in
-        // lane 0: control flow stays uniform) and hands it to the others
-        if (wave == 0) {
-            const int t0 = atomicAdd(ticket, lane == 0 ? 1 : 0);
-            ticket_sh = __builtin_amdgcn_readfirstlane(t0);
-        }
-        __syncthreads();
         const int t = ticket_sh;
         __syncthreads();
         if (t >= n1 + n2)
             break;
+        int next = 0;
+        if (wave == 0)
+            next = atomicAdd(ticket, lane == 0 ? 1 : 0);
         if (t < n1) {
-            const int q = t / NT1, nt = t - q * NT1;
-            tiled_item<true, BM, BN1, 1, true>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
-            wait_vmcnt<0>();   // this thread's h stores have reached device scope
+            const int q = x + nq * (t / NT1), nt = t % NT1;
+            tiled_item<true, BM, BN1, 1, false>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
+            wait_vmcnt<0>();   // this thread's h stores are in the L2
             __syncthreads();   // ... and every thread's
             if (wave == 0)
                 atomicAdd(&ready[q], lane == 0 ? 1 : 0);
         } else {
-            const int q = (t - n1) / NT2, nt = (t - n1) - q * NT2;
+            const int q = x + nq * ((t - n1) / NT2), nt = (t - n1) % NT2;
             if (wave == 0) {
                 for (int it = 0; it < (1 << 22); ++it) {
                     const int v = __builtin_amdgcn_readfirstlane(
@@ -470,8 +471,10 @@ layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync)
             }
             __syncthreads();
             tiled_item<false, BM, BN2, 1, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
-            __syncthreads();
         }
+        if (wave == 0)
+            ticket_sh = __builtin_amdgcn_readfirstlane(next);
+        __syncthreads();
     }
 }
 
@@ -602,17 +605,25 @@ hipError_t launch_gemm1_tiled(const moe_shape &sh, const uint8_t *x, const uint8
                                   nullptr, st);
 }
 
+// XCDs of the device: the MI355X has 32 CUs per XCD, and its partition modes
+// give a device 1, 2, 4 or 8 of them (0 for any other CU count).
+static int xcd_count()
+{
+    const int cus = device_cu_count();
+    return cus == 32 || cus == 64 || cus == 128 || cus == 256 ? cus / 32 : 0;
+}
+
 // The persistent layer takes the 128-row tiles (the prefill sizes) of both
-// GEMMs.
+// GEMMs, on a device whose XCDs it can tell apart.
 bool persistent_supported(const moe_shape &sh)
 {
-    if (sh.H < 512 || sh.I < 512)
+    if (sh.H < 512 || sh.I < 512 || xcd_count() == 0)
         return false;
     const TiledConfig a = tiled_config(sh, true), b = tiled_config(sh, false);
     return a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1;
 }
 
-int persistent_sync_words(const moe_shape &sh) { return 1 + (int)tile_upper_bound(sh, 128); }
+int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 128); }
 
 hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
                                    const int32_t *counts, const int32_t *offsets,
@@ -626,9 +637,13 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
     const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr};
     const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y};
     const int bn1 = tiled_config(sh, true).bn, bn2 = tiled_config(sh, false).bn;
+    const int nq = xcd_count();
+    // workgroup b runs on XCD b mod nq: a grid of nq or more workgroups puts
+    // at least one on every XCD, so every queue is served
     auto go = [&](auto k, int b1, int b2) {
         const long items = tile_upper_bound(sh, 128) * (long)(sh.I / (b1 / 2) + sh.H / b2);
-        k<<<tiled_grid(k, items), kThreads, 0, st>>>(to_dev(sh), g1, g2, sync);
+        const int grid = tiled_grid(k, items);
+        k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, nq);
     };
     if (bn1 == 256 && bn2 == 256)
         go(layer_persistent_kernel<128, 256, 256>, 256, 256);

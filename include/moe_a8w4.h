@@ -171,13 +171,16 @@ int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_s
 /*
  * The same layer with GEMM1 + SwiGLU + requant and GEMM2 in one persistent
  * launch ("MegaMoEV2 ...", Technical Details: the large-M path is a
- * persistent kernel that overlaps the stages): workgroups take tickets from
- * one counter, every GEMM1 item first, then every GEMM2 item, and a GEMM2
- * item of a row chunk waits until all GEMM1 items of that chunk are done.
- * Same arguments, workspace and result as moe_forward (the output bits are
- * identical); MOE_ENOTSUP for shapes it does not cover (it takes the
- * 128-row, 256-column tiles of the prefill sizes: H and I >= 512 and
- * enough rows per expert).
+ * persistent kernel that overlaps the stages): the row chunks are split over
+ * one work queue per XCD, whose workgroups take tickets for every GEMM1 item
+ * of the queue's chunks first, then every GEMM2 item; a GEMM2 item of a row
+ * chunk waits until all GEMM1 items of that chunk are done, and h passes
+ * between them through that XCD's L2.  Same arguments, workspace and result
+ * as moe_forward (the output bits are identical); MOE_ENOTSUP for shapes it
+ * does not cover (it takes the 128-row tiles of the prefill sizes: H and
+ * I >= 512 and enough rows per expert) and on a device whose CU count is not
+ * that of 1, 2, 4 or 8 MI355X XCDs.  Calls that overlap on one workspace
+ * race, as for moe_forward.
  */
 int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
                            const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,
