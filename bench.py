@@ -19,6 +19,10 @@ Reported (one JSON line):
                bytes per launch from the rocprofv3 counter summary
   cpu_baseline the CPU oracle timed on a bounded sample of the same batch
                (whole tokens), scaled to the full batch by its routes
+  cold         the same replay with the caches cold: before each replay a
+               512 MiB buffer (twice the 256 MB Infinity Cache) is written,
+               outside the timed span; each replay is timed alone with HIP
+               events; median and spread over the replays
 """
 
 from __future__ import annotations
@@ -53,6 +57,8 @@ def parse():
                    help="routes in the oracle's timed sample")
     p.add_argument("--kernel-iters", type=int, default=0,
                    help="launches per kernel for the roofline timing (default: steps)")
+    p.add_argument("--cold-steps", type=int, default=20,
+                   help="replays timed one by one after a 512 MiB cache flush (0: skip)")
     p.add_argument("--persistent", action="store_true",
                    help="time moe_forward_persistent (GEMM1 and GEMM2 in one persistent "
                         "launch; 128-row tile sizes only)")
@@ -174,6 +180,25 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
+    # ---- whole layer with cold caches: flush, then one timed replay ---------------
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        st0 = torch.cuda.current_stream()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for a, b in cev:
+            flush.fill_(1)
+            a.record(st0)
+            graph.replay()
+            b.record(st0)
+        torch.cuda.synchronize()
+        cus = np.array([a.elapsed_time(b) * 1e3 for a, b in cev])
+        cold = {"us_per_layer": round(float(np.median(cus)), 2),
+                "min": round(float(cus.min()), 2), "max": round(float(cus.max()), 2),
+                "replays": args.cold_steps, "flush_mib": 512}
+        del flush
+
     # ---- per-kernel times: the four steps back to back on one stream --------------
     d = moe.alloc_dispatch(shape, dev)
     R = max(moe.moe_row_capacity(shape), 1)
@@ -251,6 +276,9 @@ def main():
         "dispatch_status": status.tolist(),
         "roofline": roof,
     }
+    if cold is not None:
+        cold["weight_gbps"] = round(work["weight_bytes"] / (cold["us_per_layer"] * 1e-6) / 1e9, 2)
+        result["cold"] = cold
 
     if not args.no_cpu_baseline:
         import oracle
