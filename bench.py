@@ -59,6 +59,9 @@ def parse():
                    help="launches per kernel for the roofline timing (default: steps)")
     p.add_argument("--cold-steps", type=int, default=20,
                    help="replays timed one by one after a 512 MiB cache flush (0: skip)")
+    p.add_argument("--bf16-input", action="store_true",
+                   help="time moe_forward_bf16: the layer from bf16 activation rows, their "
+                        "MX FP8 quant included in the step")
     p.add_argument("--persistent", action="store_true",
                    help="time moe_forward_persistent (GEMM1 and GEMM2 in one persistent "
                         "launch; 128-row tile sizes only)")
@@ -158,7 +161,15 @@ def main():
     ws = moe.alloc_workspace(shape, dev)
     out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=dev)
 
+    if args.bf16_input and args.persistent:
+        print("--bf16-input and --persistent are separate entry points", file=sys.stderr)
+        sys.exit(2)
+
     def forward(stream=None):
+        if args.bf16_input:
+            moe.moe_forward_bf16(shape, g["x_bf16"], g["topk_ids"], g["topk_w"], g["w13"],
+                                 g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream)
+            return
         moe.moe_forward(shape, g["x_fp8"], g["x_scale"], g["topk_ids"], g["topk_w"], g["w13"],
                         g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream,
                         persistent=args.persistent)
@@ -207,11 +218,16 @@ def main():
     y = torch.empty((R, spec.H), dtype=torch.uint16, device=dev)
     st = torch.cuda.current_stream()
     iters = args.kernel_iters or args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(iters)]
+    xq = torch.empty((spec.T, spec.H), dtype=torch.uint8, device=dev)
+    xqs = torch.empty((spec.T, spec.H // 32), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e8))   # keep the GPU busy while the launches are queued
     for i in range(iters):
         e = ev[i]
+        e[5].record(st)
+        if args.bf16_input:
+            moe.moe_quant_mxfp8(shape, g["x_bf16"], xq, xqs, stream=st)
         e[0].record(st)
         moe.moe_dispatch(shape, g["topk_ids"], d, stream=st)
         e[1].record(st)
@@ -226,6 +242,11 @@ def main():
     names = ["dispatch", "gemm1_swiglu", "gemm2", "combine"]
     kern_us = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(iters)]))
                * 1e3 for j, n in enumerate(names)}
+    if args.bf16_input:
+        # the quant as a launch of its own (inside the layer it shares the
+        # dispatch launch where the dispatch is one workgroup)
+        kern_us = {"quant": float(np.mean([ev[i][5].elapsed_time(ev[i][0])
+                                           for i in range(iters)])) * 1e3, **kern_us}
     status = d.status.cpu().numpy()
 
     us = ms_per_step * 1e3
@@ -266,7 +287,9 @@ def main():
                    "dispatch": "fixed-slot" if spec.dispatch_mode else "compact",
                    "capacity": spec.capacity, "routes": work["routes"],
                    "touched_experts": work["touched"],
-                   "forward": "persistent" if args.persistent else "four launches"},
+                   "forward": "persistent" if args.persistent else "four launches",
+                   "input": "bf16 rows, quantised in the step" if args.bf16_input
+                   else "MX FP8 rows"},
         "us_per_layer": round(us, 2),
         "routed_tflops": round(tflops, 3),
         "weight_gbps": round(weight_gbs, 2),

@@ -37,7 +37,8 @@ library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
             "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
-            "moe_combine", "moe_forward", "moe_forward_persistent", "moe_strerror"]
+            "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
+            "moe_forward_bf16", "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -115,6 +116,10 @@ def lib() -> ctypes.CDLL:
         h.moe_forward.restype = ctypes.c_int
         h.moe_forward_persistent.argtypes = h.moe_forward.argtypes
         h.moe_forward_persistent.restype = ctypes.c_int
+        h.moe_quant_mxfp8.argtypes = [S, P, P, P, P]
+        h.moe_quant_mxfp8.restype = ctypes.c_int
+        h.moe_forward_bf16.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        h.moe_forward_bf16.restype = ctypes.c_int
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -293,6 +298,39 @@ def moe_combine(shape: MoeShape, topk_w, route_row, y_bf16, out_bf16, stream=Non
             _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
     c = shape.c()
     _check(lib().moe_combine(ctypes.byref(c), *args, _stream(stream, dev)), "moe_combine")
+
+
+def moe_quant_mxfp8(shape: MoeShape, x_bf16, x_fp8, x_scale, stream=None):
+    """bf16 activation rows [T, H] -> e4m3 codes [T, H] + E8M0 exponents [T, H/32]."""
+    dev = x_bf16.device
+    T, H = shape.T, shape.H
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(x_bf16, "x_bf16", (T, H), bf, dev),
+            _ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev),
+            _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev)]
+    c = shape.c()
+    _check(lib().moe_quant_mxfp8(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_quant_mxfp8")
+
+
+def moe_forward_bf16(shape: MoeShape, x_bf16, topk_ids, topk_w, w13, w13_scale, w2, w2_scale,
+                     out_bf16, workspace, stream=None):
+    """The layer from bf16 activation rows (quantised into the workspace first)."""
+    dev = x_bf16.device
+    T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(x_bf16, "x_bf16", (T, H), bf, dev),
+            _ptr(topk_ids, "topk_ids", (T, K), {torch.int32}, dev),
+            _ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
+            _ptr(w13, "w13", (E, 2 * I, H // 2), _fp4(), dev),
+            _ptr(w13_scale, "w13_scale", (E, 2 * I, H // 32), _e8m0("w13_scale"), dev),
+            _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
+            _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
+            _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
+    ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
+    c = shape.c()
+    _check(lib().moe_forward_bf16(ctypes.byref(c), *args, ws, workspace.numel(),
+                                  _stream(stream, dev)), "moe_forward_bf16")
 
 
 def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2,

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_a8w4.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "combine.hip"]
+SOURCES = ["api.hip", "dispatch.hip", "quant.hip", "gemm_skinny.hip", "gemm_tiled.hip",
+           "combine.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -23,7 +23,7 @@ bool all_aligned16(const P *...p)
 
 // Byte layout of the moe_forward workspace.
 struct Layout {
-    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, total;
+    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, xq, xqs, total;
 };
 
 Layout layout_of(const moe_shape &s)
@@ -55,6 +55,11 @@ Layout layout_of(const moe_shape &s)
     p = align_up(p + R * (size_t)(s.I / 32));
     L.y = p;
     p = align_up(p + R * (size_t)s.H * sizeof(uint16_t));
+    // MX FP8 activations of moe_forward_bf16
+    L.xq = p;
+    p = align_up(p + (size_t)s.T * (size_t)s.H);
+    L.xqs = p;
+    p = align_up(p + (size_t)s.T * (size_t)(s.H / 32));
     L.total = p;
     return L;
 }
@@ -170,6 +175,22 @@ int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int
         moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, as_stream(stream)));
 }
 
+int moe_quant_mxfp8(const moe_shape *s, const uint16_t *x, uint8_t *xq, uint8_t *xqs,
+                    void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!x || !xq || !xqs)
+        return MOE_EINVAL;
+    if (!all_aligned16(x, xq))
+        return MOE_EINVAL;
+    const moe::QuantJob q{x, xq, xqs, (long)s->T * (s->H / 32)};
+    return hip_status(moe::launch_quant_mxfp8(q, as_stream(stream)));
+}
+
 int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, const uint16_t *y,
                 uint16_t *out, void *stream)
 {
@@ -190,10 +211,12 @@ int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, c
 namespace {
 
 // The layer; `persistent` runs GEMM1 and GEMM2 in one persistent launch.
+// With x_bf16 the activations arrive as bf16 rows and are quantised into the
+// workspace first (x and xs are then ignored).
 int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
                  const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                  const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
-                 bool persistent)
+                 bool persistent, const uint16_t *x_bf16 = nullptr)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
@@ -202,14 +225,25 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
         return MOE_ENOTSUP;
     if (s->T == 0)
         return MOE_OK;
-    if (!x || !xs || !ids || !tw || !w13 || !w13s || !w2 || !w2s || !out)
-        return MOE_EINVAL;
-    if (!all_aligned16(x, xs, w13, w13s, w2, w2s, out))
-        return MOE_EINVAL;
     const Layout L = layout_of(*s);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    moe::QuantJob quant{nullptr, nullptr, nullptr, 0};
+    if (x_bf16) {
+        if (!all_aligned16(x_bf16))
+            return MOE_EINVAL;
+        if (base) {
+            x = base + L.xq;
+            xs = base + L.xqs;
+            quant = moe::QuantJob{x_bf16, base + L.xq, base + L.xqs, (long)s->T * (s->H / 32)};
+        }
+    }
+    if (!ids || !tw || !w13 || !w13s || !w2 || !w2s || !out || (!x_bf16 && (!x || !xs)))
+        return MOE_EINVAL;
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
         return MOE_EWORKSPACE;
-    uint8_t *base = static_cast<uint8_t *>(ws);
+    if (!all_aligned16(x, xs, w13, w13s, w2, w2s, out))
+        return MOE_EINVAL;
+    const moe::QuantJob *qj = x_bf16 ? &quant : nullptr;
     int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
     int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
     int32_t *row_route = reinterpret_cast<int32_t *>(base + L.row_route);
@@ -226,14 +260,14 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
         int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
         hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row,
                                             status, scratch, st, sync,
-                                            moe::fused_sync_words(*s));
+                                            moe::fused_sync_words(*s), qj);
         if (e == hipSuccess)
             e = moe::launch_fused_decode(*s, x, xs, counts, offsets, row_route, route_row, tw,
                                          w13, w13s, w2, w2s, h, hs, y, out, sync, st);
         return hip_status(e);
     }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
-                                        scratch, st);
+                                        scratch, st, nullptr, 0, qj);
     if (persistent) {
         int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
         if (e == hipSuccess)
@@ -267,6 +301,16 @@ int moe_forward_persistent(const moe_shape *s, const uint8_t *x, const uint8_t *
                            uint16_t *out, void *ws, size_t ws_bytes, void *stream)
 {
     return forward_impl(s, x, xs, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes, stream, true);
+}
+
+int moe_forward_bf16(const moe_shape *s, const uint16_t *x_bf16, const int32_t *ids,
+                     const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                     const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (s && s->T > 0 && !x_bf16)
+        return moe_check_shape(s) != MOE_OK ? moe_check_shape(s) : MOE_EINVAL;
+    return forward_impl(s, nullptr, nullptr, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes,
+                        stream, false, x_bf16);
 }
 
 const char *moe_strerror(int code)

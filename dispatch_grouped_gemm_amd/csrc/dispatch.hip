@@ -172,8 +172,14 @@ __global__ void __launch_bounds__(kThreads)
 compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                      int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
                      int32_t *__restrict__ route_row, int32_t *__restrict__ status,
-                     int32_t *__restrict__ zero, int nzero)
+                     int32_t *__restrict__ zero, int nzero, QuantJob quant)
 {
+    // workgroups past the first quantise the activation rows
+    if (blockIdx.x > 0) {
+        quant_mx8_part(quant, (long)(blockIdx.x - 1) * kThreads + threadIdx.x,
+                       (long)(gridDim.x - 1) * kThreads);
+        return;
+    }
     for (int i = threadIdx.x; i < nzero; i += kThreads)
         zero[i] = 0;
     extern __shared__ int hist[]; // [kWaves][E_local]
@@ -390,8 +396,14 @@ __global__ void __launch_bounds__(kThreads)
 fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                    int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
                    int32_t *__restrict__ route_row, int32_t *__restrict__ status,
-                   int32_t *__restrict__ zero, int nzero)
+                   int32_t *__restrict__ zero, int nzero, QuantJob quant)
 {
+    // workgroups past the first quantise the activation rows
+    if (blockIdx.x > 0) {
+        quant_mx8_part(quant, (long)(blockIdx.x - 1) * kThreads + threadIdx.x,
+                       (long)(gridDim.x - 1) * kThreads);
+        return;
+    }
     for (int i = threadIdx.x; i < nzero; i += kThreads)
         zero[i] = 0;
     extern __shared__ int cnt[]; // [E_local]
@@ -486,16 +498,24 @@ size_t dispatch_scratch_bytes(const moe_shape &s)
 hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
                            int32_t *status, void *scratch, hipStream_t st, int32_t *zero,
-                           int nzero)
+                           int nzero, const QuantJob *quant)
 {
     if (nzero > 0 && !dispatch_is_single_block(sh))
         return hipErrorInvalidValue;
     const Shape s = to_dev(sh);
     const size_t E = (size_t)sh.E_local;
+    // one-workgroup paths: the quant rides in extra workgroups of the launch
+    const QuantJob qj = quant ? *quant : QuantJob{nullptr, nullptr, nullptr, 0};
+    const int grid = 1 + (qj.blocks > 0 ? quant_blocks(qj, kThreads) : 0);
+    if (!dispatch_is_single_block(sh) && qj.blocks > 0) {
+        const hipError_t e = launch_quant_mxfp8(qj, st);
+        if (e != hipSuccess)
+            return e;
+    }
     if (sh.dispatch_mode == MOE_DISPATCH_COMPACT) {
         if (compact_is_small(sh)) {
-            compact_small_kernel<<<1, kThreads, kWaves * E * sizeof(int), st>>>(
-                s, ids, counts, offsets, row_route, route_row, status, zero, nzero);
+            compact_small_kernel<<<grid, kThreads, kWaves * E * sizeof(int), st>>>(
+                s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj);
             return hipGetLastError();
         }
         const int nblk = large_blocks(sh);
@@ -513,8 +533,8 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
         return hipGetLastError();
     }
     if (num_slots(sh) <= kSmallSlots) {
-        fixed_small_kernel<<<1, kThreads, E * sizeof(int), st>>>(s, ids, counts, offsets, row_route,
-                                                                  route_row, status, zero, nzero);
+        fixed_small_kernel<<<grid, kThreads, E * sizeof(int), st>>>(
+            s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj);
         return hipGetLastError();
     }
     fixed_reset_kernel<<<(int)((E + 256) / 256), 256, 0, st>>>(s, counts, offsets, status);

@@ -300,12 +300,8 @@ __device__ __forceinline__ void gemm1_item(const Shape &s, const LayerPtrs &p, c
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         const int E = mx8_block_exponent(amax);
-        uint32_t pk[2] = {0u, 0u};
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                pk[half] |= f32_to_e4m3(ldexpf(hv[half * 4 + v], -E)) << (8 * v);
+        const uint32_t pk[2] = {mx8_pack4(hv[0], hv[1], hv[2], hv[3], E, amax),
+                                mx8_pack4(hv[4], hv[5], hv[6], hv[7], E, amax)};
         if (rloc < nrows) {
             const size_t row = (size_t)(row0 + rloc);
             uint8_t *hr = p.h + row * (size_t)I + j0 + 4 * kq;

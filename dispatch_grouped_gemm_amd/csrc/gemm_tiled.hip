@@ -363,10 +363,8 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                         const int col0 = nt * (BN / 2) + (BN / 4) * wn + 32 * blk;
 #pragma unroll
                         for (int cb = 2 * blk; cb < 2 * blk + 2; ++cb) {
-                            uint32_t pk = 0;
-#pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                pk |= f32_to_e4m3(ldexpf(hv[cb][v], -E)) << (8 * v);
+                            const uint32_t pk =
+                                mx8_pack4(hv[cb][0], hv[cb][1], hv[cb][2], hv[cb][3], E, amax);
                             *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + col0 +
                                                           16 * (cb - 2 * blk) + 4 * kq) = pk;
                         }

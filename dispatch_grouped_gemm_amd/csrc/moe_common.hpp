@@ -66,36 +66,6 @@ __device__ __forceinline__ v4f mfma_w4a8(const v8i &a_fp4, const v8i &b_fp8, v4f
                                                             sb);
 }
 
-// ---------------------------------------------------------------------------
-// e4m3 encode (round to nearest even, saturate at 448) done on the float's
-// bit pattern: the 23-bit mantissa is cut to 3 bits.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
-{
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const uint32_t mag = bits & 0x7FFFFFFFu;
-    if (mag > 0x7F800000u)
-        return 0x7Fu;                           // NaN
-    if (mag >= 0x43E00000u)                     // |v| >= 448
-        return sign | 0x7Eu;
-    if (mag < 0x3C800000u) {                    // |v| < 2^-6: multiples of 2^-9
-        const float q = __uint_as_float(mag) * 512.0f;   // exact
-        return sign | (uint32_t)__builtin_rintf(q);       // 0..8
-    }
-    uint32_t expo = (mag >> 23) - 120u;         // biased e4m3 exponent, 1..15
-    uint32_t keep = (mag >> 20) & 7u;
-    const uint32_t rest = mag & 0xFFFFFu;
-    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u)))
-        ++keep;
-    if (keep == 8u) {
-        keep = 0;
-        ++expo;
-    }
-    const uint32_t code = (expo << 3) | keep;
-    return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
 // float -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint32_t f32_to_bf16(float v)
 {
@@ -115,6 +85,83 @@ __device__ __forceinline__ int mx8_block_exponent(float amax)
     (void)frexpf(amax, &ex);                    // amax in [2^(ex-1), 2^ex)
     int E = ex - 1 - 8;
     return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// Four values of a 1x32 block with exponent E as e4m3 codes, the first in
+// the low byte, by the hardware conversion (v_cvt_pk_fp8_f32, OCP e4m3 on
+// gfx950, round to nearest even): each value is first scaled by 2^-E (exact)
+// and clamped to +-448, so the conversion never overflows.  A block whose
+// largest magnitude is zero is all +0 codes (-0 inputs included), as its
+// exponent byte is 127.  Checked against the oracle on every bf16 value
+// below 2^9 at a block exponent of 0 (the scaling is exact, so that covers
+// every exponent), and on float32 values through GEMM1's requant codes.
+__device__ __forceinline__ uint32_t mx8_pack4(float a, float b, float c, float d, int E,
+                                              float amax)
+{
+    if (!(amax > 0.0f))
+        return 0u;
+    auto sc = [E](float v) { return __builtin_amdgcn_fmed3f(ldexpf(v, -E), -448.0f, 448.0f); };
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(a), sc(b), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(sc(c), sc(d), r, true);
+    return (uint32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+// BF16 activation rows to MX FP8 (the 1x32 rule of the requant above): the
+// step in front of the layer ("MegaMoEV2: fuse dispatch, GEMM1, GEMM2 and
+// combine into one kernel", Summary: the small-input path fuses the quant,
+// the large-input path runs it as its own kernel on the caller's stream).
+// Four consecutive threads take one 32-value block, thread j the values
+// 8j .. 8j+7 (one 16-byte load, one 8-byte store); the block's amax meets
+// over two lane exchanges.  Thread tid of nthreads (nthreads a multiple of
+// four) walks the blocks with a stride of nthreads / 4, four at a time.
+// ---------------------------------------------------------------------------
+struct QuantJob {
+    const uint16_t *x;   // [rows, H] bf16
+    uint8_t *codes;      // [rows, H] e4m3
+    uint8_t *scales;     // [rows, H / 32] E8M0
+    long blocks;         // rows * H / 32
+};
+
+__device__ __forceinline__ void quant_mx8_part(const QuantJob &q, long tid, long nthreads)
+{
+    // four blocks per pass, their loads issued together (the stream needs
+    // several loads in flight per thread to cover the memory latency)
+    constexpr int kU = 4;
+    const int j = (int)(tid & 3);
+    const long step = nthreads >> 2;
+    for (long g0 = tid >> 2; g0 < q.blocks; g0 += kU * step) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const long g = g0 + u * step;
+            if (g < q.blocks)
+                v[u] = *reinterpret_cast<const uint4 *>(q.x + 32 * g + 8 * j);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const long g = g0 + u * step;
+            if (g >= q.blocks)
+                break;
+            const float f[8] = {
+                __uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xFFFF0000u),
+                __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xFFFF0000u),
+                __uint_as_float(v[u].z << 16), __uint_as_float(v[u].z & 0xFFFF0000u),
+                __uint_as_float(v[u].w << 16), __uint_as_float(v[u].w & 0xFFFF0000u)};
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            const int E = mx8_block_exponent(amax);
+            *reinterpret_cast<uint2 *>(q.codes + 32 * g + 8 * j) =
+                uint2{mx8_pack4(f[0], f[1], f[2], f[3], E, amax),
+                      mx8_pack4(f[4], f[5], f[6], f[7], E, amax)};
+            if (j == 0)
+                q.scales[g] = (uint8_t)(E + 127);
+        }
+    }
 }
 
 __device__ __forceinline__ float swiglu_clamped(float g, float u, float gl, float ul)
@@ -250,11 +297,18 @@ __device__ __forceinline__ void combine_cols(const Shape &s, const float *__rest
 // ---------------------------------------------------------------------------
 size_t dispatch_scratch_bytes(const moe_shape &s);
 bool dispatch_is_single_block(const moe_shape &s);
-// zero[0 .. nzero) is cleared by the dispatch launch (one workgroup paths only)
+// zero[0 .. nzero) is cleared by the dispatch launch (one workgroup paths
+// only).  With a quant job the activation quant runs first: in the same
+// launch as a one-workgroup dispatch (extra workgroups), else as its own
+// launch before the dispatch.
 hipError_t launch_dispatch(const moe_shape &s, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
                            int32_t *status, void *scratch, hipStream_t st,
-                           int32_t *zero = nullptr, int nzero = 0);
+                           int32_t *zero = nullptr, int nzero = 0,
+                           const QuantJob *quant = nullptr);
+// workgroups of `threads` threads that the quant job wants (at least one)
+int quant_blocks(const QuantJob &q, int threads);
+hipError_t launch_quant_mxfp8(const QuantJob &q, hipStream_t st);
 bool use_fused_decode(const moe_shape &s);
 int fused_sync_words(const moe_shape &s);
 hipError_t launch_fused_decode(const moe_shape &s, const uint8_t *x, const uint8_t *xs,

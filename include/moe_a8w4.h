@@ -104,7 +104,8 @@ int64_t moe_row_capacity(const moe_shape *shape);
 /* Device scratch bytes moe_dispatch needs (0 for small T). */
 size_t moe_dispatch_workspace_size(const moe_shape *shape);
 
-/* Device scratch bytes moe_forward needs (dispatch results, h, y). */
+/* Device scratch bytes moe_forward needs (dispatch results, h, y, and the
+ * MX FP8 activations of moe_forward_bf16). */
 size_t moe_workspace_size(const moe_shape *shape);
 
 /*
@@ -144,6 +145,21 @@ int moe_gemm1_swiglu(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t
 int moe_gemm2(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_scale,
               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
               const uint8_t *w2_scale, uint16_t *y_bf16, void *stream);
+
+/*
+ * Activation quant in front of the layer ("MegaMoEV2: fuse dispatch, GEMM1,
+ * GEMM2 and combine into one kernel", Summary: the large-input path runs it
+ * as its own kernel on the caller's stream): bf16 rows x_bf16[T, H] to e4m3
+ * codes x_fp8[T, H] and E8M0 exponents x_scale[T, H/32], one exponent per
+ * 32 consecutive values of a row, by the same 1x32 rule as the requant of h:
+ * exponent floor(log2(amax)) - 8 clamped to [-127, 127], values divided by
+ * 2^exponent, rounded to nearest even, saturated at +-448; a block whose
+ * amax is zero gets byte 127 and +0 codes.  Exact: the codes are a function
+ * of the bf16 bits only.  x_bf16 and x_fp8 16-byte aligned; T = 0 is a
+ * no-op.  Finite inputs (a NaN makes its block's codes unspecified).
+ */
+int moe_quant_mxfp8(const moe_shape *shape, const uint16_t *x_bf16, uint8_t *x_fp8,
+                    uint8_t *x_scale, void *stream);
 
 /*
  * Combine ("MegaMoEV2 ...": the combine skips invalid (-1) top-k slots;
@@ -187,6 +203,20 @@ int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const u
                            const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
                            uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * The layer from bf16 activations (the pages' small-input path fuses the
+ * quant with the layer, the large-input path runs it first on the same
+ * stream): moe_quant_mxfp8 of x_bf16 into the workspace, then moe_forward
+ * on those codes.  Where the dispatch runs as one workgroup (at most 8,192
+ * route slots) the quant shares its launch; otherwise it is a launch of its
+ * own.  The output bits equal moe_forward's on moe_quant_mxfp8's codes.
+ * Same workspace as moe_forward.
+ */
+int moe_forward_bf16(const moe_shape *shape, const uint16_t *x_bf16, const int32_t *topk_ids,
+                     const float *topk_w, const uint8_t *w13, const uint8_t *w13_scale,
+                     const uint8_t *w2, const uint8_t *w2_scale, uint16_t *out_bf16,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a return code. */
 const char *moe_strerror(int code);

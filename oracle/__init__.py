@@ -120,6 +120,22 @@ def mx8_quant_block(v: np.ndarray):
 
 # ---- dispatch ----------------------------------------------------------------
 
+def quant_mxfp8(x_bf16: np.ndarray):
+    """bf16 bit patterns uint16 [rows, H] -> (e4m3 codes uint8 [rows, H],
+    E8M0 exponents uint8 [rows, H/32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, H = x.shape
+    assert H % 32 == 0
+    codes = np.empty((rows, H), dtype=np.uint8)
+    scales = np.empty((rows, H // 32), dtype=np.uint8)
+    h = lib()
+    h.orc_quant_mxfp8.restype = None
+    h.orc_quant_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    h.orc_quant_mxfp8(_p(x), rows, H, _p(codes), _p(scales))
+    return codes, scales
+
+
 def row_capacity(spec) -> int:
     s = shape_of(spec)
     return int(lib().orc_row_capacity(ctypes.byref(s)))

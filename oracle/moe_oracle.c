@@ -163,6 +163,28 @@ ORC_EXPORT void orc_mx8_quant_block(const float *v, uint8_t *codes, uint8_t *sca
         codes[i] = orc_e4m3_encode(ldexp((double)v[i], -E));
 }
 
+/* bf16 activation rows to MX FP8, the step in front of the layer
+ * ("MegaMoEV2: fuse dispatch, GEMM1, GEMM2 and combine into one kernel",
+ * Summary: the quant runs before the dispatch, fused with the layer for
+ * small inputs, as a kernel of its own for large ones): each row's values
+ * decoded from bf16 exactly, then every 32 consecutive values through
+ * orc_mx8_quant_block, the same rule as the requant of the intermediate. */
+ORC_EXPORT void orc_quant_mxfp8(const uint16_t *x, int64_t rows, int32_t H, uint8_t *codes,
+                                uint8_t *scales)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < rows; ++t) {
+        float v[32];
+        int32_t b, i;
+        for (b = 0; b < H / 32; ++b) {
+            for (i = 0; i < 32; ++i)
+                v[i] = orc_bf16_decode(x[t * H + 32 * b + i]);
+            orc_mx8_quant_block(v, codes + t * H + 32 * b, scales + t * (H / 32) + b);
+        }
+    }
+}
+
 /* Clamped SwiGLU of one (gate, up) pair. */
 ORC_EXPORT float orc_swiglu(float g, float u, float gate_limit, float up_limit)
 {

@@ -184,7 +184,8 @@ def make_routing(spec: CaseSpec | str, seed: Optional[int] = None, **overrides):
 def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> dict:
     """Draw one case.  Returns a dict of numpy arrays plus the spec:
 
-    x_fp8     uint8 [T, H]          e4m3 codes
+    x_bf16    uint16 [T, H]         the bf16 activation rows (bit patterns)
+    x_fp8     uint8 [T, H]          e4m3 codes of x_bf16
     x_scale   uint8 [T, H/32]       E8M0 exponents (bias 127)
     topk_ids  int32 [T, K]          global expert ids, -1 = no expert
     topk_w    float32 [T, K]        routing weights (pad slots keep theirs)
@@ -213,6 +214,7 @@ def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> 
 
     xf = _bf16_round(rng.standard_normal((T, H), dtype=np.float32))
     x_fp8, x_scale = _quant_x(xf)
+    x_bf16 = (xf.view(np.uint32) >> 16).astype(np.uint16)
     del xf
 
     def codes(n):
@@ -222,7 +224,7 @@ def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> 
     w13_scale = rng.integers(121, 125, size=(EL, 2 * I, H // 32), dtype=np.uint8)
     w2 = codes(EL * H * (I // 2)).reshape(EL, H, I // 2)
     w2_scale = rng.integers(121, 125, size=(EL, H, I // 32), dtype=np.uint8)
-    return dict(spec=spec, x_fp8=x_fp8, x_scale=x_scale, topk_ids=ids, topk_w=w,
+    return dict(spec=spec, x_bf16=x_bf16, x_fp8=x_fp8, x_scale=x_scale, topk_ids=ids, topk_w=w,
                 w13=w13, w13_scale=w13_scale, w2=w2, w2_scale=w2_scale)
 
 
@@ -250,3 +252,61 @@ def algorithmic_work(case: dict) -> dict:
     wbytes = c["touched"] * (H * I + H * I // 16 + H * I // 2 + H * I // 32)
     bytes_ = wbytes + c["tokens_with_route"] * (H + H // 32) + T * 8 * K + T * 2 * H
     return dict(flop=6 * H * I * c["routes"], weight_bytes=wbytes, bytes=bytes_, **c)
+
+
+def _bf16_bits(v) -> np.ndarray:
+    """bf16 bit patterns of float32 values (the low 16 bits dropped)."""
+    f = np.asarray(v, dtype=np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def quant_edge_rows(H: int = 512, seed: int = 7) -> np.ndarray:
+    """bf16 rows [64, H] covering the rule's corners: zero blocks of +0 and
+    -0, lone nonzero values among -0, the largest and the subnormal bf16
+    values, amax mantissas that saturate, e4m3 rounding midpoints, then
+    random finite bit patterns over the whole exponent range."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = np.zeros((64, H), dtype=np.uint16)
+    x[1, :] = 0x8000                                   # all -0
+    x[2, :] = rng.choice(np.array([0x0000, 0x8000], dtype=np.uint16), size=H)
+    x[3, :] = 0x8000
+    x[3, ::32] = _bf16_bits(1.5)                       # one value per block
+    big = rng.choice(np.array([0x7F7F, 0xFF7F, 0x3F80, 0x0001], dtype=np.uint16), size=H)
+    x[4, :] = big
+    x[5, :] = rng.integers(0x0001, 0x0080, size=H, dtype=np.uint16)  # subnormals
+    x[5, 1::2] |= 0x8000
+    sat = np.array([1.75, 1.875, 1.9921875, -1.75], dtype=np.float32)
+    for b in range(H // 32):
+        blk = slice(32 * b, 32 * b + 32)
+        x[6, blk] = _bf16_bits(rng.standard_normal(32) * 0.25 * 2.0 ** (b - 8))
+        x[6, 32 * b] = _bf16_bits(sat[b % 4] * 2.0 ** (b - 8))
+    # E = 0 blocks (amax 256): values on e4m3 midpoints of every binade
+    mids = np.array([1.0625, 1.1875, 2.125, 2.375, 0.001953125 / 2, 3 * 0.001953125 / 2,
+                     5 * 0.001953125 / 2, 0.015625 * 1.0625, 208.0, 240.0, 448.0, 464.0],
+                    dtype=np.float32)
+    row = rng.choice(np.concatenate([mids, -mids]), size=H).astype(np.float32)
+    row[::32] = 256.0
+    x[7, :] = _bf16_bits(row)
+    r = rng.integers(0, 1 << 16, size=(56, H), dtype=np.uint16)
+    finite = (r & 0x7F80) != 0x7F80
+    x[8:] = np.where(finite, r, r & 0xBFFF)          # clear an exponent bit of inf / NaN
+    return x
+
+
+def quant_exhaustive_rows(H: int = 512) -> np.ndarray:
+    """Every bf16 value of magnitude below 2^9, both signs (codes 0x0000 to
+    0x43FF and their negatives), 31 to a 32-value block whose first value is
+    256: the block exponent is then 0, so each value meets the e4m3 rounding
+    unscaled (normal, subnormal, underflow and the saturating [448, 512)).
+    Zero-padded to whole rows of H values."""
+    mags = np.arange(0, 0x4400, dtype=np.uint16)
+    vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+    nb = -(-vals.size // 31)
+    per_row = H // 32
+    nb = -(-nb // per_row) * per_row
+    blocks = np.zeros((nb, 32), dtype=np.uint16)
+    blocks[:, 0] = 0x4380                      # 256.0
+    flat = np.zeros(nb * 31, dtype=np.uint16)
+    flat[:vals.size] = vals
+    blocks[:, 1:] = flat.reshape(nb, 31)
+    return blocks.reshape(-1, H)

@@ -98,3 +98,26 @@ def test_refusals_return_before_any_launch(lib):
     assert lib.moe_forward(ctypes.byref(z), *([null] * 10), 0, null) == 0
     assert lib.moe_combine(ctypes.byref(z), *([null] * 4), null) == 0
     assert moe.moe_strerror(-3).startswith("workspace")
+
+
+def test_quant_and_bf16_forward_refusals(lib):
+    c = moe.MoeShape(**V4).c()
+    bad = moe.MoeShape(**{**V4, "K": 0}).c()
+    z = moe.MoeShape(**{**V4, "T": 0}).c()
+    null = None
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 4)
+    assert lib.moe_quant_mxfp8(ctypes.byref(bad), fake, fake, fake, null) == -1
+    assert lib.moe_quant_mxfp8(ctypes.byref(c), null, fake, fake, null) == -1
+    assert lib.moe_quant_mxfp8(ctypes.byref(c), fake, null, fake, null) == -1
+    assert lib.moe_quant_mxfp8(ctypes.byref(c), odd, fake, fake, null) == -1
+    assert lib.moe_quant_mxfp8(ctypes.byref(c), fake, odd, fake, null) == -1
+    assert lib.moe_quant_mxfp8(ctypes.byref(z), null, null, null, null) == 0
+    assert lib.moe_forward_bf16(ctypes.byref(bad), *([fake] * 8), fake, 1 << 40, null) == -1
+    assert lib.moe_forward_bf16(ctypes.byref(c), *([null] * 8), null, 0, null) == -1
+    assert lib.moe_forward_bf16(ctypes.byref(c), odd, *([fake] * 7), fake, 1 << 40, null) == -1
+    assert lib.moe_forward_bf16(ctypes.byref(c), *([fake] * 8), fake, 16, null) == -3
+    assert lib.moe_forward_bf16(ctypes.byref(z), *([null] * 8), null, 0, null) == 0
+    # the workspace carries the MX FP8 activations of the bf16 entry point
+    s = moe.MoeShape(**V4)
+    assert moe.moe_workspace_size(s) >= 128 * 6 * (3072 + 96 + 2 * 7168) + 128 * (7168 + 224)

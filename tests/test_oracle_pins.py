@@ -153,6 +153,45 @@ def test_mx8_block_scale_rule_and_dense_requant():
     assert oracle.e4m3_decode(max(codes)) == 448.0
 
 
+def test_quant_mxfp8_against_numpy_exponent_and_torch_cast():
+    """The bf16 -> MX FP8 activation quant against an independent
+    quantiser: numpy's frexp for the block exponent and torch's own
+    float8_e4m3fn cast (round to nearest even) after clipping at +-448 (the
+    generator's x quantiser), on the edge rows (zero blocks of +0 and -0,
+    the largest and subnormal bf16 values, saturating amax mantissas, e4m3
+    rounding midpoints, random bit patterns over every exponent) and on
+    random rows; the float64 requantiser agrees on the dequantised values.
+    A block whose amax is zero must give exponent byte 127 and +0 codes."""
+    rows = [synth.quant_edge_rows(512, 7), synth.quant_edge_rows(256, 8),
+            synth.quant_exhaustive_rows(512)]
+    rng = np.random.default_rng(12)
+    rows.append((rng.integers(0, 1 << 16, size=(32, 1024), dtype=np.uint16) & 0xBFFF)
+                .astype(np.uint16))
+    for x in rows:
+        codes, scales = oracle.quant_mxfp8(x)
+        xf = oracle.bf16_to_f32(x).astype(np.float32)
+        T, H = x.shape
+        tc, ts = synth._quant_x(xf)
+        blk_zero = np.abs(xf.reshape(T, H // 32, 32)).max(axis=2) == 0
+        np.testing.assert_array_equal(scales, ts)
+        nz = np.repeat(~blk_zero, 32, axis=1)
+        np.testing.assert_array_equal(codes[nz], tc[nz])
+        assert (codes[~nz] == 0).all() and (scales[blk_zero] == 127).all()
+        # dequantised values equal the independent float64 requantiser
+        E = scales.astype(np.float64) - 127
+        deq = np.array([oracle.e4m3_decode(c) for c in range(256)])[codes] * \
+            np.repeat(np.exp2(E), 32, axis=1)
+        ref = q8_rows(xf.astype(np.float64))
+        np.testing.assert_array_equal(deq[nz], ref[nz])
+    # the edge rows reach every corner they are meant to reach
+    x = synth.quant_edge_rows(512, 7)
+    codes, scales = oracle.quant_mxfp8(x)
+    assert (codes[1] == 0).all() and (codes[2] == 0).all()           # zero blocks: +0
+    assert (codes[3, 1::32] == 0x80).all()                          # -0 in a live block
+    assert ((codes[6, ::32] & 0x7F) == 0x7E).all()                  # amax at / past 448
+    assert (scales[5] == 0).all()                                   # subnormal blocks
+
+
 # -------------------------------------------------------------- dispatch ----
 
 def _brute_dispatch(spec, ids):
