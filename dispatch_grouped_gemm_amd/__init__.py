@@ -38,7 +38,7 @@ library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
             "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
-            "moe_forward_bf16", "moe_strerror"]
+            "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -53,6 +53,15 @@ class _CShape(ctypes.Structure):
                 ("expert_begin", ctypes.c_int32), ("E_local", ctypes.c_int32),
                 ("dispatch_mode", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("gate_limit", ctypes.c_float), ("up_limit", ctypes.c_float)]
+
+
+class _CForwardArgs(ctypes.Structure):
+    _fields_ = [("x_fp8", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("x_bf16", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p),
+                ("topk_w", ctypes.c_void_p), ("w13", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("out_bf16", ctypes.c_void_p),
+                ("num_valid_tokens", ctypes.c_void_p), ("persistent", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -120,6 +129,10 @@ def lib() -> ctypes.CDLL:
         h.moe_quant_mxfp8.restype = ctypes.c_int
         h.moe_forward_bf16.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         h.moe_forward_bf16.restype = ctypes.c_int
+        h.moe_dispatch_valid.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        h.moe_dispatch_valid.restype = ctypes.c_int
+        h.moe_forward_ex.argtypes = [S, ctypes.POINTER(_CForwardArgs), P, ctypes.c_size_t, P]
+        h.moe_forward_ex.restype = ctypes.c_int
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -230,7 +243,10 @@ def alloc_workspace(shape: MoeShape, device) -> torch.Tensor:
     return torch.empty(max(moe_workspace_size(shape), 1), dtype=torch.uint8, device=device)
 
 
-def moe_dispatch(shape: MoeShape, topk_ids, d: DispatchBuffers, stream=None):
+def moe_dispatch(shape: MoeShape, topk_ids, d: DispatchBuffers, stream=None,
+                 num_valid_tokens=None):
+    """Dispatch; num_valid_tokens (int32 tensor [1] on the device) calls
+    moe_dispatch_valid: rows past the count are padding."""
     dev = topk_ids.device
     T, K, E = shape.T, shape.K, shape.E_local
     R = max(moe_row_capacity(shape), 1)
@@ -246,8 +262,13 @@ def moe_dispatch(shape: MoeShape, topk_ids, d: DispatchBuffers, stream=None):
         ws_ptr = _ptr(d.workspace, "workspace", None, {torch.uint8}, dev)
         ws_n = d.workspace.numel()
     c = shape.c()
-    _check(lib().moe_dispatch(ctypes.byref(c), *args, ws_ptr, ws_n, _stream(stream, dev)),
-           "moe_dispatch")
+    if num_valid_tokens is None:
+        _check(lib().moe_dispatch(ctypes.byref(c), *args, ws_ptr, ws_n, _stream(stream, dev)),
+               "moe_dispatch")
+        return
+    nv = _ptr(num_valid_tokens, "num_valid_tokens", (1,), i32, dev)
+    _check(lib().moe_dispatch_valid(ctypes.byref(c), args[0], nv, *args[1:], ws_ptr, ws_n,
+                                    _stream(stream, dev)), "moe_dispatch_valid")
 
 
 def moe_gemm1_swiglu(shape: MoeShape, x_fp8, x_scale, d: DispatchBuffers, w13, w13_scale,
@@ -353,6 +374,37 @@ def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scal
     fn, name = ((lib().moe_forward_persistent, "moe_forward_persistent") if persistent
                 else (lib().moe_forward, "moe_forward"))
     _check(fn(ctypes.byref(c), *args, ws, workspace.numel(), _stream(stream, dev)), name)
+
+
+def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out_bf16,
+                   workspace, x_fp8=None, x_scale=None, x_bf16=None, num_valid_tokens=None,
+                   persistent=False, stream=None):
+    """The layer with every option (one of x_fp8 + x_scale or x_bf16;
+    num_valid_tokens an int32 tensor [1] on the device)."""
+    dev = topk_ids.device
+    T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    a = _CForwardArgs()
+    if x_bf16 is not None:
+        a.x_bf16 = _ptr(x_bf16, "x_bf16", (T, H), bf, dev)
+    if x_fp8 is not None or x_scale is not None:
+        a.x_fp8 = _ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev)
+        a.x_scale = _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev)
+    a.topk_ids = _ptr(topk_ids, "topk_ids", (T, K), {torch.int32}, dev)
+    a.topk_w = _ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev)
+    a.w13 = _ptr(w13, "w13", (E, 2 * I, H // 2), _fp4(), dev)
+    a.w13_scale = _ptr(w13_scale, "w13_scale", (E, 2 * I, H // 32), _e8m0("w13_scale"), dev)
+    a.w2 = _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev)
+    a.w2_scale = _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev)
+    a.out_bf16 = _ptr(out_bf16, "out_bf16", (T, H), bf, dev)
+    if num_valid_tokens is not None:
+        a.num_valid_tokens = _ptr(num_valid_tokens, "num_valid_tokens", (1,), {torch.int32},
+                                  dev)
+    a.persistent = 1 if persistent else 0
+    ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
+    c = shape.c()
+    _check(lib().moe_forward_ex(ctypes.byref(c), ctypes.byref(a), ws, workspace.numel(),
+                                _stream(stream, dev)), "moe_forward_ex")
 
 
 def moe_forward_persistent(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale,

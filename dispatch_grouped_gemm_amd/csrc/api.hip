@@ -122,9 +122,10 @@ size_t moe_workspace_size(const moe_shape *s)
     return layout_of(*s).total;
 }
 
-int moe_dispatch(const moe_shape *s, const int32_t *ids, int32_t *counts, int32_t *offsets,
-                 int32_t *row_route, int32_t *route_row, int32_t *status, void *ws,
-                 size_t ws_bytes, void *stream)
+static int dispatch_impl(const moe_shape *s, const int32_t *ids, const int32_t *valid,
+                         int32_t *counts, int32_t *offsets, int32_t *row_route,
+                         int32_t *route_row, int32_t *status, void *ws, size_t ws_bytes,
+                         void *stream)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
@@ -137,7 +138,25 @@ int moe_dispatch(const moe_shape *s, const int32_t *ids, int32_t *counts, int32_
     if (need && (!ws || ws_bytes < need))
         return MOE_EWORKSPACE;
     return hip_status(moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
-                                           ws, as_stream(stream)));
+                                           ws, as_stream(stream), nullptr, 0, nullptr, valid));
+}
+
+int moe_dispatch(const moe_shape *s, const int32_t *ids, int32_t *counts, int32_t *offsets,
+                 int32_t *row_route, int32_t *route_row, int32_t *status, void *ws,
+                 size_t ws_bytes, void *stream)
+{
+    return dispatch_impl(s, ids, nullptr, counts, offsets, row_route, route_row, status, ws,
+                         ws_bytes, stream);
+}
+
+int moe_dispatch_valid(const moe_shape *s, const int32_t *ids, const int32_t *num_valid_tokens,
+                       int32_t *counts, int32_t *offsets, int32_t *row_route, int32_t *route_row,
+                       int32_t *status, void *ws, size_t ws_bytes, void *stream)
+{
+    if (s && s->T > 0 && !num_valid_tokens)
+        return moe_check_shape(s) != MOE_OK ? moe_check_shape(s) : MOE_EINVAL;
+    return dispatch_impl(s, ids, num_valid_tokens, counts, offsets, row_route, route_row, status,
+                         ws, ws_bytes, stream);
 }
 
 int moe_gemm1_swiglu(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
@@ -216,7 +235,8 @@ namespace {
 int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
                  const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                  const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
-                 bool persistent, const uint16_t *x_bf16 = nullptr)
+                 bool persistent, const uint16_t *x_bf16 = nullptr,
+                 const int32_t *valid = nullptr)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
@@ -260,14 +280,14 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
         int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
         hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row,
                                             status, scratch, st, sync,
-                                            moe::fused_sync_words(*s), qj);
+                                            moe::fused_sync_words(*s), qj, valid);
         if (e == hipSuccess)
             e = moe::launch_fused_decode(*s, x, xs, counts, offsets, row_route, route_row, tw,
                                          w13, w13s, w2, w2s, h, hs, y, out, sync, st);
         return hip_status(e);
     }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
-                                        scratch, st, nullptr, 0, qj);
+                                        scratch, st, nullptr, 0, qj, valid);
     if (persistent) {
         int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
         if (e == hipSuccess)
@@ -311,6 +331,23 @@ int moe_forward_bf16(const moe_shape *s, const uint16_t *x_bf16, const int32_t *
         return moe_check_shape(s) != MOE_OK ? moe_check_shape(s) : MOE_EINVAL;
     return forward_impl(s, nullptr, nullptr, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes,
                         stream, false, x_bf16);
+}
+
+int moe_forward_ex(const moe_shape *s, const moe_forward_args *a, void *ws, size_t ws_bytes,
+                   void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (!a)
+        return MOE_EINVAL;
+    // exactly one activation form
+    const bool fp8 = a->x_fp8 || a->x_scale, bf16 = a->x_bf16 != nullptr;
+    if (fp8 == bf16)
+        return s->T == 0 ? MOE_OK : MOE_EINVAL;
+    return forward_impl(s, a->x_fp8, a->x_scale, a->topk_ids, a->topk_w, a->w13, a->w13_scale,
+                        a->w2, a->w2_scale, a->out_bf16, ws, ws_bytes, stream, a->persistent != 0,
+                        a->x_bf16, a->num_valid_tokens);
 }
 
 const char *moe_strerror(int code)

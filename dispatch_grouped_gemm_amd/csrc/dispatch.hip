@@ -64,17 +64,32 @@ __device__ __forceinline__ int wave_sum(int v)
 // rather than once per 64.
 constexpr int kBatch = 8;
 
-// Local expert (route_local) of the slots base + 64 p + lane, p < P; -1 past e.
+// Slots of the tokens the call counts: rows t >= *valid are padding (their
+// slots read as -1, no expert), the count clamped to [0, T]; all T rows when
+// valid is null.  Read on the device, so a replayed graph follows the count
+// the caller wrote for that replay ("feat(moe): route before the rows move;
+// per-pass real row counts", Per-pass real row counts).
+__device__ __forceinline__ long valid_slots(const Shape &s, const int32_t *valid)
+{
+    if (!valid)
+        return (long)s.T * s.K;
+    const int v = *valid;
+    return (long)(v < 0 ? 0 : (v > s.T ? s.T : v)) * s.K;
+}
+
+// Local expert (route_local) of the slots base + 64 p + lane, p < P; -1 past
+// e and past the valid slots nv.
 template <int P>
 __device__ __forceinline__ void load_keys(const Shape &s, const int32_t *__restrict__ ids,
-                                          long base, long e, int (&ex)[P])
+                                          long base, long e, long nv, int (&ex)[P])
 {
     const int lane = threadIdx.x & 63;
+    const long lim = e < nv ? e : nv;
     int raw[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const long r = base + 64 * p + lane;
-        raw[p] = r < e ? ids[r] : -1;
+        raw[p] = r < lim ? ids[r] : -1;
     }
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -85,12 +100,12 @@ __device__ __forceinline__ void load_keys(const Shape &s, const int32_t *__restr
 // the wavefront's count of invalid ids (in every lane).
 template <int P>
 __device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
-                              int *hist_row)
+                              long nv, int *hist_row)
 {
     int invalid = 0;
     for (long base = b; base < e; base += 64 * P) {
         int ex[P];
-        load_keys<P>(s, ids, base, e, ex);
+        load_keys<P>(s, ids, base, e, nv, ex);
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             if (base + 64 * p >= e)
@@ -108,13 +123,13 @@ __device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, l
 // own row) is the next row of expert ex for this wavefront.
 template <int P>
 __device__ void wave_scatter(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
-                             int *base_row, int32_t *__restrict__ row_route,
+                             long nv, int *base_row, int32_t *__restrict__ row_route,
                              int32_t *__restrict__ route_row)
 {
     const int lane = threadIdx.x & 63;
     for (long base = b; base < e; base += 64 * P) {
         int ex[P];
-        load_keys<P>(s, ids, base, e, ex);
+        load_keys<P>(s, ids, base, e, nv, ex);
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             if (base + 64 * p >= e)
@@ -172,7 +187,8 @@ __global__ void __launch_bounds__(kThreads)
 compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                      int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
                      int32_t *__restrict__ route_row, int32_t *__restrict__ status,
-                     int32_t *__restrict__ zero, int nzero, QuantJob quant)
+                     int32_t *__restrict__ zero, int nzero, QuantJob quant,
+                     const int32_t *__restrict__ valid)
 {
     // workgroups past the first quantise the activation rows
     if (blockIdx.x > 0) {
@@ -182,6 +198,7 @@ compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restri
     }
     for (int i = threadIdx.x; i < nzero; i += kThreads)
         zero[i] = 0;
+    const long nv = valid_slots(s, valid);
     extern __shared__ int hist[]; // [kWaves][E_local]
     __shared__ int invalid_total;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -195,7 +212,7 @@ compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restri
     if (tid == 0)
         invalid_total = 0;
     __syncthreads();
-    const int inv = wave_histogram<kBatch>(s, ids, b, e, hist + wave * E);
+    const int inv = wave_histogram<kBatch>(s, ids, b, e, nv, hist + wave * E);
     if (lane == 0 && inv)
         atomicAdd(&invalid_total, inv);
     __syncthreads();
@@ -223,15 +240,17 @@ compact_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restri
         status[1] = status[2] = status[3] = 0;
     }
     __syncthreads();
-    wave_scatter<kBatch>(s, ids, b, e, hist + wave * E, row_route, route_row);
+    wave_scatter<kBatch>(s, ids, b, e, nv, hist + wave * E, row_route, route_row);
 }
 
 // ---- compact, many workgroups ------------------------------------------------
 
 // Pass 1: per-workgroup histograms; scratch[blk][E] holds the invalid count.
 __global__ void __launch_bounds__(kThreads)
-compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ scratch)
+compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ scratch,
+                    const int32_t *__restrict__ valid)
 {
+    const long nv = valid_slots(s, valid);
     extern __shared__ int hist[]; // [E_local]
     __shared__ int invalid_total;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -248,7 +267,7 @@ compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restric
     int inv = 0;
     for (long base = b; base < e; base += 64 * kLargeBatch) {
         int ex[kLargeBatch];
-        load_keys<kLargeBatch>(s, ids, base, e, ex);
+        load_keys<kLargeBatch>(s, ids, base, e, nv, ex);
 #pragma unroll
         for (int p = 0; p < kLargeBatch; ++p) {
             const Match m = wave_match(ex[p], ex[p] >= 0);
@@ -324,8 +343,10 @@ compact_scan_kernel(Shape s, int nblk, int32_t *__restrict__ scratch, int32_t *_
 // Pass 3: stable scatter of each workgroup's slots from its first rows.
 __global__ void __launch_bounds__(kThreads)
 compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *__restrict__ scratch,
-                       int32_t *__restrict__ row_route, int32_t *__restrict__ route_row)
+                       int32_t *__restrict__ row_route, int32_t *__restrict__ route_row,
+                       const int32_t *__restrict__ valid)
 {
+    const long nv = valid_slots(s, valid);
     extern __shared__ int hist[]; // [kWaves][E_local]
     const int tid = threadIdx.x, wave = tid >> 6;
     const int E = s.E_local;
@@ -335,7 +356,7 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
     __syncthreads();
     const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
     const long e = min(n, b + kSlotsPerWaveLarge);
-    (void)wave_histogram<kLargeBatch>(s, ids, b, e, hist + wave * E);
+    (void)wave_histogram<kLargeBatch>(s, ids, b, e, nv, hist + wave * E);
     __syncthreads();
     if (tid < E) {
         int run = scratch[(size_t)blockIdx.x * (E + 1) + tid];
@@ -346,7 +367,7 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
         }
     }
     __syncthreads();
-    wave_scatter<kLargeBatch>(s, ids, b, e, hist + wave * E, row_route, route_row);
+    wave_scatter<kLargeBatch>(s, ids, b, e, nv, hist + wave * E, row_route, route_row);
 }
 
 // ---- fixed-slot ----------------------------------------------------------------
@@ -355,13 +376,13 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
 // group's size to the expert's counter and hands out consecutive slots.
 template <int P>
 __device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
-                            int32_t *cnt, int32_t *__restrict__ row_route,
+                            long nv, int32_t *cnt, int32_t *__restrict__ row_route,
                             int32_t *__restrict__ route_row, int &invalid, int &dropped)
 {
     const int lane = threadIdx.x & 63;
     for (long base = b; base < e; base += 64 * P) {
         int exs[P];
-        load_keys<P>(s, ids, base, e, exs);
+        load_keys<P>(s, ids, base, e, nv, exs);
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             if (base + 64 * p >= e)
@@ -396,7 +417,8 @@ __global__ void __launch_bounds__(kThreads)
 fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                    int32_t *__restrict__ offsets, int32_t *__restrict__ row_route,
                    int32_t *__restrict__ route_row, int32_t *__restrict__ status,
-                   int32_t *__restrict__ zero, int nzero, QuantJob quant)
+                   int32_t *__restrict__ zero, int nzero, QuantJob quant,
+                   const int32_t *__restrict__ valid)
 {
     // workgroups past the first quantise the activation rows
     if (blockIdx.x > 0) {
@@ -419,7 +441,8 @@ fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
     const long per_wave = (n + kWaves - 1) / kWaves;
     const long b = min(n, per_wave * wave), e = min(n, b + per_wave);
     int invalid = 0, dropped = 0;
-    claim_slots<kBatch>(s, ids, b, e, cnt, row_route, route_row, invalid, dropped);
+    claim_slots<kBatch>(s, ids, b, e, valid_slots(s, valid), cnt, row_route, route_row, invalid,
+                        dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
@@ -457,14 +480,15 @@ fixed_reset_kernel(Shape s, int32_t *__restrict__ counts, int32_t *__restrict__ 
 __global__ void __launch_bounds__(kThreads)
 fixed_claim_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
                    int32_t *__restrict__ row_route, int32_t *__restrict__ route_row,
-                   int32_t *__restrict__ status)
+                   int32_t *__restrict__ status, const int32_t *__restrict__ valid)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long n = (long)s.T * s.K;
     const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
     const long e = min(n, b + kSlotsPerWaveLarge);
     int invalid = 0, dropped = 0;
-    claim_slots<kLargeBatch>(s, ids, b, e, counts, row_route, route_row, invalid, dropped);
+    claim_slots<kLargeBatch>(s, ids, b, e, valid_slots(s, valid), counts, row_route, route_row,
+                             invalid, dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
@@ -498,7 +522,7 @@ size_t dispatch_scratch_bytes(const moe_shape &s)
 hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
                            int32_t *status, void *scratch, hipStream_t st, int32_t *zero,
-                           int nzero, const QuantJob *quant)
+                           int nzero, const QuantJob *quant, const int32_t *valid)
 {
     if (nzero > 0 && !dispatch_is_single_block(sh))
         return hipErrorInvalidValue;
@@ -515,12 +539,12 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
     if (sh.dispatch_mode == MOE_DISPATCH_COMPACT) {
         if (compact_is_small(sh)) {
             compact_small_kernel<<<grid, kThreads, kWaves * E * sizeof(int), st>>>(
-                s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj);
+                s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj, valid);
             return hipGetLastError();
         }
         const int nblk = large_blocks(sh);
         int32_t *blk = static_cast<int32_t *>(scratch);
-        compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk);
+        compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk, valid);
         const size_t table = (size_t)nblk * (E + 1) * sizeof(int);
         if (table <= 128 * 1024)
             compact_scan_kernel<true><<<1, kThreads, table, st>>>(s, nblk, blk, counts, offsets,
@@ -529,17 +553,17 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
             compact_scan_kernel<false><<<1, kThreads, 0, st>>>(s, nblk, blk, counts, offsets,
                                                                 status);
         compact_scatter_kernel<<<nblk, kThreads, kWaves * E * sizeof(int), st>>>(
-            s, ids, blk, row_route, route_row);
+            s, ids, blk, row_route, route_row, valid);
         return hipGetLastError();
     }
     if (num_slots(sh) <= kSmallSlots) {
         fixed_small_kernel<<<grid, kThreads, E * sizeof(int), st>>>(
-            s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj);
+            s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj, valid);
         return hipGetLastError();
     }
     fixed_reset_kernel<<<(int)((E + 256) / 256), 256, 0, st>>>(s, counts, offsets, status);
     fixed_claim_kernel<<<large_blocks(sh), kThreads, 0, st>>>(s, ids, counts, row_route, route_row,
-                                                              status);
+                                                              status, valid);
     return hipGetLastError();
 }
 

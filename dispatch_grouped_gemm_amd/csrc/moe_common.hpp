@@ -164,11 +164,14 @@ __device__ __forceinline__ void quant_mx8_part(const QuantJob &q, long tid, long
     }
 }
 
+// Clamped SwiGLU: min(g, gl) * sigmoid(min(g, gl)) * clamp(u, -ul, ul), the
+// logistic from the hardware exp and reciprocal (v_exp_f32, v_rcp_f32: a
+// few float32 ulps; the value is requantised to 3 mantissa bits next).
 __device__ __forceinline__ float swiglu_clamped(float g, float u, float gl, float ul)
 {
     const float gc = fminf(g, gl);
     const float uc = fminf(fmaxf(u, -ul), ul);
-    return gc / (1.0f + expf(-gc)) * uc;
+    return gc * __builtin_amdgcn_rcpf(1.0f + __expf(-gc)) * uc;
 }
 
 // ---------------------------------------------------------------------------
@@ -300,12 +303,13 @@ bool dispatch_is_single_block(const moe_shape &s);
 // zero[0 .. nzero) is cleared by the dispatch launch (one workgroup paths
 // only).  With a quant job the activation quant runs first: in the same
 // launch as a one-workgroup dispatch (extra workgroups), else as its own
-// launch before the dispatch.
+// launch before the dispatch.  valid (device int32, may be null) is the
+// count of real tokens: rows past it are padding, routed nowhere.
 hipError_t launch_dispatch(const moe_shape &s, const int32_t *ids, int32_t *counts,
                            int32_t *offsets, int32_t *row_route, int32_t *route_row,
                            int32_t *status, void *scratch, hipStream_t st,
                            int32_t *zero = nullptr, int nzero = 0,
-                           const QuantJob *quant = nullptr);
+                           const QuantJob *quant = nullptr, const int32_t *valid = nullptr);
 // workgroups of `threads` threads that the quant job wants (at least one)
 int quant_blocks(const QuantJob &q, int threads);
 hipError_t launch_quant_mxfp8(const QuantJob &q, hipStream_t st);

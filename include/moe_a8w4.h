@@ -121,6 +121,20 @@ int moe_dispatch(const moe_shape *shape, const int32_t *topk_ids, int32_t *count
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_dispatch for a padded batch: *num_valid_tokens (a device int32, read
+ * by the kernels, so a captured graph follows the value written before each
+ * replay) is the count of real tokens; rows t >= that count (clamped to
+ * [0, T]) are padding and every slot of theirs is treated as -1: no route,
+ * not counted as invalid, route_row = -1 ("feat(moe): route before the rows
+ * move; per-pass real row counts", Per-pass real row counts: the count
+ * reaches every routing kernel and replaces the pad-row mask).
+ */
+int moe_dispatch_valid(const moe_shape *shape, const int32_t *topk_ids,
+                       const int32_t *num_valid_tokens, int32_t *counts, int32_t *offsets,
+                       int32_t *row_route, int32_t *route_row, int32_t *status, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
  * GEMM1 + clamped SwiGLU + FP8 1x32 requantisation ("full-expert DeepSeek
  * V4.1 Flash MegaMoE tuning", Summary: W13, clamp-10 SwiGLU, FP8
  * intermediate quantisation).  For every used row of every expert segment:
@@ -217,6 +231,32 @@ int moe_forward_bf16(const moe_shape *shape, const uint16_t *x_bf16, const int32
                      const float *topk_w, const uint8_t *w13, const uint8_t *w13_scale,
                      const uint8_t *w2, const uint8_t *w2_scale, uint16_t *out_bf16,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The layer with every option: MX FP8 activations (x_fp8 + x_scale) or bf16
+ * rows (x_bf16, quantised in the call as by moe_forward_bf16) -- exactly one
+ * of the two; num_valid_tokens (device int32, or NULL for all T rows) as in
+ * moe_dispatch_valid, so padding rows cost no expert work and get +0 output
+ * rows; persistent != 0 takes moe_forward_persistent's launch (same
+ * refusals).  Same workspace and result as moe_forward.
+ */
+typedef struct {
+    const uint8_t *x_fp8;             /* [T, H] e4m3, or NULL */
+    const uint8_t *x_scale;           /* [T, H/32] E8M0, or NULL */
+    const uint16_t *x_bf16;           /* [T, H] bf16, or NULL */
+    const int32_t *topk_ids;          /* [T, K] */
+    const float *topk_w;              /* [T, K] */
+    const uint8_t *w13;               /* [E_local, 2I, H/2] */
+    const uint8_t *w13_scale;         /* [E_local, 2I, H/32] */
+    const uint8_t *w2;                /* [E_local, H, I/2] */
+    const uint8_t *w2_scale;          /* [E_local, H, I/32] */
+    uint16_t *out_bf16;               /* [T, H] */
+    const int32_t *num_valid_tokens;  /* device int32, or NULL */
+    int32_t persistent;
+} moe_forward_args;
+
+int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /* Static description of a return code. */
 const char *moe_strerror(int code);

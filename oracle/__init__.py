@@ -141,8 +141,21 @@ def row_capacity(spec) -> int:
     return int(lib().orc_row_capacity(ctypes.byref(s)))
 
 
-def dispatch(spec, topk_ids: np.ndarray) -> dict:
+def pad_rows(topk_ids: np.ndarray, num_valid: int) -> np.ndarray:
+    """The per-pass real row count ("feat(moe): route before the rows move;
+    per-pass real row counts", Per-pass real row counts): rows at and past
+    num_valid (clamped to [0, T]) are padding, every slot of theirs -1."""
+    ids = np.array(topk_ids, dtype=np.int32, copy=True)
+    n = min(max(int(num_valid), 0), ids.shape[0])
+    ids[n:] = -1
+    return ids
+
+
+def dispatch(spec, topk_ids: np.ndarray, num_valid: Optional[int] = None) -> dict:
+    """Dispatch of the route slots; num_valid marks rows past it as padding."""
     s = shape_of(spec)
+    if num_valid is not None:
+        topk_ids = pad_rows(topk_ids, num_valid)
     ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     R = row_capacity(spec)
     counts = np.zeros(spec.E_local, np.int32)
@@ -197,8 +210,12 @@ def expert_ffn_gu(case: dict, t: int, e: int) -> np.ndarray:
     return gu
 
 
-def moe_layer(case: dict, tokens: Optional[np.ndarray] = None) -> np.ndarray:
-    """bf16 bits (uint16) of the layer output rows of ``tokens`` (all if None)."""
+def moe_layer(case: dict, tokens: Optional[np.ndarray] = None,
+              num_valid: Optional[int] = None) -> np.ndarray:
+    """bf16 bits (uint16) of the layer output rows of ``tokens`` (all if None);
+    num_valid marks rows past it as padding (no routes, +0 rows)."""
+    if num_valid is not None:
+        case = dict(case, topk_ids=pad_rows(case["topk_ids"], num_valid))
     spec = case["spec"]
     s = shape_of(spec)
     w13, w13s, w2, w2s = _weights(case)

@@ -10,6 +10,7 @@ import numpy as np
 import torch
 
 import dispatch_grouped_gemm_amd as moe
+import oracle
 import synth
 
 DEV = torch.device("cuda", 0)
@@ -249,3 +250,34 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
     if n_codes:
         assert n_flips <= max(4, max_flip_rate * n_codes), what + ": too many requant flips"
     return lit
+
+
+def check_dispatch(spec, ids: np.ndarray, d, num_valid=None):
+    """GPU dispatch buffers against the oracle: compact bit-exact, fixed-slot
+    as sets of routes per expert segment."""
+    ref = oracle.dispatch(spec, ids, num_valid=num_valid)
+    counts, offsets, status = host(d.counts), host(d.offsets), host(d.status)
+    np.testing.assert_array_equal(counts, ref["counts"])
+    np.testing.assert_array_equal(offsets, ref["offsets"])
+    np.testing.assert_array_equal(status, ref["status"])
+    rr = host(d.route_row)[:spec.T * spec.K]
+    row_route = host(d.row_route)
+    if spec.dispatch_mode == 0:
+        total = int(offsets[-1])
+        np.testing.assert_array_equal(row_route[:total], ref["row_route"][:total])
+        np.testing.assert_array_equal(rr, ref["route_row"])
+    else:
+        C = spec.capacity
+        for e in range(spec.E_local):
+            kept = min(int(counts[e]), C)
+            seg = row_route[e * C:e * C + kept]
+            refseg = ref["row_route"][e * C:e * C + kept]
+            if counts[e] <= C:
+                np.testing.assert_array_equal(np.sort(seg), np.sort(refseg))
+            else:
+                assert len(set(seg.tolist())) == kept
+            assert (row_route[e * C + kept:(e + 1) * C] == -1).all()  # untouched
+        kept_r = np.nonzero(rr >= 0)[0]
+        np.testing.assert_array_equal(row_route[rr[kept_r]], kept_r)
+        assert ((rr >= 0) == (ref["route_row"] >= 0)).all() or status[1] > 0
+    return ref

@@ -118,6 +118,23 @@ def test_quant_and_bf16_forward_refusals(lib):
     assert lib.moe_forward_bf16(ctypes.byref(c), odd, *([fake] * 7), fake, 1 << 40, null) == -1
     assert lib.moe_forward_bf16(ctypes.byref(c), *([fake] * 8), fake, 16, null) == -3
     assert lib.moe_forward_bf16(ctypes.byref(z), *([null] * 8), null, 0, null) == 0
+    # moe_dispatch_valid: the count pointer is required
+    assert lib.moe_dispatch_valid(ctypes.byref(c), fake, null, *([fake] * 5), null, 0,
+                                  null) == -1
+    assert lib.moe_dispatch_valid(ctypes.byref(bad), fake, fake, *([fake] * 5), null, 0,
+                                  null) == -1
+    # moe_forward_ex: exactly one activation form
+    args = moe._CForwardArgs()
+    for f in ("topk_ids", "topk_w", "w13", "w13_scale", "w2", "w2_scale", "out_bf16"):
+        setattr(args, f, 256)
+    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 1 << 40, null) == -1
+    args.x_fp8, args.x_scale, args.x_bf16 = 256, 256, 256
+    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 1 << 40, null) == -1
+    args.x_bf16 = None
+    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 16, null) == -3
+    assert lib.moe_forward_ex(ctypes.byref(c), None, fake, 1 << 40, null) == -1
+    args.persistent = 1
+    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 1 << 40, null) == -2
     # the workspace carries the MX FP8 activations of the bf16 entry point
     s = moe.MoeShape(**V4)
     assert moe.moe_workspace_size(s) >= 128 * 6 * (3072 + 96 + 2 * 7168) + 128 * (7168 + 224)

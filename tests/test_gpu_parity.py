@@ -20,43 +20,14 @@ import torch
 import dispatch_grouped_gemm_amd as moe
 import oracle
 import synth
-from gpu_util import (DEV, bf16_f64, bf16_ulp, cached_case, check_layer, dev, gemm1_mfma_bound,
-                      host, run_dispatch, run_forward, run_steps, say, sample_tokens, shape_of,
-                      upload)
+from gpu_util import (DEV, bf16_f64, bf16_ulp, cached_case, check_dispatch, check_layer, dev,
+                      gemm1_mfma_bound, host, run_dispatch, run_forward, run_steps, say,
+                      sample_tokens, shape_of, upload)
 
 pytestmark = pytest.mark.gpu
 
 ALL = list(synth.CONFIGS)
 BIG = [n for n in ALL if n != "tiny"]
-
-
-def check_dispatch(spec, ids: np.ndarray, d):
-    ref = oracle.dispatch(spec, ids)
-    counts, offsets, status = host(d.counts), host(d.offsets), host(d.status)
-    np.testing.assert_array_equal(counts, ref["counts"])
-    np.testing.assert_array_equal(offsets, ref["offsets"])
-    np.testing.assert_array_equal(status, ref["status"])
-    rr = host(d.route_row)[:spec.T * spec.K]
-    row_route = host(d.row_route)
-    if spec.dispatch_mode == 0:
-        total = int(offsets[-1])
-        np.testing.assert_array_equal(row_route[:total], ref["row_route"][:total])
-        np.testing.assert_array_equal(rr, ref["route_row"])
-    else:
-        C = spec.capacity
-        for e in range(spec.E_local):
-            kept = min(int(counts[e]), C)
-            seg = row_route[e * C:e * C + kept]
-            refseg = ref["row_route"][e * C:e * C + kept]
-            if counts[e] <= C:
-                np.testing.assert_array_equal(np.sort(seg), np.sort(refseg))
-            else:
-                assert len(set(seg.tolist())) == kept
-            assert (row_route[e * C + kept:(e + 1) * C] == -1).all()  # untouched
-        kept_r = np.nonzero(rr >= 0)[0]
-        np.testing.assert_array_equal(row_route[rr[kept_r]], kept_r)
-        assert ((rr >= 0) == (ref["route_row"] >= 0)).all() or status[1] > 0
-    return ref
 
 
 @pytest.mark.parametrize("name", ALL)

@@ -394,6 +394,35 @@ def test_duplicate_ids_are_independent_routes():
     assert oracle.dispatch(spec, ids)["counts"][3] >= spec.T
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_padding_rows_past_the_valid_count(mode):
+    """Rows past the real row count are padding: the dispatch equals the
+    dispatch of the first n rows alone (same counts, compact row order,
+    status), the rest of route_row is -1; the layer's first n rows are the
+    rows of the unpadded layer and the rest are +0."""
+    case = synth.make_case("tiny", T=24, dispatch_mode=mode, capacity=16 if mode else 0,
+                           seed=77)
+    spec = case["spec"]
+    ids = case["topk_ids"]
+    full = oracle.moe_layer(case)
+    for n in (0, 1, 9, 24, 30, -2):
+        m = min(max(n, 0), spec.T)
+        d = oracle.dispatch(spec, ids, num_valid=n)
+        head = spec.with_(T=m)
+        ref = oracle.dispatch(head, ids[:m])
+        np.testing.assert_array_equal(d["counts"], ref["counts"])
+        np.testing.assert_array_equal(d["offsets"], ref["offsets"])
+        np.testing.assert_array_equal(d["status"], ref["status"])
+        np.testing.assert_array_equal(d["route_row"][:m * spec.K], ref["route_row"])
+        assert (d["route_row"][m * spec.K:] == -1).all()
+        if mode == 0:
+            tot = int(ref["offsets"][-1])
+            np.testing.assert_array_equal(d["row_route"][:tot], ref["row_route"][:tot])
+        out = oracle.moe_layer(case, num_valid=n)
+        np.testing.assert_array_equal(out[:m], full[:m])
+        assert (out[m:] == 0).all()
+
+
 def test_generator_pad_count_and_determinism():
     a = synth.make_case("tiny")
     b = synth.make_case("tiny")
