@@ -110,9 +110,8 @@ __device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, l
         for (int p = 0; p < P; ++p) {
             if (base + 64 * p >= e)
                 break;
-            const Match m = wave_match(ex[p], ex[p] >= 0);
-            if (ex[p] >= 0 && m.rank == 0)
-                hist_row[ex[p]] += m.count; // one leader per expert: no two lanes collide
+            if (ex[p] >= 0)
+                atomicAdd(&hist_row[ex[p]], 1);
             invalid += ex[p] == -2;
         }
     }
@@ -270,9 +269,8 @@ compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restric
         load_keys<kLargeBatch>(s, ids, base, e, nv, ex);
 #pragma unroll
         for (int p = 0; p < kLargeBatch; ++p) {
-            const Match m = wave_match(ex[p], ex[p] >= 0);
-            if (ex[p] >= 0 && m.rank == 0)
-                atomicAdd(&hist[ex[p]], m.count);
+            if (ex[p] >= 0)
+                atomicAdd(&hist[ex[p]], 1);
             inv += ex[p] == -2;
         }
     }
@@ -372,9 +370,12 @@ compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *
 
 // ---- fixed-slot ----------------------------------------------------------------
 
-// Claim one slot per kept route: the leader of each expert group adds the
-// group's size to the expert's counter and hands out consecutive slots.
-template <int P>
+// Claim one slot per kept route.  kPerLane (counters in LDS): every lane
+// takes its own slot with an LDS atomic (the order of a segment is free in
+// fixed-slot mode).  Otherwise (counters in global memory) the leader of each
+// expert group adds the group's size to the expert's counter and hands out
+// consecutive slots, one global atomic per expert and wavefront.
+template <int P, bool kPerLane>
 __device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
                             long nv, int32_t *cnt, int32_t *__restrict__ row_route,
                             int32_t *__restrict__ route_row, int &invalid, int &dropped)
@@ -389,6 +390,23 @@ __device__ void claim_slots(const Shape &s, const int32_t *__restrict__ ids, lon
                 break;
             const long r = base + 64 * p + lane;
             const int ex = exs[p];
+            if (kPerLane) {
+                int row = -1;
+                if (ex >= 0) {
+                    const int slot = atomicAdd(&cnt[ex], 1);
+                    if (slot < s.capacity)
+                        row = ex * s.capacity + slot;
+                    else
+                        ++dropped;
+                }
+                invalid += ex == -2;
+                if (r < e) {
+                    route_row[r] = row;
+                    if (row >= 0)
+                        row_route[row] = (int32_t)r;
+                }
+                continue;
+            }
             const Match m = wave_match(ex, ex >= 0);
             int first = 0;
             if (ex >= 0 && m.rank == 0)
@@ -441,8 +459,8 @@ fixed_small_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
     const long per_wave = (n + kWaves - 1) / kWaves;
     const long b = min(n, per_wave * wave), e = min(n, b + per_wave);
     int invalid = 0, dropped = 0;
-    claim_slots<kBatch>(s, ids, b, e, valid_slots(s, valid), cnt, row_route, route_row, invalid,
-                        dropped);
+    claim_slots<kBatch, true>(s, ids, b, e, valid_slots(s, valid), cnt, row_route, route_row,
+                              invalid, dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
@@ -487,8 +505,8 @@ fixed_claim_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
     const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
     const long e = min(n, b + kSlotsPerWaveLarge);
     int invalid = 0, dropped = 0;
-    claim_slots<kLargeBatch>(s, ids, b, e, valid_slots(s, valid), counts, row_route, route_row,
-                             invalid, dropped);
+    claim_slots<kLargeBatch, false>(s, ids, b, e, valid_slots(s, valid), counts, row_route,
+                                    route_row, invalid, dropped);
     invalid = wave_sum(invalid);
     dropped = wave_sum(dropped);
     if (lane == 0) {
