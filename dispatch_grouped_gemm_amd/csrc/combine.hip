@@ -2,7 +2,8 @@
 // weights and summed in float32 in ascending k, rounded to bf16 once.  Slots whose
 // route_row is -1 (pad, foreign, invalid or dropped) contribute nothing, so
 // the result does not depend on their weights.  No atomics: a thread owns 8
-// output columns of one token, which makes the sum order fixed.
+// output columns of one token, which makes the sum order fixed; it loads the
+// token's slots, then all its kept routes' y pieces at once.
 #include "moe_common.hpp"
 
 namespace moe {
@@ -15,10 +16,14 @@ __global__ void __launch_bounds__(kThreads)
 combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict__ route_row,
                const uint16_t *__restrict__ y, uint16_t *__restrict__ out)
 {
-    const int per_token = (s.H + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
-    const int t = blockIdx.x / per_token;
-    const int col = ((blockIdx.x - t * per_token) * kThreads + threadIdx.x) * kCombineVec;
-    combine_cols(s, tw, route_row, y, out, t, col);
+    // one flat index over (token, 8-column piece): no idle threads at the
+    // end of a row
+    const int pieces = s.H / kCombineVec;
+    const long i = (long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (long)s.T * pieces)
+        return;
+    const int t = (int)(i / pieces);
+    combine_cols(s, tw, route_row, y, out, t, (int)(i - (long)t * pieces) * kCombineVec);
 }
 
 } // namespace
@@ -27,8 +32,8 @@ hipError_t launch_combine(const moe_shape &sh, const float *tw, const int32_t *r
                           const uint16_t *y, uint16_t *out, hipStream_t st)
 {
     const Shape s = to_dev(sh);
-    const int per_block = kThreads * kCombineVec;
-    const long grid = (long)((sh.H + per_block - 1) / per_block) * sh.T;
+    const long threads = (long)sh.T * (sh.H / kCombineVec);
+    const long grid = (threads + kThreads - 1) / kThreads;
     combine_kernel<<<(unsigned)grid, kThreads, 0, st>>>(s, tw, route_row, y, out);
     return hipGetLastError();
 }

@@ -264,28 +264,38 @@ __device__ __forceinline__ void combine_cols(const Shape &s, const float *__rest
 #pragma clang fp contract(off)
     if (col >= s.H)
         return;
+    // the token's slots first, then every kept route's 16 bytes of y, all in
+    // flight together; the sum itself runs in ascending k
+    constexpr int kMaxK = 8;
+    const size_t slot0 = (size_t)t * s.K;
+    int rows[kMaxK];
+    float w[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        rows[k] = k < s.K ? route_row[slot0 + k] : -1;
+        w[k] = k < s.K ? tw[slot0 + k] : 0.0f;
+    }
+    uint4 q[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+        if (rows[k] >= 0)
+            q[k] = *reinterpret_cast<const uint4 *>(y + (size_t)rows[k] * s.H + col);
     float acc[kCombineVec];
 #pragma unroll
     for (int i = 0; i < kCombineVec; ++i)
         acc[i] = 0.0f;
-    const size_t slot0 = (size_t)t * s.K;
-    for (int k = 0; k < s.K; ++k) {
-        const int row = route_row[slot0 + k];
-        if (row < 0)
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (rows[k] < 0)
             continue;
-        const float w = tw[slot0 + k];
-        const uint4 q = *reinterpret_cast<const uint4 *>(y + (size_t)row * s.H + col);
-        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-        float v[8];
+        const uint32_t wd[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(wd[i] << 16);
-            v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int i = 0; i < kCombineVec; ++i) {
-            const float prod = w * v[i];
-            acc[i] = acc[i] + prod;
+            const float lo = __uint_as_float(wd[i] << 16);
+            const float hi = __uint_as_float(wd[i] & 0xffff0000u);
+            const float p0 = w[k] * lo, p1 = w[k] * hi;
+            acc[2 * i] = acc[2 * i] + p0;
+            acc[2 * i + 1] = acc[2 * i + 1] + p1;
         }
     }
     uint32_t o[4];
