@@ -38,7 +38,8 @@ library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
             "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
-            "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_strerror"]
+            "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_set_tile_table",
+            "moe_get_tile_config", "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -62,6 +63,15 @@ class _CForwardArgs(ctypes.Structure):
                 ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("out_bf16", ctypes.c_void_p),
                 ("num_valid_tokens", ctypes.c_void_p), ("persistent", ctypes.c_int32)]
+
+
+class TileEntry(ctypes.Structure):
+    """One entry of the tuned tile table (moe_tile_entry)."""
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("gemm", "H", "I", "K", "E_total", "E_local", "max_tokens", "bm", "bn", "ku")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
 @dataclass(frozen=True)
@@ -133,10 +143,46 @@ def lib() -> ctypes.CDLL:
         h.moe_dispatch_valid.restype = ctypes.c_int
         h.moe_forward_ex.argtypes = [S, ctypes.POINTER(_CForwardArgs), P, ctypes.c_size_t, P]
         h.moe_forward_ex.restype = ctypes.c_int
+        h.moe_set_tile_table.argtypes = [ctypes.POINTER(TileEntry), ctypes.c_int32]
+        h.moe_set_tile_table.restype = ctypes.c_int
+        h.moe_get_tile_config.argtypes = [S, ctypes.c_int32, ctypes.POINTER(TileEntry)]
+        h.moe_get_tile_config.restype = ctypes.c_int
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
     return _lib
+
+
+def set_tile_table(entries) -> None:
+    """Replace the tuned tile table with entries (dicts with TileEntry's
+    fields); an empty list restores the built-in rule everywhere."""
+    entries = list(entries)
+    arr = (TileEntry * max(len(entries), 1))()
+    for i, e in enumerate(entries):
+        for n, _ in TileEntry._fields_:
+            setattr(arr[i], n, int(e[n]))
+    _check(lib().moe_set_tile_table(arr, len(entries)), "moe_set_tile_table")
+
+
+def load_tile_table(path: str) -> int:
+    """Install the table of a JSON file written by the tuner; returns its size."""
+    import json
+    with open(path) as f:
+        entries = json.load(f)["entries"]
+    set_tile_table(entries)
+    return len(entries)
+
+
+def get_tile_config(shape: MoeShape, gemm: int) -> Optional[dict]:
+    """The tile (bm, bn, ku) a launch of GEMM 1 or 2 would take, or None where
+    the register-streaming kernels serve the shape."""
+    c = shape.c()
+    out = TileEntry()
+    rc = lib().moe_get_tile_config(ctypes.byref(c), int(gemm), ctypes.byref(out))
+    if rc == -2:
+        return None
+    _check(rc, "moe_get_tile_config")
+    return out.as_dict()
 
 
 def moe_strerror(code: int) -> str:

@@ -350,6 +350,25 @@ int moe_forward_ex(const moe_shape *s, const moe_forward_args *a, void *ws, size
                         a->x_bf16, a->num_valid_tokens);
 }
 
+int moe_set_tile_table(const moe_tile_entry *entries, int32_t n)
+{
+    return moe::set_tile_table(entries, n);
+}
+
+int moe_get_tile_config(const moe_shape *s, int32_t gemm, moe_tile_entry *out)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (!out || (gemm != 1 && gemm != 2))
+        return MOE_EINVAL;
+    int bm = 0, bn = 0, ku = 0;
+    if (!moe::tile_config_of(*s, gemm == 1, &bm, &bn, &ku))
+        return MOE_ENOTSUP;
+    *out = moe_tile_entry{gemm, s->H, s->I, s->K, s->E_total, s->E_local, s->T, bm, bn, ku};
+    return MOE_OK;
+}
+
 const char *moe_strerror(int code)
 {
     switch (code) {

@@ -551,16 +551,6 @@ double rows_per_expert(const moe_shape &s)
     return (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
 }
 
-// The tiled kernels need a contraction of at least four K steps (512); where
-// they have it they are faster at every row count (measured on the V4 and
-// Flash shapes from 2.7 to 1000 rows per expert: their 64-row tiles read
-// each weight row 128 contiguous bytes at a time, which HBM serves faster
-// than the 64-byte fragments these kernels stream), so the kernels here
-// serve the shorter contractions.
-bool use_tiled_gemm1(const moe_shape &s) { return s.H >= 512; }
-
-bool use_tiled_gemm2(const moe_shape &s) { return s.I >= 512; }
-
 // Rows per chunk: enough for nearly every expert's rows in one pass over its
 // weights (mean + 3 standard deviations of the binomial route count, + 1),
 // at most 64; a second chunk of an expert streams its weights again.
@@ -576,6 +566,16 @@ int pick_nmb(const moe_shape &s)
 }
 
 } // namespace
+
+// The tiled kernels need a contraction of at least four K steps (512); where
+// they have it they are faster at every row count (measured on the V4 and
+// Flash shapes from 2.7 to 1000 rows per expert: their 64-row tiles read
+// each weight row 128 contiguous bytes at a time, which HBM serves faster
+// than the 64-byte fragments these kernels stream), so the kernels here
+// serve the shorter contractions.
+bool use_tiled_gemm1(const moe_shape &s) { return s.H >= 512; }
+
+bool use_tiled_gemm2(const moe_shape &s) { return s.I >= 512; }
 
 int device_cu_count()
 {

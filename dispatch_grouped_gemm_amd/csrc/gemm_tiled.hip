@@ -25,6 +25,8 @@
 // Work items are (row tile of one expert, N tile), derived on every
 // workgroup from counts as in the skinny kernels, and taken in a grid-stride
 // loop.
+#include <mutex>
+
 #include "moe_common.hpp"
 
 namespace moe {
@@ -521,6 +523,13 @@ long tile_upper_bound(const moe_shape &s, int bm)
 
 } // namespace
 
+// 64-row tiles up to 96 expected rows per expert.  An expert past 64 rows
+// streams its weights twice (64-row tiles read them non-temporally), yet on
+// the Flash shape with a tenth of the slots -1 (57 rows per expert on
+// average) the 64-row tiles still win, 334 against 360 us for GEMM1; with no
+// -1 slots (64 rows) the 128-row tiles win, 354 against 434 us.  The host
+// sees neither the -1 slots nor the skew, so shapes near the bound are left
+// to the tuned table.
 int tiled_bm(const moe_shape &s)
 {
     const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
@@ -552,8 +561,44 @@ struct TiledConfig {
     int bm, bn, ku;
 };
 
+// The tile shapes compiled for both GEMMs (a tuned table may name only these).
+constexpr TiledConfig kTiledShapes[] = {{64, 128, 2}, {64, 256, 1}, {128, 128, 1}, {128, 256, 1}};
+
+// A tuned table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE tuning
+// for gfx950", tuning: one config per shape and token bucket, a count between
+// two buckets taking the larger one): entries set through
+// moe_set_tile_table, read by every launch under a lock.
+constexpr int kMaxTileEntries = 256;
+std::mutex g_table_mu;
+moe_tile_entry g_table[kMaxTileEntries];
+int g_table_n = 0;
+
+bool table_lookup(const moe_shape &s, bool gemm1, TiledConfig *out)
+{
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    int best = -1;
+    for (int i = 0; i < g_table_n; ++i) {
+        const moe_tile_entry &e = g_table[i];
+        if (e.gemm != (gemm1 ? 1 : 2) || e.H != s.H || e.I != s.I || e.K != s.K ||
+            e.E_total != s.E_total || e.E_local != s.E_local || e.max_tokens < s.T)
+            continue;
+        // N tiles must cover the output columns exactly
+        if (gemm1 ? s.I % (e.bn / 2) != 0 : s.H % e.bn != 0)
+            continue;
+        if (best < 0 || e.max_tokens < g_table[best].max_tokens)
+            best = i;
+    }
+    if (best < 0)
+        return false;
+    *out = TiledConfig{g_table[best].bm, g_table[best].bn, g_table[best].ku};
+    return true;
+}
+
 TiledConfig tiled_config(const moe_shape &s, bool gemm1)
 {
+    TiledConfig c;
+    if (table_lookup(s, gemm1, &c))
+        return c;
     const int bm = tiled_bm(s), bn = tiled_bn(s, gemm1);
     if (bm == 64)
         return {64, 128, 2};
@@ -586,6 +631,7 @@ hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8
         return launch_tiled<kGemm1, BM, BN, KU>(sh, act, act_s, counts, offsets, row_route, w, ws, \
                                                 h, hs, y, st);
     MOE_TILED_CASE(64, 128, 2)
+    MOE_TILED_CASE(64, 256, 1)
     MOE_TILED_CASE(128, 128, 1)
 #undef MOE_TILED_CASE
     return launch_tiled<kGemm1, 128, 256, 1>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
@@ -609,6 +655,36 @@ static int xcd_count()
 {
     const int cus = device_cu_count();
     return cus == 32 || cus == 64 || cus == 128 || cus == 256 ? cus / 32 : 0;
+}
+
+int set_tile_table(const moe_tile_entry *entries, int n)
+{
+    if (n < 0 || n > kMaxTileEntries || (n > 0 && !entries))
+        return MOE_EINVAL;
+    for (int i = 0; i < n; ++i) {
+        const moe_tile_entry &e = entries[i];
+        bool known = false;
+        for (const TiledConfig &c : kTiledShapes)
+            known |= c.bm == e.bm && c.bn == e.bn && c.ku == e.ku;
+        if (!known || (e.gemm != 1 && e.gemm != 2) || e.max_tokens < 0)
+            return MOE_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    for (int i = 0; i < n; ++i)
+        g_table[i] = entries[i];
+    g_table_n = n;
+    return MOE_OK;
+}
+
+bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
+{
+    if (!(gemm1 ? use_tiled_gemm1(s) : use_tiled_gemm2(s)))
+        return false;
+    const TiledConfig c = tiled_config(s, gemm1);
+    *bm = c.bm;
+    *bn = c.bn;
+    *ku = c.ku;
+    return true;
 }
 
 // The persistent layer takes the 128-row tiles (the prefill sizes) of both

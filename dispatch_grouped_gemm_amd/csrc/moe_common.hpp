@@ -339,6 +339,13 @@ hipError_t launch_gemm2(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                         const uint8_t *w2s, uint16_t *y, hipStream_t st);
 int tiled_bm(const moe_shape &s);
+bool use_tiled_gemm1(const moe_shape &s);
+bool use_tiled_gemm2(const moe_shape &s);
+// tuned tile table (copied in; MOE_OK or MOE_EINVAL) and the tile shape a
+// launch of the tiled GEMM would take (false where the register-streaming
+// kernels serve the shape)
+int set_tile_table(const moe_tile_entry *entries, int n);
+bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku);
 hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                               const int32_t *counts, const int32_t *offsets,
                               const int32_t *row_route, const uint8_t *w13, const uint8_t *w13s,

@@ -258,6 +258,39 @@ typedef struct {
 int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/*
+ * Tuned tile table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE
+ * tuning for gfx950", tuning: one kernel config per shape and token bucket,
+ * a token count between two buckets taking the larger bucket, every
+ * candidate checked against the reference config).  An entry names a GEMM
+ * (1: GEMM1 + SwiGLU + requant, 2: GEMM2), the shape fields it applies to
+ * (H, I, K, E_total, E_local exactly), the bucket's largest T, and the tile
+ * of the LDS-tiled kernel: rows bm x weight rows bn, ku K steps per stage,
+ * one of (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1).  A call
+ * takes the entry of its GEMM and shape with the smallest max_tokens >= T;
+ * with none, the built-in rule (64-row tiles up to 96 expected rows per
+ * expert, else 128-row tiles).  Every tile gives the same bits (the K order of each sum does not
+ * depend on it).  The table applies where the tiled kernels run (H or I at
+ * least 512); an entry whose N tile does not divide the output columns
+ * (GEMM1: I by bn/2, GEMM2: H by bn) is passed over.
+ */
+typedef struct {
+    int32_t gemm;
+    int32_t H, I, K, E_total, E_local;
+    int32_t max_tokens;
+    int32_t bm, bn, ku;
+} moe_tile_entry;
+
+/* Replace the table with n entries (copied; n = 0 clears it).  MOE_EINVAL
+ * for an unknown tile or GEMM.  Takes effect for launches issued after it
+ * returns; safe to call while other threads launch. */
+int moe_set_tile_table(const moe_tile_entry *entries, int32_t n);
+
+/* The tile a launch of GEMM `gemm` (1 or 2) with this shape would take, in
+ * out->bm, bn, ku (the other fields copied from the shape); MOE_ENOTSUP where
+ * the register-streaming kernels serve the shape. */
+int moe_get_tile_config(const moe_shape *shape, int32_t gemm, moe_tile_entry *out);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

@@ -138,3 +138,39 @@ def test_quant_and_bf16_forward_refusals(lib):
     # the workspace carries the MX FP8 activations of the bf16 entry point
     s = moe.MoeShape(**V4)
     assert moe.moe_workspace_size(s) >= 128 * 6 * (3072 + 96 + 2 * 7168) + 128 * (7168 + 224)
+
+
+def test_tile_table(lib):
+    """The tuned tile table: refusals, the built-in rule, bucket choice (the
+    smallest bucket holding T, so a count between two buckets takes the
+    larger), and clearing.  Host logic only."""
+    small = moe.MoeShape(**{**V4, "H": 256})
+    assert moe.get_tile_config(small, 1) is None            # register-streaming kernels
+    dec = moe.MoeShape(**V4)                                 # 128 tokens: 64-row tiles
+    assert {k: moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")} == \
+        {"bm": 64, "bn": 128, "ku": 2}
+    pre = moe.MoeShape(**{**V4, "T": 65536})
+    assert moe.get_tile_config(pre, 2)["bm"] == 128
+    base = dict(gemm=1, H=7168, I=3072, K=6, E_total=384, E_local=48)
+    with pytest.raises(moe.MoeError):
+        moe.set_tile_table([dict(base, max_tokens=128, bm=32, bn=128, ku=2)])
+    with pytest.raises(moe.MoeError):
+        moe.set_tile_table([dict(base, gemm=3, max_tokens=128, bm=64, bn=128, ku=2)])
+    assert lib.moe_set_tile_table(None, -1) == -1
+    try:
+        moe.set_tile_table([dict(base, max_tokens=256, bm=128, bn=128, ku=1),
+                            dict(base, max_tokens=2048, bm=64, bn=256, ku=1),
+                            dict(base, gemm=2, max_tokens=256, bm=128, bn=256, ku=1)])
+        t = lambda T, g: tuple(moe.get_tile_config(moe.MoeShape(**{**V4, "T": T}), g)[k]
+                               for k in ("bm", "bn", "ku"))
+        assert t(128, 1) == (128, 128, 1)        # first bucket
+        assert t(256, 1) == (128, 128, 1)        # on its bound
+        assert t(257, 1) == (64, 256, 1)         # between buckets: the larger one
+        assert t(4096, 1) == (64, 128, 2)        # past every bucket: the rule
+        assert t(65536, 1) == (128, 256, 1)
+        assert t(128, 2) == (128, 256, 1)
+        other = moe.MoeShape(**{**V4, "E_local": 96})
+        assert moe.get_tile_config(other, 1)["bm"] == 64   # another shape: the rule
+    finally:
+        moe.set_tile_table([])
+    assert tuple(moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")) == (64, 128, 2)
