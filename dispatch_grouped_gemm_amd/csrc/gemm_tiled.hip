@@ -376,18 +376,30 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                 }
             }
         } else {
+            // the bf16 tile goes through LDS (rows of BN*2 + 16 bytes: the
+            // fragment writes of a half-wavefront hit distinct banks), then
+            // out as whole 16-byte pieces of rows, 32 lanes to a 512-byte row
+            constexpr int PITCH = BN * 2 + 16;
+            static_assert(BM * PITCH <= L::kStages * L::kStage + L::kExpSlots * L::kExp,
+                          "y tile fits the stage ring");
+            __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 const int m = wm * (BM / 2) + 16 * j + i16;
-                if (m < nrows) {
-                    uint16_t *yr = y_out + (size_t)(row0 + m) * (size_t)H + (size_t)nt * BN +
-                                   (BN / 2) * wn + 4 * kq;
 #pragma unroll
-                    for (int i = 0; i < GW; ++i)
-                        *reinterpret_cast<uint2 *>(yr + 16 * i) =
-                            uint2{f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16),
-                                  f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16)};
-                }
+                for (int i = 0; i < GW; ++i)
+                    *reinterpret_cast<uint2 *>(lds + m * PITCH + 2 * ((BN / 2) * wn + 16 * i + 4 * kq)) =
+                        uint2{f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16),
+                              f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16)};
+            }
+            __syncthreads();
+            constexpr int PR = BN / 8;                 // 16-byte pieces per row
+#pragma unroll
+            for (int p = 0; p < BM * PR / kThreads; ++p) {
+                const int piece = p * kThreads + tid, r = piece / PR, c = piece % PR;
+                if (r < nrows)
+                    *reinterpret_cast<u32x4 *>(y_out + (size_t)(row0 + r) * (size_t)H +
+                                               (size_t)nt * BN + 8 * c) = lds_read16(lds + r * PITCH + 16 * c);
             }
         }
     }
