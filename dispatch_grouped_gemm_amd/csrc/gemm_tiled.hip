@@ -339,6 +339,13 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         // 4kq..4kq+3 of each of its GW groups
         if (kGemm1) {
             constexpr int CB = GW / 2;   // 16-column blocks of h per wavefront
+            // the h codes go through LDS (rows of BN/2 + 16 bytes, so the
+            // 4-byte writes of a wavefront hit distinct banks), then out as
+            // whole 16-byte pieces of rows
+            constexpr int HP = BN / 2 + 16;
+            static_assert(BM * HP <= L::kStages * L::kStage + L::kExpSlots * L::kExp,
+                          "h tile fits the stage ring");
+            __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 const int m = wm * (BM / 2) + 16 * j + i16;
@@ -360,20 +367,26 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                     amax = fmaxf(amax, __shfl_xor(amax, 16));
                     amax = fmaxf(amax, __shfl_xor(amax, 32));
                     const int E = mx8_block_exponent(amax);
-                    if (m < nrows) {
-                        const size_t row = (size_t)(row0 + m);
-                        const int col0 = nt * (BN / 2) + (BN / 4) * wn + 32 * blk;
+                    const int tcol = (BN / 4) * wn + 32 * blk;   // column in the tile
 #pragma unroll
-                        for (int cb = 2 * blk; cb < 2 * blk + 2; ++cb) {
-                            const uint32_t pk =
-                                mx8_pack4(hv[cb][0], hv[cb][1], hv[cb][2], hv[cb][3], E, amax);
-                            *reinterpret_cast<uint32_t *>(h_out + row * (size_t)I + col0 +
-                                                          16 * (cb - 2 * blk) + 4 * kq) = pk;
-                        }
-                        if (kq == 0)
-                            hs_out[row * (size_t)(I / 32) + col0 / 32] = (uint8_t)(E + 127);
-                    }
+                    for (int cb = 2 * blk; cb < 2 * blk + 2; ++cb)
+                        *reinterpret_cast<uint32_t *>(lds + m * HP + tcol + 16 * (cb - 2 * blk) +
+                                                      4 * kq) =
+                            mx8_pack4(hv[cb][0], hv[cb][1], hv[cb][2], hv[cb][3], E, amax);
+                    if (m < nrows && kq == 0)
+                        hs_out[(size_t)(row0 + m) * (size_t)(I / 32) + (nt * (BN / 2) + tcol) / 32] =
+                            (uint8_t)(E + 127);
                 }
+            }
+            __syncthreads();
+            constexpr int PR = BN / 32;                // 16-byte pieces per row
+#pragma unroll
+            for (int p = 0; p < (BM * PR + kThreads - 1) / kThreads; ++p) {
+                const int piece = p * kThreads + tid, r = piece / PR, c = piece % PR;
+                if (piece < BM * PR && r < nrows)
+                    *reinterpret_cast<u32x4 *>(h_out + (size_t)(row0 + r) * (size_t)I +
+                                               (size_t)nt * (BN / 2) + 16 * c) =
+                        lds_read16(lds + r * HP + 16 * c);
             }
         } else {
             // the bf16 tile goes through LDS (rows of BN*2 + 16 bytes: the
