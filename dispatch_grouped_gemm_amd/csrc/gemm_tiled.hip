@@ -445,12 +445,12 @@ struct TileShared {
 // sync[256 + q] = ready[q], all zero at launch.  Every wait is bounded:
 // past the bound a workgroup goes on (wrong numbers, which the tests would
 // catch, rather than a GPU that never finishes).
-template <int BM, int BN1, int BN2>
+template <int BM, int BN1, int BN2, int KU>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int nq)
 {
     // one stage ring, sized for the wider of the two weight tiles
-    __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), 1> sh;
+    __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), KU> sh;
     __shared__ int ticket_sh;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int NT1 = s.I / (BN1 / 2), NT2 = s.H / BN2;
@@ -478,7 +478,7 @@ layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int 
             next = atomicAdd(ticket, lane == 0 ? 1 : 0);
         if (t < n1) {
             const int q = x + nq * (t / NT1), nt = t % NT1;
-            tiled_item<true, BM, BN1, 1, false>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
+            tiled_item<true, BM, BN1, KU, false>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
             wait_vmcnt<0>();   // this thread's h stores are in the L2
             __syncthreads();   // ... and every thread's
             if (wave == 0)
@@ -495,7 +495,7 @@ layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int 
                 }
             }
             __syncthreads();
-            tiled_item<false, BM, BN2, 1, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
+            tiled_item<false, BM, BN2, KU, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
         }
         if (wave == 0)
             ticket_sh = __builtin_amdgcn_readfirstlane(next);
@@ -712,17 +712,21 @@ bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
     return true;
 }
 
-// The persistent layer takes the 128-row tiles (the prefill sizes) of both
-// GEMMs, on a device whose XCDs it can tell apart.
+// The persistent layer takes the tiled GEMMs when both use the same row
+// tile: 128 rows with one K step per stage (any weight tile widths) or 64
+// rows with two K steps and 128 weight rows; on a device whose XCDs it can
+// tell apart.
 bool persistent_supported(const moe_shape &sh)
 {
     if (sh.H < 512 || sh.I < 512 || xcd_count() == 0)
         return false;
     const TiledConfig a = tiled_config(sh, true), b = tiled_config(sh, false);
-    return a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1;
+    if (a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1)
+        return true;
+    return a.bm == 64 && b.bm == 64 && a.ku == 2 && b.ku == 2 && a.bn == 128 && b.bn == 128;
 }
 
-int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 128); }
+int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 64); }
 
 hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
                                    const int32_t *counts, const int32_t *offsets,
@@ -735,23 +739,26 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
     fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
     const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr};
     const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y};
-    const int bn1 = tiled_config(sh, true).bn, bn2 = tiled_config(sh, false).bn;
+    const TiledConfig c1 = tiled_config(sh, true);
+    const int bn1 = c1.bn, bn2 = tiled_config(sh, false).bn;
     const int nq = xcd_count();
     // workgroup b runs on XCD b mod nq: a grid of nq or more workgroups puts
     // at least one on every XCD, so every queue is served
-    auto go = [&](auto k, int b1, int b2) {
-        const long items = tile_upper_bound(sh, 128) * (long)(sh.I / (b1 / 2) + sh.H / b2);
+    auto go = [&](auto k, int bm, int b1, int b2) {
+        const long items = tile_upper_bound(sh, bm) * (long)(sh.I / (b1 / 2) + sh.H / b2);
         const int grid = tiled_grid(k, items);
         k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, nq);
     };
-    if (bn1 == 256 && bn2 == 256)
-        go(layer_persistent_kernel<128, 256, 256>, 256, 256);
+    if (c1.bm == 64)
+        go(layer_persistent_kernel<64, 128, 128, 2>, 64, 128, 128);
+    else if (bn1 == 256 && bn2 == 256)
+        go(layer_persistent_kernel<128, 256, 256, 1>, 128, 256, 256);
     else if (bn1 == 256)
-        go(layer_persistent_kernel<128, 256, 128>, 256, 128);
+        go(layer_persistent_kernel<128, 256, 128, 1>, 128, 256, 128);
     else if (bn2 == 256)
-        go(layer_persistent_kernel<128, 128, 256>, 128, 256);
+        go(layer_persistent_kernel<128, 128, 256, 1>, 128, 128, 256);
     else
-        go(layer_persistent_kernel<128, 128, 128>, 128, 128);
+        go(layer_persistent_kernel<128, 128, 128, 1>, 128, 128, 128);
     return hipGetLastError();
 }
 

@@ -89,8 +89,10 @@ def test_refusals_return_before_any_launch(lib):
     assert lib.moe_gemm1_swiglu(ctypes.byref(c), *([fake] * 6), odd, fake, fake, null) == -1
     assert lib.moe_gemm2(ctypes.byref(c), *([fake] * 6), odd, null) == -1
     assert lib.moe_combine(ctypes.byref(c), fake, fake, odd, fake, null) == -1
-    # the persistent variant takes 128-row tiles only: refused at decode sizes
-    assert lib.moe_forward_persistent(ctypes.byref(c), *([fake] * 9), fake, 1 << 40, null) == -2
+    # the persistent variant needs contractions of 512 or more: refused for H = 256
+    short = moe.MoeShape(**{**V4, "H": 256}).c()
+    assert lib.moe_forward_persistent(ctypes.byref(short), *([fake] * 9), fake, 1 << 40,
+                                      null) == -2
     pre = moe.MoeShape(**{**V4, "T": 65536}).c()
     assert lib.moe_forward_persistent(ctypes.byref(pre), *([null] * 10), 0, null) == -1
     # T = 0 is a no-op for the steps that have nothing to do
@@ -102,6 +104,7 @@ def test_refusals_return_before_any_launch(lib):
 
 def test_quant_and_bf16_forward_refusals(lib):
     c = moe.MoeShape(**V4).c()
+    short = moe.MoeShape(**{**V4, "H": 256}).c()
     bad = moe.MoeShape(**{**V4, "K": 0}).c()
     z = moe.MoeShape(**{**V4, "T": 0}).c()
     null = None
@@ -134,7 +137,8 @@ def test_quant_and_bf16_forward_refusals(lib):
     assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 16, null) == -3
     assert lib.moe_forward_ex(ctypes.byref(c), None, fake, 1 << 40, null) == -1
     args.persistent = 1
-    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(args), fake, 1 << 40, null) == -2
+    assert lib.moe_forward_ex(ctypes.byref(short), ctypes.byref(args), fake, 1 << 40,
+                              null) == -2
     # the workspace carries the MX FP8 activations of the bf16 entry point
     s = moe.MoeShape(**V4)
     assert moe.moe_workspace_size(s) >= 128 * 6 * (3072 + 96 + 2 * 7168) + 128 * (7168 + 224)

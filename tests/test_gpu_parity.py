@@ -259,10 +259,13 @@ def test_persistent_layer_small(T, H, I):
     check_layer(case, np.arange(T), ref, steps, "persistent T=%d H=%d I=%d" % (T, H, I))
 
 
-@pytest.mark.parametrize("name", ["v4_prefill_t65536_uniform", "v4_prefill_t65536_hot30"])
+@pytest.mark.parametrize("name", ["v4_decode_t128_fixed", "v4_t1024_compact", "v4_t2048_fixed",
+                                  "flash_t4096_compact", "v4_prefill_t65536_uniform",
+                                  "v4_prefill_t65536_hot30"])
 def test_persistent_layer_full_size(name):
-    """The persistent layer on the prefill workloads: every output element
-    equals moe_forward's (which the sampled oracle checks cover)."""
+    """The persistent layer on the full-size workloads (64-row tiles with two
+    K steps up to T=4096, 128-row tiles at 65,536 tokens): every output
+    element equals moe_forward's (which the sampled oracle checks cover)."""
     case = cached_case(name)
     say("persistent", name)
     g = upload(case)
