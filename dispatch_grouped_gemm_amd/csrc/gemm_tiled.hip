@@ -216,10 +216,9 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)cc;
             xrow_used[i] = R < nrows;
         }
-        // exponents, four K steps (16 bytes) per row at a time: wavefront v
-        // brings weight rows 64 (v mod BN/64) + l and activation rows
-        // 64 (v mod BM/64) + l (where there are fewer than four such row
-        // blocks, two wavefronts write the same bytes to the same place).
+        // exponents, four K steps (16 bytes) per row at a time: wavefront
+        // v < BN/64 brings weight rows 64 v + l, wavefront v < BM/64
+        // activation rows 64 v + l.
         // The last group of a row is read from 16 bytes before the row's
         // end, so no read passes it (KS >= 4).
         const int we_wave = wave % (BN / 64);
@@ -266,8 +265,10 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                 const int grp = ks0 >> 2;
                 const uint32_t es = (uint32_t)((grp % L::kExpSlots) * L::kExp);
                 const uint32_t eb = (uint32_t)ebase(grp);
-                g2lds<16>(ws, weoff + eb, lds_we + es);
-                if (xe_used)
+                // one wavefront per 64-row block (no two load the same rows)
+                if (wave < BN / 64)
+                    g2lds<16>(ws, weoff + eb, lds_we + es);
+                if (wave < BM / 64 && xe_used)
                     g2lds<16, false, kL2>(act_s, xeoff + eb, lds_xe + es);
             }
         };
