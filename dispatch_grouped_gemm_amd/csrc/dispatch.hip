@@ -21,8 +21,13 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSlotsPerWaveLarge = 128;
 constexpr int kLargeBatch = kSlotsPerWaveLarge / 64;
 constexpr int kSlotsPerBlockLarge = kWaves * kSlotsPerWaveLarge;
-// compact dispatch of at most this many slots runs in one workgroup
-constexpr long kSmallSlots = 8192;
+// Dispatches of at most this many slots run in one workgroup (measured, back
+// to back: compact 6144 slots 10.3 us in one workgroup, 7.7 us over three in
+// two launches; fixed-slot 24,576 slots 8.6 us in one workgroup, 10.9 us as
+// reset + claim).  Past one workgroup's 2048 slots the compact passes run
+// workgroups in parallel; a fixed-slot claim is one LDS atomic per route.
+constexpr long kCompactOneWgSlots = kSlotsPerBlockLarge;
+constexpr long kFixedOneWgSlots = 32768;
 
 struct Match {
     int rank;                 // lanes below with the same key
@@ -118,37 +123,47 @@ __device__ int wave_histogram(const Shape &s, const int32_t *__restrict__ ids, l
     return wave_sum(invalid);
 }
 
-// Stable scatter of the slots [b, e): base_row[ex] (LDS, this wavefront's
-// own row) is the next row of expert ex for this wavefront.
+// Stable scatter of the slots base + 64 p + lane below e, whose keys ex[]
+// were loaded by load_keys: base_row[ex] (LDS, this wavefront's own row) is
+// the next row of expert ex for this wavefront.
+template <int P>
+__device__ __forceinline__ void scatter_keys(const int (&ex)[P], long base, long e, int *base_row,
+                                             int32_t *__restrict__ row_route,
+                                             int32_t *__restrict__ route_row)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        if (base + 64 * p >= e)
+            break;
+        const long r = base + 64 * p + lane;
+        const Match m = wave_match(ex[p], ex[p] >= 0);
+        int row = -1;
+        if (ex[p] >= 0)
+            row = base_row[ex[p]] + m.rank;
+        // every lane has read its base before a leader moves it on
+        __builtin_amdgcn_wave_barrier();
+        if (ex[p] >= 0 && m.rank == 0)
+            base_row[ex[p]] += m.count;
+        __builtin_amdgcn_wave_barrier();
+        if (r < e) {
+            route_row[r] = row;
+            if (row >= 0)
+                row_route[row] = (int32_t)r;
+        }
+    }
+}
+
+// Stable scatter of the slots [b, e), keys loaded P batches at a time.
 template <int P>
 __device__ void wave_scatter(const Shape &s, const int32_t *__restrict__ ids, long b, long e,
                              long nv, int *base_row, int32_t *__restrict__ row_route,
                              int32_t *__restrict__ route_row)
 {
-    const int lane = threadIdx.x & 63;
     for (long base = b; base < e; base += 64 * P) {
         int ex[P];
         load_keys<P>(s, ids, base, e, nv, ex);
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            if (base + 64 * p >= e)
-                break;
-            const long r = base + 64 * p + lane;
-            const Match m = wave_match(ex[p], ex[p] >= 0);
-            int row = -1;
-            if (ex[p] >= 0)
-                row = base_row[ex[p]] + m.rank;
-            // every lane has read its base before a leader moves it on
-            __builtin_amdgcn_wave_barrier();
-            if (ex[p] >= 0 && m.rank == 0)
-                base_row[ex[p]] += m.count;
-            __builtin_amdgcn_wave_barrier();
-            if (r < e) {
-                route_row[r] = row;
-                if (row >= 0)
-                    row_route[row] = (int32_t)r;
-            }
-        }
+        scatter_keys<P>(ex, base, e, base_row, row_route, route_row);
     }
 }
 
@@ -285,87 +300,80 @@ compact_hist_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restric
         row[E] = invalid_total;
 }
 
-// Pass 2 (one workgroup): counts, offsets, status, and every workgroup's
-// first row per expert, written back over its histogram.
-template <bool kStaged>
+// Pass 2: the stable scatter of each workgroup's slots.  A workgroup sums the
+// pass-1 table itself: over the workgroups before it (its first row within
+// each expert's segment) and over all of them (the segment sizes, scanned
+// over the experts into the offsets); the first workgroup also writes the
+// counts, offsets and status.  Each wavefront loads its keys once.
 __global__ void __launch_bounds__(kThreads)
-compact_scan_kernel(Shape s, int nblk, int32_t *__restrict__ scratch, int32_t *__restrict__ counts,
-                    int32_t *__restrict__ offsets, int32_t *__restrict__ status)
-{
-    // kStaged: the [nblk][E+1] table is copied to LDS first (coalesced), so
-    // the per-expert walk over the blocks runs at LDS rather than global
-    // memory latency, and copied back at the end
-    extern __shared__ int staged[];
-    const int tid = threadIdx.x;
-    const int E = s.E_local;
-    const int nval = nblk * (E + 1);
-    int32_t *tab = scratch;
-    if (kStaged) {
-        for (int i = tid; i < nval; i += kThreads)
-            staged[i] = scratch[i];
-        __syncthreads();
-        tab = staged;
-    }
-    int cnt = 0;
-    if (tid < E) {
-        for (int b = 0; b < nblk; ++b) {
-            int32_t *p = tab + (size_t)b * (E + 1) + tid;
-            const int c = *p;
-            *p = cnt;
-            cnt += c;
-        }
-    }
-    int total;
-    const int off = block_exclusive_scan(tid < E ? cnt : 0, &total);
-    if (tid < E) {
-        counts[tid] = cnt;
-        offsets[tid] = off;
-        for (int b = 0; b < nblk; ++b)
-            tab[(size_t)b * (E + 1) + tid] += off;
-    }
-    if (tid == 0) {
-        offsets[E] = total;
-        int inv = 0;
-        for (int b = 0; b < nblk; ++b)
-            inv += tab[(size_t)b * (E + 1) + E];
-        status[0] = inv;
-        status[1] = status[2] = status[3] = 0;
-    }
-    if (kStaged) {
-        __syncthreads();
-        for (int i = tid; i < nval; i += kThreads)
-            scratch[i] = staged[i];
-    }
-}
-
-// Pass 3: stable scatter of each workgroup's slots from its first rows.
-__global__ void __launch_bounds__(kThreads)
-compact_scatter_kernel(Shape s, const int32_t *__restrict__ ids, const int32_t *__restrict__ scratch,
+compact_scatter_kernel(Shape s, int nblk, const int32_t *__restrict__ ids,
+                       const int32_t *__restrict__ scratch, int32_t *__restrict__ counts,
+                       int32_t *__restrict__ offsets, int32_t *__restrict__ status,
                        int32_t *__restrict__ row_route, int32_t *__restrict__ route_row,
                        const int32_t *__restrict__ valid)
 {
     const long nv = valid_slots(s, valid);
-    extern __shared__ int hist[]; // [kWaves][E_local]
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int E = s.E_local;
+    // [kWaves][E] histograms, then [kWaves][E+1] partial sums before / all
+    extern __shared__ int lds[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = s.E_local, E1 = E + 1;
+    int *hist = lds;
+    int *part_before = hist + kWaves * E;
+    int *part_all = part_before + kWaves * E1;
     const long n = (long)s.T * s.K;
+    const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
+    const long e = min(n, b + kSlotsPerWaveLarge);
+    int ex[kLargeBatch];
+    load_keys<kLargeBatch>(s, ids, b, e, nv, ex);
+    // wavefront w sums the rows of workgroups w, w + 16, ... of the table
+    for (int c = lane; c < E1; c += 64) {
+        int before = 0, all = 0;
+#pragma unroll 4
+        for (int w = wave; w < nblk; w += kWaves) {
+            const int v = scratch[(size_t)w * E1 + c];
+            all += v;
+            before += w < (int)blockIdx.x ? v : 0;
+        }
+        part_before[wave * E1 + c] = before;
+        part_all[wave * E1 + c] = all;
+    }
     for (int i = tid; i < kWaves * E; i += kThreads)
         hist[i] = 0;
     __syncthreads();
-    const long b = min(n, (long)blockIdx.x * kSlotsPerBlockLarge + (long)wave * kSlotsPerWaveLarge);
-    const long e = min(n, b + kSlotsPerWaveLarge);
-    (void)wave_histogram<kLargeBatch>(s, ids, b, e, nv, hist + wave * E);
-    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kLargeBatch; ++p)
+        if (ex[p] >= 0)
+            atomicAdd(&hist[wave * E + ex[p]], 1);
+    int before = 0, all = 0;
+    if (tid < E1)
+        for (int w = 0; w < kWaves; ++w) {
+            before += part_before[w * E1 + tid];
+            all += part_all[w * E1 + tid];
+        }
+    int total;
+    const int off = block_exclusive_scan(tid < E ? all : 0, &total);
+    // block_exclusive_scan ends with a barrier: the histograms are complete
     if (tid < E) {
-        int run = scratch[(size_t)blockIdx.x * (E + 1) + tid];
+        int run = off + before; // per-wavefront bases, wavefronts in slot order
         for (int w = 0; w < kWaves; ++w) {
             const int c = hist[w * E + tid];
             hist[w * E + tid] = run;
             run += c;
         }
     }
+    if (blockIdx.x == 0) {
+        if (tid < E) {
+            counts[tid] = all;
+            offsets[tid] = off;
+        }
+        if (tid == E) {
+            offsets[E] = total;
+            status[0] = all; // column E holds the invalid ids
+            status[1] = status[2] = status[3] = 0;
+        }
+    }
     __syncthreads();
-    wave_scatter<kLargeBatch>(s, ids, b, e, nv, hist + wave * E, row_route, route_row);
+    scatter_keys<kLargeBatch>(ex, b, e, hist + wave * E, row_route, route_row);
 }
 
 // ---- fixed-slot ----------------------------------------------------------------
@@ -519,8 +527,6 @@ fixed_claim_kernel(Shape s, const int32_t *__restrict__ ids, int32_t *__restrict
 
 long num_slots(const moe_shape &s) { return (long)s.T * s.K; }
 
-bool compact_is_small(const moe_shape &s) { return num_slots(s) <= kSmallSlots; }
-
 int large_blocks(const moe_shape &s)
 {
     return (int)((num_slots(s) + kSlotsPerBlockLarge - 1) / kSlotsPerBlockLarge);
@@ -528,11 +534,15 @@ int large_blocks(const moe_shape &s)
 
 } // namespace
 
-bool dispatch_is_single_block(const moe_shape &s) { return num_slots(s) <= kSmallSlots; }
+bool dispatch_is_single_block(const moe_shape &s)
+{
+    return num_slots(s) <= (s.dispatch_mode == MOE_DISPATCH_COMPACT ? kCompactOneWgSlots
+                                                                    : kFixedOneWgSlots);
+}
 
 size_t dispatch_scratch_bytes(const moe_shape &s)
 {
-    if (s.dispatch_mode != MOE_DISPATCH_COMPACT || compact_is_small(s))
+    if (s.dispatch_mode != MOE_DISPATCH_COMPACT || dispatch_is_single_block(s))
         return 0;
     return (size_t)large_blocks(s) * (size_t)(s.E_local + 1) * sizeof(int32_t);
 }
@@ -542,20 +552,21 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
                            int32_t *status, void *scratch, hipStream_t st, int32_t *zero,
                            int nzero, const QuantJob *quant, const int32_t *valid)
 {
-    if (nzero > 0 && !dispatch_is_single_block(sh))
+    const bool one = dispatch_is_single_block(sh);
+    if (nzero > 0 && !one)
         return hipErrorInvalidValue;
     const Shape s = to_dev(sh);
     const size_t E = (size_t)sh.E_local;
     // one-workgroup paths: the quant rides in extra workgroups of the launch
     const QuantJob qj = quant ? *quant : QuantJob{nullptr, nullptr, nullptr, 0};
     const int grid = 1 + (qj.blocks > 0 ? quant_blocks(qj, kThreads) : 0);
-    if (!dispatch_is_single_block(sh) && qj.blocks > 0) {
+    if (!one && qj.blocks > 0) {
         const hipError_t e = launch_quant_mxfp8(qj, st);
         if (e != hipSuccess)
             return e;
     }
     if (sh.dispatch_mode == MOE_DISPATCH_COMPACT) {
-        if (compact_is_small(sh)) {
+        if (one) {
             compact_small_kernel<<<grid, kThreads, kWaves * E * sizeof(int), st>>>(
                 s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj, valid);
             return hipGetLastError();
@@ -563,18 +574,12 @@ hipError_t launch_dispatch(const moe_shape &sh, const int32_t *ids, int32_t *cou
         const int nblk = large_blocks(sh);
         int32_t *blk = static_cast<int32_t *>(scratch);
         compact_hist_kernel<<<nblk, kThreads, E * sizeof(int), st>>>(s, ids, blk, valid);
-        const size_t table = (size_t)nblk * (E + 1) * sizeof(int);
-        if (table <= 128 * 1024)
-            compact_scan_kernel<true><<<1, kThreads, table, st>>>(s, nblk, blk, counts, offsets,
-                                                                   status);
-        else
-            compact_scan_kernel<false><<<1, kThreads, 0, st>>>(s, nblk, blk, counts, offsets,
-                                                                status);
-        compact_scatter_kernel<<<nblk, kThreads, kWaves * E * sizeof(int), st>>>(
-            s, ids, blk, row_route, route_row, valid);
+        const size_t lds = (kWaves * E + 2 * kWaves * (E + 1)) * sizeof(int);
+        compact_scatter_kernel<<<nblk, kThreads, lds, st>>>(s, nblk, ids, blk, counts, offsets,
+                                                           status, row_route, route_row, valid);
         return hipGetLastError();
     }
-    if (num_slots(sh) <= kSmallSlots) {
+    if (one) {
         fixed_small_kernel<<<grid, kThreads, E * sizeof(int), st>>>(
             s, ids, counts, offsets, row_route, route_row, status, zero, nzero, qj, valid);
         return hipGetLastError();

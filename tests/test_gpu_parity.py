@@ -54,7 +54,8 @@ def _edge_ids(rng, T, K, E_total):
     return ids
 
 
-@pytest.mark.parametrize("T", [0, 1, 5, 700, 5000])
+# K = 8: compact runs in one workgroup up to T = 256, fixed-slot up to 4096
+@pytest.mark.parametrize("T", [0, 1, 5, 200, 700, 3000, 5000])
 @pytest.mark.parametrize("mode,cap", [(0, 0), (1, 3), (1, 64)])
 def test_dispatch_edges(T, mode, cap):
     rng = np.random.default_rng(T * 7 + cap)
