@@ -1,21 +1,25 @@
 // Expert GEMMs for many rows per expert: LDS-tiled scaled FP4 x FP8 MFMA.
 //
 // A workgroup computes a tile of BN weight rows x BM dispatched rows of one
-// expert.  Its four wavefronts form a 2 x 2 grid: wavefront (wn, wm) owns
-// weight rows [wn BN/2, (wn+1) BN/2) of the tile (BN/32 16-row MFMA groups)
-// and dispatched rows [wm BM/2, (wm+1) BM/2).  The operands of KU K steps of
-// 128 (one stage) are brought into LDS with direct global-to-LDS loads,
-// double-buffered: the loads of stage u+1 are in flight while stage u is
-// computed.  Each workgroup fits in half a CU's LDS and registers, so two
-// independent workgroups share every CU: while one waits at its barrier or
-// on memory, the other's MFMAs run (measured faster than one workgroup of
-// eight wavefronts, whose halves wait at the same barriers, and than
-// three-stage rings at one workgroup per CU).
+// expert.  Its NW wavefronts (four, or eight for the 256-row GEMM1 tile) form
+// a 2 x NW/2 grid: wavefront (wn, wm) owns weight rows [wn BN/2, (wn+1) BN/2)
+// of the tile (BN/32 16-row MFMA groups) and BM/(NW/2) dispatched rows from
+// wm BM/(NW/2).  The operands of KU K steps of 128 (one stage) are brought
+// into LDS with direct global-to-LDS loads, double-buffered: the loads of
+// stage u+1 are in flight while stage u is computed.  A four-wavefront
+// workgroup fits in half a CU's LDS and registers, so two independent
+// workgroups share every CU: while one waits at its barrier or on memory,
+// the other's MFMAs run (measured faster than one workgroup of eight
+// wavefronts over the same rows, whose halves wait at the same barriers, and
+// than three-stage rings at one workgroup per CU).
 //
 // Tiles: 128-row tiles (MFMA-bound prefill sizes) take 256 weight rows (or
 // 128 when 256 would leave fewer than three rounds of items) and one K step
 // per stage; 64-row tiles (HBM-bound) take 128 weight rows and two K steps
 // per stage, so every weight row is read 128 contiguous bytes at a time.
+// GEMM1 past 512 expected rows per expert takes 256 x 256 tiles on eight
+// wavefronts, one workgroup per CU: the two 128-row halves share one weight
+// stage, so a CU moves 48 KB per K step for 256 MFMAs instead of 64 KB.
 //
 // GEMM1 tile: BN/2 intermediate columns.  Each wavefront holds BN/4 of them
 // as BN/64 gate groups and the matching up groups, so the clamped SwiGLU and
@@ -127,7 +131,7 @@ struct TiledArgs {
 // reads h through the XCD's L2, past the CU's L1 (the persistent layer,
 // where GEMM1 items of the same launch and XCD wrote it).  Ends with the
 // workgroup's LDS still in use: the caller synchronises before the next item.
-template <bool kGemm1, int BM, int BN, int KU, bool kL2>
+template <bool kGemm1, int BM, int BN, int KU, bool kL2, int NW = 4>
 __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                                            const int *prefix, int *arow, uint8_t *lds, int q,
                                            int nt)
@@ -148,8 +152,11 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
     // activation rows; 128-row tiles reuse each weight tile across row chunks
     constexpr bool kStreamW = BM == 64;
     constexpr int GW = BN / 32;             // 16-row weight groups per wavefront
-    constexpr int WI = BN * KU / 64;        // weight load instructions per wavefront and stage
-    constexpr int TB = BM / 32;             // 16-row activation blocks per wavefront
+    constexpr int NTH = NW * 64;            // threads
+    constexpr int NWM = NW / 2;             // wavefronts along the rows
+    constexpr int WI = BN * KU / (16 * NW); // weight load instructions per wavefront and stage
+    constexpr int TBL = BM / (8 * NW);      // activation load instructions per wavefront and K step
+    constexpr int TB = BM / (16 * NWM);     // 16-row activation blocks per wavefront
     constexpr int NS = L::kStages;
     constexpr int WROW = 64 * KU;           // LDS bytes of one weight row in a stage
     constexpr int WSWZ = 4 * KU - 1;        // chunk swizzle mask of the weight rows
@@ -196,22 +203,22 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         // 64-byte ones.
         //
         // Weight instruction i brings tile rows rpi h .. rpi h + rpi - 1 with
-        // rpi = 1024 / WROW and h = wave + 4i: lane l -> row
+        // rpi = 1024 / WROW and h = wave + NW i: lane l -> row
         // rpi h + l / (WROW/16), chunk (l mod WROW/16) ^ swz.  Activation
-        // instruction i of a K step brings tile rows 8h.., h = wave + 4i:
+        // instruction i of a K step brings tile rows 8h.., h = wave + NW i:
         // lane l -> row R = 8h + (l >> 3), chunk (l & 7) ^ swz.
         constexpr int LPR = WROW / 16;      // lanes per weight row
-        uint32_t woff[WI], xoff[TB];
-        bool xrow_used[TB];   // activation rows past nrows are not loaded
+        uint32_t woff[WI], xoff[TBL];
+        bool xrow_used[TBL];   // activation rows past nrows are not loaded
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
-            const int r = (64 / LPR) * (wave + 4 * i) + lane / LPR;
+            const int r = (64 / LPR) * (wave + NW * i) + lane / LPR;
             const int cc = (lane % LPR) ^ ((r >> 1) & WSWZ);
             woff[i] = wrow_of(r) * (uint32_t)(KT / 2) + 16u * (uint32_t)cc;
         }
 #pragma unroll
-        for (int i = 0; i < TB; ++i) {
-            const int h = wave + 4 * i, R = 8 * h + (lane >> 3);
+        for (int i = 0; i < TBL; ++i) {
+            const int h = wave + NW * i, R = 8 * h + (lane >> 3);
             const int cc = (lane & 7) ^ ((R >> 1) & 7);
             xoff[i] = (uint32_t)arow[R] * (uint32_t)KT + 16u * (uint32_t)cc;
             xrow_used[i] = R < nrows;
@@ -243,23 +250,23 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             if (nk == KU) {
 #pragma unroll
                 for (int i = 0; i < WI; ++i)
-                    g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+                    g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + (uint32_t)(NW * 1024) * i);
             } else {
                 // one K step of a 128-byte row layout: only chunks 0..3
                 // (positions c ^ swz) are read; load them, skip the rest
 #pragma unroll
                 for (int i = 0; i < WI; ++i)
-                    if (((lane % LPR) ^ ((((64 / LPR) * (wave + 4 * i) + lane / LPR) >> 1) & WSWZ)) < 4)
-                        g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + 4096u * i);
+                    if (((lane % LPR) ^ ((((64 / LPR) * (wave + NW * i) + lane / LPR) >> 1) & WSWZ)) < 4)
+                        g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + (uint32_t)(NW * 1024) * i);
             }
 #pragma unroll
             for (int kk = 0; kk < KU; ++kk)
                 if (kk < nk) {
 #pragma unroll
-                    for (int i = 0; i < TB; ++i)
+                    for (int i = 0; i < TBL; ++i)
                         if (xrow_used[i])
                             g2lds<16, false, kL2>(act, xoff[i] + (uint32_t)(ks0 + kk) * 128u,
-                                      lds_x + st + (uint32_t)(kk * BM * 128) + 4096u * i);
+                                      lds_x + st + (uint32_t)(kk * BM * 128) + (uint32_t)(NW * 1024) * i);
                 }
             if ((ks0 & 3) == 0) {
                 const int grp = ks0 >> 2;
@@ -283,7 +290,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         // per-lane LDS offsets of the fragment reads (see the layout above);
         // K step kk of a stage reads chunks 4 kk + kq of the weight rows
         const int arow0 = wn * GW * 16 * WROW + WROW * i16;
-        const int xrow = wm * (BM / 2) + i16;
+        const int xrow = wm * (BM / NWM) + i16;
         const int bfrag_lo = L::kW + 128 * xrow + 16 * (kq ^ ((i16 >> 1) & 7));
         const int bfrag_hi = L::kW + 128 * xrow + 16 * ((kq + 4) ^ ((i16 >> 1) & 7));
         const int wexp = NS * L::kStage + 16 * (wn * (BN / 2) + i16) + kq;
@@ -291,7 +298,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
 
         // 16-row activation blocks of this wavefront that hold dispatched
         // rows (the MFMAs of the others would only feed discarded columns)
-        const int nlive = min(TB, max(0, (nrows - wm * (BM / 2) + 15) >> 4));
+        const int nlive = min(TB, max(0, (nrows - wm * (BM / NWM) + 15) >> 4));
 
         issue(0);
         for (int u = 0; u < U; ++u) {
@@ -336,9 +343,9 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             }
         }
 
-        // epilogue: lane holds tile row (wm*BM/2 + 16j + i16), weight rows
+        // epilogue: lane holds tile row (wm BM/NWM + 16j + i16), weight rows
         // 4kq..4kq+3 of each of its GW groups
-        if (kGemm1) {
+        if constexpr (kGemm1) {
             constexpr int CB = GW / 2;   // 16-column blocks of h per wavefront
             // the h codes go through LDS (rows of BN/2 + 16 bytes, so the
             // 4-byte writes of a wavefront hit distinct banks), then out as
@@ -349,7 +356,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
-                const int m = wm * (BM / 2) + 16 * j + i16;
+                const int m = wm * (BM / NWM) + 16 * j + i16;
                 float hv[CB][4];
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
@@ -382,8 +389,8 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             __syncthreads();
             constexpr int PR = BN / 32;                // 16-byte pieces per row
 #pragma unroll
-            for (int p = 0; p < (BM * PR + kThreads - 1) / kThreads; ++p) {
-                const int piece = p * kThreads + tid, r = piece / PR, c = piece % PR;
+            for (int p = 0; p < (BM * PR + NTH - 1) / NTH; ++p) {
+                const int piece = p * NTH + tid, r = piece / PR, c = piece % PR;
                 if (piece < BM * PR && r < nrows)
                     *reinterpret_cast<u32x4 *>(h_out + (size_t)(row0 + r) * (size_t)I +
                                                (size_t)nt * (BN / 2) + 16 * c) =
@@ -399,7 +406,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
-                const int m = wm * (BM / 2) + 16 * j + i16;
+                const int m = wm * (BM / NWM) + 16 * j + i16;
 #pragma unroll
                 for (int i = 0; i < GW; ++i)
                     *reinterpret_cast<uint2 *>(lds + m * PITCH + 2 * ((BN / 2) * wn + 16 * i + 4 * kq)) =
@@ -409,8 +416,8 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             __syncthreads();
             constexpr int PR = BN / 8;                 // 16-byte pieces per row
 #pragma unroll
-            for (int p = 0; p < BM * PR / kThreads; ++p) {
-                const int piece = p * kThreads + tid, r = piece / PR, c = piece % PR;
+            for (int p = 0; p < BM * PR / NTH; ++p) {
+                const int piece = p * NTH + tid, r = piece / PR, c = piece % PR;
                 if (r < nrows)
                     *reinterpret_cast<u32x4 *>(y_out + (size_t)(row0 + r) * (size_t)H +
                                                (size_t)nt * BN + 8 * c) = lds_read16(lds + r * PITCH + 16 * c);
@@ -510,26 +517,26 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(int32_t *p, int n)
         p[i] = 0;
 }
 
-template <bool kGemm1, int BM, int BN, int KU>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <bool kGemm1, int BM, int BN, int KU, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_tiled_kernel(Shape s, TiledArgs g)
 {
     __shared__ TileShared<BM, BN, KU> sh;
     const int NT = kGemm1 ? s.I / (BN / 2) : s.H / BN;
-    const int nchunks = plan_chunks(s, g.counts, BM, sh.prefix);
+    const int nchunks = plan_chunks<NW * 64>(s, g.counts, BM, sh.prefix);
     const long items = (long)nchunks * NT;
     for (long item = blockIdx.x; item < items; item += gridDim.x) {
         const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
-        tiled_item<kGemm1, BM, BN, KU, false>(s, g, sh.prefix, sh.arow, sh.ring, q, nt);
+        tiled_item<kGemm1, BM, BN, KU, false, NW>(s, g, sh.prefix, sh.arow, sh.ring, q, nt);
         __syncthreads();
     }
 }
 
 template <typename KernelT>
-int tiled_grid(KernelT kernel, long upper_items)
+int tiled_grid(KernelT kernel, long upper_items, int threads = kThreads)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) !=
             hipSuccess ||
         per_cu < 1)
         per_cu = 1;
@@ -549,7 +556,12 @@ long tile_upper_bound(const moe_shape &s, int bm)
 
 } // namespace
 
-// 64-row tiles up to 96 expected rows per expert.  An expert past 64 rows
+// 64-row tiles up to 96 expected rows per expert.  GEMM1 takes 256-row tiles
+// from 512 (measured in the layer at 65,536 tokens: GEMM1 -8% with Zipf
+// routing, +4 to +6% with uniform routing or one hot expert, where GEMM2
+// then runs 5-6% faster; the layer -5%, +0.5%, -0.5%).  GEMM2's y tile of
+// 256 rows does not fit the stage ring, and a two-pass epilogue spilled
+// registers (+40%).  An expert past 64 rows
 // streams its weights twice (64-row tiles read them non-temporally), yet on
 // the Flash shape with a tenth of the slots -1 (57 rows per expert on
 // average) the 64-row tiles still win, 334 against 360 us for GEMM1; with no
@@ -587,8 +599,11 @@ struct TiledConfig {
     int bm, bn, ku;
 };
 
-// The tile shapes compiled for both GEMMs (a tuned table may name only these).
-constexpr TiledConfig kTiledShapes[] = {{64, 128, 2}, {64, 256, 1}, {128, 128, 1}, {128, 256, 1}};
+// The tile shapes compiled for both GEMMs, then for GEMM1 only (a tuned table
+// may name only these).
+constexpr TiledConfig kTiledShapes[] = {{64, 128, 2}, {64, 256, 1}, {128, 128, 1}, {128, 256, 1},
+                                        {256, 256, 1}};
+constexpr int kBothGemmShapes = 4;
 
 // A tuned table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE tuning
 // for gfx950", tuning: one config per shape and token bucket, a count between
@@ -628,6 +643,9 @@ TiledConfig tiled_config(const moe_shape &s, bool gemm1)
     const int bm = tiled_bm(s), bn = tiled_bn(s, gemm1);
     if (bm == 64)
         return {64, 128, 2};
+    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+    if (gemm1 && bn == 256 && per_expert >= 512.0)
+        return {256, 256, 1};
     return {bm, bn, 1};
 }
 
@@ -637,10 +655,12 @@ hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *
                         const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, uint16_t *y,
                         hipStream_t st)
 {
-    auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU>;
+    // eight wavefronts for the 256-row tile, four otherwise
+    constexpr int NW = BM == 256 ? 8 : 4;
+    auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU, NW>;
     const long nt = kGemm1 ? sh.I / (BN / 2) : sh.H / BN;
-    const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt);
-    k<<<grid, kThreads, 0, st>>>(to_dev(sh),
+    const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt, NW * 64);
+    k<<<grid, NW * 64, 0, st>>>(to_dev(sh),
                                  TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs, y});
     return hipGetLastError();
 }
@@ -659,6 +679,9 @@ hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8
     MOE_TILED_CASE(64, 128, 2)
     MOE_TILED_CASE(64, 256, 1)
     MOE_TILED_CASE(128, 128, 1)
+    if constexpr (kGemm1) {
+        MOE_TILED_CASE(256, 256, 1)
+    }
 #undef MOE_TILED_CASE
     return launch_tiled<kGemm1, 128, 256, 1>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
                                              hs, y, st);
@@ -690,8 +713,11 @@ int set_tile_table(const moe_tile_entry *entries, int n)
     for (int i = 0; i < n; ++i) {
         const moe_tile_entry &e = entries[i];
         bool known = false;
-        for (const TiledConfig &c : kTiledShapes)
-            known |= c.bm == e.bm && c.bn == e.bn && c.ku == e.ku;
+        const int nshapes = e.gemm == 1 ? (int)(sizeof(kTiledShapes) / sizeof(kTiledShapes[0]))
+                                        : kBothGemmShapes;
+        for (int k = 0; k < nshapes; ++k)
+            known |= kTiledShapes[k].bm == e.bm && kTiledShapes[k].bn == e.bn &&
+                     kTiledShapes[k].ku == e.ku;
         if (!known || (e.gemm != 1 && e.gemm != 2) || e.max_tokens < 0)
             return MOE_EINVAL;
     }
@@ -713,6 +739,17 @@ bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
     return true;
 }
 
+// The tile config of the persistent layer: that of the launches, with a
+// 256-row GEMM1 tile run as 128 rows (the persistent kernels are built for
+// four wavefronts and two workgroups per CU).
+static TiledConfig persistent_config(const moe_shape &sh, bool gemm1)
+{
+    TiledConfig c = tiled_config(sh, gemm1);
+    if (c.bm == 256)
+        c.bm = 128;
+    return c;
+}
+
 // The persistent layer takes the tiled GEMMs when both use the same row
 // tile: 128 rows with one K step per stage (any weight tile widths) or 64
 // rows with two K steps and 128 weight rows; on a device whose XCDs it can
@@ -721,7 +758,7 @@ bool persistent_supported(const moe_shape &sh)
 {
     if (sh.H < 512 || sh.I < 512 || xcd_count() == 0)
         return false;
-    const TiledConfig a = tiled_config(sh, true), b = tiled_config(sh, false);
+    const TiledConfig a = persistent_config(sh, true), b = persistent_config(sh, false);
     if (a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1)
         return true;
     return a.bm == 64 && b.bm == 64 && a.ku == 2 && b.ku == 2 && a.bn == 128 && b.bn == 128;
@@ -740,8 +777,8 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
     fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
     const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr};
     const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y};
-    const TiledConfig c1 = tiled_config(sh, true);
-    const int bn1 = c1.bn, bn2 = tiled_config(sh, false).bn;
+    const TiledConfig c1 = persistent_config(sh, true);
+    const int bn1 = c1.bn, bn2 = persistent_config(sh, false).bn;
     const int nq = xcd_count();
     // workgroup b runs on XCD b mod nq: a grid of nq or more workgroups puts
     // at least one on every XCD, so every queue is served

@@ -155,11 +155,17 @@ def test_tile_table(lib):
         {"bm": 64, "bn": 128, "ku": 2}
     pre = moe.MoeShape(**{**V4, "T": 65536})
     assert moe.get_tile_config(pre, 2)["bm"] == 128
+    # GEMM1 from 512 expected rows per expert: 256 x 256 tiles (GEMM1 only)
+    assert tuple(moe.get_tile_config(pre, 1)[k] for k in ("bm", "bn", "ku")) == (256, 256, 1)
+    mid = moe.MoeShape(**{**V4, "T": 16384})                 # 256 rows per expert
+    assert tuple(moe.get_tile_config(mid, 1)[k] for k in ("bm", "bn", "ku")) == (128, 256, 1)
     base = dict(gemm=1, H=7168, I=3072, K=6, E_total=384, E_local=48)
     with pytest.raises(moe.MoeError):
         moe.set_tile_table([dict(base, max_tokens=128, bm=32, bn=128, ku=2)])
     with pytest.raises(moe.MoeError):
         moe.set_tile_table([dict(base, gemm=3, max_tokens=128, bm=64, bn=128, ku=2)])
+    with pytest.raises(moe.MoeError):
+        moe.set_tile_table([dict(base, gemm=2, max_tokens=128, bm=256, bn=256, ku=1)])
     assert lib.moe_set_tile_table(None, -1) == -1
     try:
         moe.set_tile_table([dict(base, max_tokens=256, bm=128, bn=128, ku=1),
@@ -171,7 +177,7 @@ def test_tile_table(lib):
         assert t(256, 1) == (128, 128, 1)        # on its bound
         assert t(257, 1) == (64, 256, 1)         # between buckets: the larger one
         assert t(4096, 1) == (64, 128, 2)        # past every bucket: the rule
-        assert t(65536, 1) == (128, 256, 1)
+        assert t(65536, 1) == (256, 256, 1)
         assert t(128, 2) == (128, 256, 1)
         other = moe.MoeShape(**{**V4, "E_local": 96})
         assert moe.get_tile_config(other, 1)["bm"] == 64   # another shape: the rule
