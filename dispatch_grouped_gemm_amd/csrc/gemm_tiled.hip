@@ -17,6 +17,10 @@
 // 128 when 256 would leave fewer than three rounds of items) and one K step
 // per stage; 64-row tiles (HBM-bound) take 128 weight rows and two K steps
 // per stage, so every weight row is read 128 contiguous bytes at a time.
+// Up to 16 expected rows per expert (decode) 32-row tiles keep three such
+// stages in LDS at two workgroups per CU, two of them in flight: a stage's
+// weight loads go out last, and the wait before a stage leaves the next
+// stage's weight loads outstanding.
 // GEMM1 past 512 expected rows per expert takes 256 x 256 tiles on eight
 // wavefronts, one workgroup per CU: the two 128-row halves share one weight
 // stage, so a CU moves 48 KB per K step for 256 MFMAs instead of 64 KB.
@@ -38,15 +42,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-// Tile of BN weight rows (256 or 128) x BM dispatched rows (64 or 128); one
-// LDS stage holds KU K steps of 128 (1 or 2).
+// Tile of BN weight rows (256 or 128) x BM dispatched rows (32 to 256); one
+// LDS stage holds KU K steps of 128 (1 or 2); 32-row tiles keep three stages.
 template <int BM, int BN, int KU>
 struct TileLds {
     static_assert(KU == 1 || KU == 2, "one or two K steps per stage");
     static constexpr int kW = BN * 64 * KU;    // FP4 weight tile, one stage
     static constexpr int kX = BM * 128 * KU;   // FP8 activation rows, one stage
     static constexpr int kStage = kW + kX;
-    static constexpr int kStages = 2;          // stages resident in LDS
+    static constexpr int kStages = BM == 32 ? 3 : 2;   // stages resident in LDS
     static constexpr int kWE = BN * 16;        // weight exponents of four K steps
     static constexpr int kXE = BM * 16;        // activation exponents of four K steps
     static constexpr int kExp = kWE + kXE;
@@ -150,7 +154,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
     // 64-row tiles: an expert's weights are read by one row chunk (as a
     // rule), so they stream through the L2 without displacing the
     // activation rows; 128-row tiles reuse each weight tile across row chunks
-    constexpr bool kStreamW = BM == 64;
+    constexpr bool kStreamW = BM <= 64;
     constexpr int GW = BN / 32;             // 16-row weight groups per wavefront
     constexpr int NTH = NW * 64;            // threads
     constexpr int NWM = NW / 2;             // wavefronts along the rows
@@ -229,9 +233,10 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         // The last group of a row is read from 16 bytes before the row's
         // end, so no read passes it (KS >= 4).
         const int we_wave = wave % (BN / 64);
-        const int xe_wave = wave % (BM / 64);
+        constexpr int XEW = BM >= 64 ? BM / 64 : 1;   // wavefronts loading activation exponents
+        const int xe_wave = wave % XEW;
         const uint32_t weoff = wrow_of(64 * we_wave + lane) * (uint32_t)(KT / 32);
-        const uint32_t xeoff = (uint32_t)arow[64 * xe_wave + lane] * (uint32_t)(KT / 32);
+        const uint32_t xeoff = (uint32_t)arow[min(64 * xe_wave + lane, BM - 1)] * (uint32_t)(KT / 32);
         const bool xe_used = 64 * xe_wave + lane < nrows;
         auto ebase = [&](int grp) -> int { return min(16 * grp, KT / 32 - 16); };
 
@@ -243,7 +248,8 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         const uint32_t lds_xe = __builtin_amdgcn_readfirstlane(lds_e + L::kWE + 1024u * xe_wave);
         // stage u: K steps KU u .. (the last stage of an odd KS with KU = 2
         // holds one step; its other half is neither loaded nor read)
-        auto issue = [&](int u) {
+        // the weight loads of a stage, then its activation rows and exponents
+        auto issue_w = [&](int u) {
             const uint32_t st = (uint32_t)((u % NS) * L::kStage);
             const int ks0 = KU * u;
             const int nk = min(KU, KS - ks0);
@@ -259,6 +265,11 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                     if (((lane % LPR) ^ ((((64 / LPR) * (wave + NW * i) + lane / LPR) >> 1) & WSWZ)) < 4)
                         g2lds<16, kStreamW>(w, woff[i] + (uint32_t)ks0 * 64u, lds_w + st + (uint32_t)(NW * 1024) * i);
             }
+        };
+        auto issue_x = [&](int u) {
+            const uint32_t st = (uint32_t)((u % NS) * L::kStage);
+            const int ks0 = KU * u;
+            const int nk = min(KU, KS - ks0);
 #pragma unroll
             for (int kk = 0; kk < KU; ++kk)
                 if (kk < nk) {
@@ -275,8 +286,19 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                 // one wavefront per 64-row block (no two load the same rows)
                 if (wave < BN / 64)
                     g2lds<16>(ws, weoff + eb, lds_we + es);
-                if (wave < BM / 64 && xe_used)
+                if (wave < XEW && xe_used)
                     g2lds<16, false, kL2>(act_s, xeoff + eb, lds_xe + es);
+            }
+        };
+        // three stages: a stage's weight loads go last, so that waiting for
+        // all but WI loads leaves the next stage's weight stream in flight
+        auto issue = [&](int u) {
+            if (NS == 3) {
+                issue_x(u);
+                issue_w(u);
+            } else {
+                issue_w(u);
+                issue_x(u);
             }
         };
 
@@ -301,14 +323,32 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         const int nlive = min(TB, max(0, (nrows - wm * (BM / NWM) + 15) >> 4));
 
         issue(0);
+        if (NS == 3 && U > 1)
+            issue(1);
         for (int u = 0; u < U; ++u) {
-            // this wavefront's loads of stage u are the only ones outstanding;
-            // after the barrier every wavefront's are done and nobody reads
-            // the other stage any more, so the next stage's loads go there
-            wait_vmcnt<0>();
-            raw_barrier();
-            if (u + 1 < U)
-                issue(u + 1);
+            if (NS == 3) {
+                // stage u + 1 (issued last) may keep its WI weight loads in
+                // flight when it is a whole stage; the first stage of an item
+                // waits for everything (the previous item's stores included)
+                if (u > 0 && u + 1 < U && KU * (u + 2) <= KS)
+                    wait_vmcnt<WI>();
+                else
+                    wait_vmcnt<0>();
+                // every wavefront's loads of stage u are done and every
+                // wavefront is done with stage u - 1, whose buffer u + 2 takes
+                raw_barrier();
+                if (u + 2 < U)
+                    issue(u + 2);
+            } else {
+                // this wavefront's loads of stage u are the only ones
+                // outstanding; after the barrier every wavefront's are done
+                // and nobody reads the other stage any more, so the next
+                // stage's loads go there
+                wait_vmcnt<0>();
+                raw_barrier();
+                if (u + 1 < U)
+                    issue(u + 1);
+            }
             const uint8_t *st = lds + (u % NS) * L::kStage;
 #pragma unroll
             for (int kk = 0; kk < KU; ++kk) {
@@ -556,21 +596,32 @@ long tile_upper_bound(const moe_shape &s, int bm)
 
 } // namespace
 
-// 64-row tiles up to 96 expected rows per expert.  GEMM1 takes 256-row tiles
-// from 512 (measured in the layer at 65,536 tokens: GEMM1 -8% with Zipf
-// routing, +4 to +6% with uniform routing or one hot expert, where GEMM2
-// then runs 5-6% faster; the layer -5%, +0.5%, -0.5%).  GEMM2's y tile of
-// 256 rows does not fit the stage ring, and a two-pass epilogue spilled
-// registers (+40%).  An expert past 64 rows
-// streams its weights twice (64-row tiles read them non-temporally), yet on
-// the Flash shape with a tenth of the slots -1 (57 rows per expert on
-// average) the 64-row tiles still win, 334 against 360 us for GEMM1; with no
-// -1 slots (64 rows) the 128-row tiles win, 354 against 434 us.  The host
-// sees neither the -1 slots nor the skew, so shapes near the bound are left
-// to the tuned table.
+// Rows per expert the host expects: every slot routed, experts equally likely.
+static double per_expert_rows(const moe_shape &s)
+{
+    return (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+}
+
+// Row tiles by the expected rows per expert:
+// - 32-row tiles up to 16 (decode: GEMM1 and GEMM2 -5%; 1,024 tokens -3 to
+//   -7%; at 2,048 tokens and on the Flash shape, where experts pass 32 rows
+//   and stream their weights twice, +30 to +60%);
+// - 64-row tiles up to 96.  An expert past 64 rows streams its weights twice
+//   (64-row tiles read them non-temporally), yet on the Flash shape with a
+//   tenth of the slots -1 (57 rows per expert on average) the 64-row tiles
+//   still win, 334 against 360 us for GEMM1; with no -1 slots (64 rows) the
+//   128-row tiles win, 354 against 434 us;
+// - 128-row tiles above, and 256-row tiles for GEMM1 from 512 (measured in
+//   the layer at 65,536 tokens: GEMM1 -8% with Zipf routing, +4 to +6% with
+//   uniform routing or one hot expert, where GEMM2 then runs 5-6% faster; the
+//   layer -5%, +0.5%, -0.5%).  GEMM2's y tile of 256 rows does not fit the
+//   stage ring, and a two-pass epilogue spilled registers (+40%).
+// The host sees neither the -1 slots nor the skew, so shapes near the bounds
+// are left to the tuned table.  tiled_bm gives the class (64 or 128),
+// tiled_config the tile.
 int tiled_bm(const moe_shape &s)
 {
-    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+    const double per_expert = per_expert_rows(s);
     return per_expert <= 96.0 ? 64 : 128;
 }
 
@@ -581,7 +632,7 @@ namespace {
 // per CU), so the last, partly filled round costs little.
 int tiled_bn(const moe_shape &s, bool gemm1)
 {
-    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+    const double per_expert = per_expert_rows(s);
     const int bm = tiled_bm(s);
     const double tiles = (double)s.E_local * (double)(long)((per_expert + bm - 1) / bm);
     const double nt256 = gemm1 ? s.I / 128 : s.H / 256;
@@ -601,9 +652,9 @@ struct TiledConfig {
 
 // The tile shapes compiled for both GEMMs, then for GEMM1 only (a tuned table
 // may name only these).
-constexpr TiledConfig kTiledShapes[] = {{64, 128, 2}, {64, 256, 1}, {128, 128, 1}, {128, 256, 1},
-                                        {256, 256, 1}};
-constexpr int kBothGemmShapes = 4;
+constexpr TiledConfig kTiledShapes[] = {{32, 128, 2},  {64, 128, 2},  {64, 256, 1},
+                                        {128, 128, 1}, {128, 256, 1}, {256, 256, 1}};
+constexpr int kBothGemmShapes = 5;
 
 // A tuned table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE tuning
 // for gfx950", tuning: one config per shape and token bucket, a count between
@@ -641,9 +692,9 @@ TiledConfig tiled_config(const moe_shape &s, bool gemm1)
     if (table_lookup(s, gemm1, &c))
         return c;
     const int bm = tiled_bm(s), bn = tiled_bn(s, gemm1);
+    const double per_expert = per_expert_rows(s);
     if (bm == 64)
-        return {64, 128, 2};
-    const double per_expert = (double)s.T * s.K / (double)(s.E_total > 0 ? s.E_total : 1);
+        return per_expert <= 16.0 ? TiledConfig{32, 128, 2} : TiledConfig{64, 128, 2};
     if (gemm1 && bn == 256 && per_expert >= 512.0)
         return {256, 256, 1};
     return {bm, bn, 1};
@@ -676,6 +727,7 @@ hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8
     if (c.bm == BM && c.bn == BN && c.ku == KU)                                                   \
         return launch_tiled<kGemm1, BM, BN, KU>(sh, act, act_s, counts, offsets, row_route, w, ws, \
                                                 h, hs, y, st);
+    MOE_TILED_CASE(32, 128, 2)
     MOE_TILED_CASE(64, 128, 2)
     MOE_TILED_CASE(64, 256, 1)
     MOE_TILED_CASE(128, 128, 1)
@@ -747,6 +799,8 @@ static TiledConfig persistent_config(const moe_shape &sh, bool gemm1)
     TiledConfig c = tiled_config(sh, gemm1);
     if (c.bm == 256)
         c.bm = 128;
+    if (c.bm == 32)
+        c.bm = 64;
     return c;
 }
 

@@ -29,7 +29,7 @@ import torch
 
 import dispatch_grouped_gemm_amd as moe
 
-TILES = [(64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1)]
+TILES = [(32, 128, 2), (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1)]
 TILES_GEMM1 = TILES + [(256, 256, 1)]   # eight wavefronts, GEMM1 only
 
 

@@ -150,9 +150,11 @@ def test_tile_table(lib):
     larger), and clearing.  Host logic only."""
     small = moe.MoeShape(**{**V4, "H": 256})
     assert moe.get_tile_config(small, 1) is None            # register-streaming kernels
-    dec = moe.MoeShape(**V4)                                 # 128 tokens: 64-row tiles
+    dec = moe.MoeShape(**V4)                                 # 128 tokens: 32-row tiles
     assert {k: moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")} == \
-        {"bm": 64, "bn": 128, "ku": 2}
+        {"bm": 32, "bn": 128, "ku": 2}
+    t2k = moe.MoeShape(**{**V4, "T": 2048})                  # 32 rows per expert: 64-row tiles
+    assert tuple(moe.get_tile_config(t2k, 2)[k] for k in ("bm", "bn", "ku")) == (64, 128, 2)
     pre = moe.MoeShape(**{**V4, "T": 65536})
     assert moe.get_tile_config(pre, 2)["bm"] == 128
     # GEMM1 from 512 expected rows per expert: 256 x 256 tiles (GEMM1 only)
@@ -161,7 +163,7 @@ def test_tile_table(lib):
     assert tuple(moe.get_tile_config(mid, 1)[k] for k in ("bm", "bn", "ku")) == (128, 256, 1)
     base = dict(gemm=1, H=7168, I=3072, K=6, E_total=384, E_local=48)
     with pytest.raises(moe.MoeError):
-        moe.set_tile_table([dict(base, max_tokens=128, bm=32, bn=128, ku=2)])
+        moe.set_tile_table([dict(base, max_tokens=128, bm=16, bn=128, ku=2)])
     with pytest.raises(moe.MoeError):
         moe.set_tile_table([dict(base, gemm=3, max_tokens=128, bm=64, bn=128, ku=2)])
     with pytest.raises(moe.MoeError):
@@ -180,7 +182,7 @@ def test_tile_table(lib):
         assert t(65536, 1) == (256, 256, 1)
         assert t(128, 2) == (128, 256, 1)
         other = moe.MoeShape(**{**V4, "E_local": 96})
-        assert moe.get_tile_config(other, 1)["bm"] == 64   # another shape: the rule
+        assert moe.get_tile_config(other, 1)["bm"] == 32   # another shape: the rule
     finally:
         moe.set_tile_table([])
-    assert tuple(moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")) == (64, 128, 2)
+    assert tuple(moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")) == (32, 128, 2)

@@ -11,7 +11,7 @@ from gpu_util import cached_case, host, run_forward, say, shape_of, upload
 
 pytestmark = pytest.mark.gpu
 
-TILES = [(64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1)]
+TILES = [(32, 128, 2), (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1)]
 GEMM1_ONLY = [(256, 256, 1)]   # eight wavefronts; GEMM2 keeps the rule's tile
 
 
