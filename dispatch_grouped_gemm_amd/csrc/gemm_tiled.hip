@@ -1,7 +1,7 @@
 // Expert GEMMs for many rows per expert: LDS-tiled scaled FP4 x FP8 MFMA.
 //
 // A workgroup computes a tile of BN weight rows x BM dispatched rows of one
-// expert.  Its NW wavefronts (four, or eight for the 256-row GEMM1 tile) form
+// expert.  Its NW wavefronts (four, or eight for the 256-row tiles) form
 // a 2 x NW/2 grid: wavefront (wn, wm) owns weight rows [wn BN/2, (wn+1) BN/2)
 // of the tile (BN/32 16-row MFMA groups) and BM/(NW/2) dispatched rows from
 // wm BM/(NW/2).  The operands of KU K steps of 128 (one stage) are brought
@@ -55,6 +55,11 @@ struct TileLds {
     static constexpr int kXE = BM * 16;        // activation exponents of four K steps
     static constexpr int kExp = kWE + kXE;
     static constexpr int kExpSlots = 2;
+    // the stage ring, grown where the bf16 y tile of a 256-row tile needs
+    // more (that tile runs one workgroup per CU)
+    static constexpr int kPipe = kStages * kStage + kExpSlots * kExp;
+    static constexpr int kYTile = BM * (BN * 2 + 16);
+    static constexpr int kRing = BM == 256 && kYTile > kPipe ? kYTile : kPipe;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -391,7 +396,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             // 4-byte writes of a wavefront hit distinct banks), then out as
             // whole 16-byte pieces of rows
             constexpr int HP = BN / 2 + 16;
-            static_assert(BM * HP <= L::kStages * L::kStage + L::kExpSlots * L::kExp,
+            static_assert(BM * HP <= L::kRing,
                           "h tile fits the stage ring");
             __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
@@ -441,7 +446,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             // fragment writes of a half-wavefront hit distinct banks), then
             // out as whole 16-byte pieces of rows, 32 lanes to a 512-byte row
             constexpr int PITCH = BN * 2 + 16;
-            static_assert(BM * PITCH <= L::kStages * L::kStage + L::kExpSlots * L::kExp,
+            static_assert(BM * PITCH <= L::kRing,
                           "y tile fits the stage ring");
             __syncthreads();   // every wavefront is done with the stage ring
 #pragma unroll
@@ -470,7 +475,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
 template <int BM, int BN, int KU>
 struct TileShared {
     using L = TileLds<BM, BN, KU>;
-    __align__(16) uint8_t ring[L::kStages * L::kStage + L::kExpSlots * L::kExp];
+    __align__(16) uint8_t ring[L::kRing];
     int prefix[kMaxLocalExperts + 1];
     int arow[BM];
 };
@@ -614,8 +619,9 @@ static double per_expert_rows(const moe_shape &s)
 // - 128-row tiles above, and 256-row tiles for GEMM1 from 512 (measured in
 //   the layer at 65,536 tokens: GEMM1 -8% with Zipf routing, +4 to +6% with
 //   uniform routing or one hot expert, where GEMM2 then runs 5-6% faster; the
-//   layer -5%, +0.5%, -0.5%).  GEMM2's y tile of 256 rows does not fit the
-//   stage ring, and a two-pass epilogue spilled registers (+40%).
+//   layer -5%, +0.5%, -0.5%).  GEMM2 keeps 128-row tiles: its 256-row tile
+//   (ring grown to the 135 KB y tile) took the layer -4% with Zipf routing
+//   but +1.5% with uniform routing; the tuned table can name it.
 // The host sees neither the -1 slots nor the skew, so shapes near the bounds
 // are left to the tuned table.  tiled_bm gives the class (64 or 128),
 // tiled_config the tile.
@@ -650,11 +656,9 @@ struct TiledConfig {
     int bm, bn, ku;
 };
 
-// The tile shapes compiled for both GEMMs, then for GEMM1 only (a tuned table
-// may name only these).
+// The tile shapes compiled for both GEMMs (a tuned table may name only these).
 constexpr TiledConfig kTiledShapes[] = {{32, 128, 2},  {64, 128, 2},  {64, 256, 1},
                                         {128, 128, 1}, {128, 256, 1}, {256, 256, 1}};
-constexpr int kBothGemmShapes = 5;
 
 // A tuned table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE tuning
 // for gfx950", tuning: one config per shape and token bucket, a count between
@@ -731,9 +735,7 @@ hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8
     MOE_TILED_CASE(64, 128, 2)
     MOE_TILED_CASE(64, 256, 1)
     MOE_TILED_CASE(128, 128, 1)
-    if constexpr (kGemm1) {
-        MOE_TILED_CASE(256, 256, 1)
-    }
+    MOE_TILED_CASE(256, 256, 1)
 #undef MOE_TILED_CASE
     return launch_tiled<kGemm1, 128, 256, 1>(sh, act, act_s, counts, offsets, row_route, w, ws, h,
                                              hs, y, st);
@@ -765,11 +767,8 @@ int set_tile_table(const moe_tile_entry *entries, int n)
     for (int i = 0; i < n; ++i) {
         const moe_tile_entry &e = entries[i];
         bool known = false;
-        const int nshapes = e.gemm == 1 ? (int)(sizeof(kTiledShapes) / sizeof(kTiledShapes[0]))
-                                        : kBothGemmShapes;
-        for (int k = 0; k < nshapes; ++k)
-            known |= kTiledShapes[k].bm == e.bm && kTiledShapes[k].bn == e.bn &&
-                     kTiledShapes[k].ku == e.ku;
+        for (const TiledConfig &c : kTiledShapes)
+            known |= c.bm == e.bm && c.bn == e.bn && c.ku == e.ku;
         if (!known || (e.gemm != 1 && e.gemm != 2) || e.max_tokens < 0)
             return MOE_EINVAL;
     }

@@ -29,8 +29,7 @@ import torch
 
 import dispatch_grouped_gemm_amd as moe
 
-TILES = [(32, 128, 2), (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1)]
-TILES_GEMM1 = TILES + [(256, 256, 1)]   # eight wavefronts, GEMM1 only
+TILES = [(32, 128, 2), (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1), (256, 256, 1)]
 
 
 def parse_shape(text: str) -> dict:
@@ -110,7 +109,7 @@ def tune_bucket(base: dict, T: int, mode: int, capacity: int, iters: int, dev,
             run(shape, d, inp, 2, ref)
         torch.cuda.synchronize()
         best = None
-        for bm, bn, ku in (TILES_GEMM1 if gemm == 1 else TILES):
+        for bm, bn, ku in TILES:
             e = dict(gemm=gemm, H=shape.H, I=shape.I, K=shape.K, E_total=shape.E_total,
                      E_local=shape.E_local, max_tokens=T, bm=bm, bn=bn, ku=ku)
             moe.set_tile_table([e])

@@ -157,7 +157,7 @@ def test_tile_table(lib):
     assert tuple(moe.get_tile_config(t2k, 2)[k] for k in ("bm", "bn", "ku")) == (64, 128, 2)
     pre = moe.MoeShape(**{**V4, "T": 65536})
     assert moe.get_tile_config(pre, 2)["bm"] == 128
-    # GEMM1 from 512 expected rows per expert: 256 x 256 tiles (GEMM1 only)
+    # GEMM1 from 512 expected rows per expert: 256 x 256 tiles (GEMM2 by the table only)
     assert tuple(moe.get_tile_config(pre, 1)[k] for k in ("bm", "bn", "ku")) == (256, 256, 1)
     mid = moe.MoeShape(**{**V4, "T": 16384})                 # 256 rows per expert
     assert tuple(moe.get_tile_config(mid, 1)[k] for k in ("bm", "bn", "ku")) == (128, 256, 1)
@@ -166,8 +166,6 @@ def test_tile_table(lib):
         moe.set_tile_table([dict(base, max_tokens=128, bm=16, bn=128, ku=2)])
     with pytest.raises(moe.MoeError):
         moe.set_tile_table([dict(base, gemm=3, max_tokens=128, bm=64, bn=128, ku=2)])
-    with pytest.raises(moe.MoeError):
-        moe.set_tile_table([dict(base, gemm=2, max_tokens=128, bm=256, bn=256, ku=1)])
     assert lib.moe_set_tile_table(None, -1) == -1
     try:
         moe.set_tile_table([dict(base, max_tokens=256, bm=128, bn=128, ku=1),
