@@ -790,9 +790,10 @@ bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
     return true;
 }
 
-// The tile config of the persistent layer: that of the launches, with a
-// 256-row GEMM1 tile run as 128 rows (the persistent kernels are built for
-// four wavefronts and two workgroups per CU).
+// The tile config of the persistent layer: that of the launches, with
+// 256-row tiles run as 128 rows and 32-row tiles as 64 rows (the persistent
+// kernels are built for four wavefronts, two LDS stages and two workgroups
+// per CU).
 static TiledConfig persistent_config(const moe_shape &sh, bool gemm1)
 {
     TiledConfig c = tiled_config(sh, gemm1);
