@@ -68,6 +68,21 @@ def test_dispatch_edges(T, mode, cap):
     check_dispatch(spec, ids, d)
 
 
+@pytest.mark.parametrize("T,mode,cap", [(1024, 0, 0), (4200, 1, 80)])
+def test_dispatch_512_experts_many_workgroups(T, mode, cap):
+    """512 local experts on the many-workgroup paths: compact (8,192 slots,
+    four histogram workgroups, the largest LDS table) and fixed-slot past
+    one workgroup's 32,768 slots (reset + claim, with overflow)."""
+    rng = np.random.default_rng(T + cap)
+    spec = synth.CaseSpec("e512", T=T, H=512, I=256, E_total=520, E_local=512, expert_begin=4,
+                          K=8, dispatch_mode=mode, capacity=cap)
+    ids = _edge_ids(rng, T, 8, 520)
+    say("dispatch e512", T, mode, cap)
+    d = run_dispatch(spec, dev(ids))
+    torch.cuda.synchronize()
+    check_dispatch(spec, ids, d)
+
+
 def test_dispatch_single_hot_expert_large():
     T, K = 9000, 6
     spec = synth.CaseSpec("hot", T=T, H=512, I=256, E_total=64, E_local=16, K=K)
