@@ -333,9 +333,10 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         for (int u = 0; u < U; ++u) {
             if (NS == 3) {
                 // stage u + 1 (issued last) may keep its WI weight loads in
-                // flight when it is a whole stage; the first stage of an item
-                // waits for everything (the previous item's stores included)
-                if (u > 0 && u + 1 < U && KU * (u + 2) <= KS)
+                // flight when it is a whole stage (vector memory operations
+                // count down in issue order, the previous item's stores
+                // included); a partial stage u + 1 waits for everything
+                if (u + 1 < U && KU * (u + 2) <= KS)
                     wait_vmcnt<WI>();
                 else
                     wait_vmcnt<0>();
