@@ -23,7 +23,13 @@ combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict_
     if (i >= (long)s.T * pieces)
         return;
     const int t = (int)(i / pieces);
-    combine_cols(s, tw, route_row, y, out, t, (int)(i - (long)t * pieces) * kCombineVec);
+    const int col = (int)(i - (long)t * pieces) * kCombineVec;
+    // a row of a multiple of 64 pieces puts every wavefront inside one token:
+    // its slots and weights are then read once per wavefront (scalar loads)
+    if ((pieces & 63) == 0)
+        combine_cols(s, tw, route_row, y, out, __builtin_amdgcn_readfirstlane(t), col);
+    else
+        combine_cols(s, tw, route_row, y, out, t, col);
 }
 
 } // namespace
