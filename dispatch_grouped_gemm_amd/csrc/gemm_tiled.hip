@@ -792,23 +792,20 @@ bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
 }
 
 // The tile config of the persistent layer: that of the launches, with
-// 256-row tiles run as 128 rows and 32-row tiles as 64 rows (the persistent
-// kernels are built for four wavefronts, two LDS stages and two workgroups
-// per CU).
+// 256-row tiles run as 128 rows (the persistent kernels are built for four
+// wavefronts and two workgroups per CU).
 static TiledConfig persistent_config(const moe_shape &sh, bool gemm1)
 {
     TiledConfig c = tiled_config(sh, gemm1);
     if (c.bm == 256)
         c.bm = 128;
-    if (c.bm == 32)
-        c.bm = 64;
     return c;
 }
 
 // The persistent layer takes the tiled GEMMs when both use the same row
-// tile: 128 rows with one K step per stage (any weight tile widths) or 64
-// rows with two K steps and 128 weight rows; on a device whose XCDs it can
-// tell apart.
+// tile: 128 rows with one K step per stage (any weight tile widths) or 32 or
+// 64 rows with two K steps and 128 weight rows; on a device whose XCDs it
+// can tell apart.
 bool persistent_supported(const moe_shape &sh)
 {
     if (sh.H < 512 || sh.I < 512 || xcd_count() == 0)
@@ -816,10 +813,11 @@ bool persistent_supported(const moe_shape &sh)
     const TiledConfig a = persistent_config(sh, true), b = persistent_config(sh, false);
     if (a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1)
         return true;
-    return a.bm == 64 && b.bm == 64 && a.ku == 2 && b.ku == 2 && a.bn == 128 && b.bn == 128;
+    return (a.bm == 32 || a.bm == 64) && b.bm == a.bm && a.ku == 2 && b.ku == 2 && a.bn == 128 &&
+           b.bn == 128;
 }
 
-int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 64); }
+int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 32); }
 
 hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
                                    const int32_t *counts, const int32_t *offsets,
@@ -842,7 +840,9 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
         const int grid = tiled_grid(k, items);
         k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, nq);
     };
-    if (c1.bm == 64)
+    if (c1.bm == 32)
+        go(layer_persistent_kernel<32, 128, 128, 2>, 32, 128, 128);
+    else if (c1.bm == 64)
         go(layer_persistent_kernel<64, 128, 128, 2>, 64, 128, 128);
     else if (bn1 == 256 && bn2 == 256)
         go(layer_persistent_kernel<128, 256, 256, 1>, 128, 256, 256);
