@@ -207,9 +207,9 @@ int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_s
  * chunk waits until all GEMM1 items of that chunk are done, and h passes
  * between them through that XCD's L2.  Same arguments, workspace and result
  * as moe_forward (the output bits are identical); MOE_ENOTSUP for shapes it
- * does not cover (it takes the 128-row tiles of the prefill sizes: H and
- * I >= 512 and enough rows per expert) and on a device whose CU count is not
- * that of 1, 2, 4 or 8 MI355X XCDs.  Calls that overlap on one workspace
+ * does not cover (H or I below 512, or a tuned table giving GEMM1 and GEMM2
+ * different row tiles) and on a device whose CU count is not that of 1, 2,
+ * 4 or 8 MI355X XCDs.  Calls that overlap on one workspace
  * race, as for moe_forward.
  */
 int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
@@ -266,11 +266,12 @@ int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *w
  * (1: GEMM1 + SwiGLU + requant, 2: GEMM2), the shape fields it applies to
  * (H, I, K, E_total, E_local exactly), the bucket's largest T, and the tile
  * of the LDS-tiled kernel: rows bm x weight rows bn, ku K steps per stage,
- * one of (64, 128, 2), (64, 256, 1), (128, 128, 1), (128, 256, 1).  A call
- * takes the entry of its GEMM and shape with the smallest max_tokens >= T;
- * with none, the built-in rule (64-row tiles up to 96 expected rows per
- * expert, else 128-row tiles).  Every tile gives the same bits (the K order of each sum does not
- * depend on it).  The table applies where the tiled kernels run (H or I at
+ * one of (32, 128, 2), (64, 128, 2), (64, 256, 1), (128, 128, 1),
+ * (128, 256, 1), (256, 256, 1).  A call takes the entry of its GEMM and
+ * shape with the smallest max_tokens >= T; with none, the built-in rule
+ * (by the expected rows per expert T*K/E_total: 32-row tiles up to 16,
+ * 64-row up to 96, else 128-row, and 256-row for GEMM1 from 512).  Every
+ * tile gives the same bits (the K order of each sum does not depend on it).  The table applies where the tiled kernels run (H or I at
  * least 512); an entry whose N tile does not divide the output columns
  * (GEMM1: I by bn/2, GEMM2: H by bn) is passed over.
  */
