@@ -113,6 +113,11 @@ def tune_bucket(base: dict, T: int, mode: int, capacity: int, iters: int, dev,
             e = dict(gemm=gemm, H=shape.H, I=shape.I, K=shape.K, E_total=shape.E_total,
                      E_local=shape.E_local, max_tokens=T, bm=bm, bn=bn, ku=ku)
             moe.set_tile_table([e])
+            got = moe.get_tile_config(shape, gemm)
+            if got is None or (got["bm"], got["bn"], got["ku"]) != (bm, bn, ku):
+                # the N tile does not divide the output columns: passed over
+                print("  gemm%d tile %s does not apply to this shape" % (gemm, (bm, bn, ku)))
+                continue
             out = bufs()
             if gemm == 2:
                 out[0].copy_(ref[0])
