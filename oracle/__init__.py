@@ -6,10 +6,12 @@ shares no code with it.  The arithmetic lives in ``moe_oracle.c`` (plain C,
 float32 accumulation, no fast-math); this module only loads it and marshals
 numpy arrays.
 
-Parity status: decode tables, the e4m3 encoder, bf16 rounding, dispatch and
+Parity status: decode tables, the e4m3 encoder, bf16 rounding, dispatch,
+the single-step checkers (GEMM2 of given rows, combine of given rows) and
 the whole layer are pinned by the ``-m "not gpu"`` tests (closed forms,
 exhaustive code sweeps, torch's own float8/bfloat16 casts, brute-force
-nearest search, a float64 dense evaluation and invariants).
+nearest search, a float64 dense evaluation, a numpy float32 combine loop
+and invariants).
 """
 
 from __future__ import annotations

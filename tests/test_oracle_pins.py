@@ -435,3 +435,133 @@ def test_generator_pad_count_and_determinism():
     # the x codes decode to BF16-rounded N(0,1) values within e4m3 precision
     x = dec_fp8_rows(a["x_fp8"], a["x_scale"])
     assert 0.9 < x.std() < 1.1
+
+
+# ------------------------------------------------ single-step checkers ----
+
+def _fp8_rows_wide(rng, n, k):
+    """MX FP8 rows whose codes cover every finite e4m3 value (subnormals and
+    both zeros included) with exponents spread over 100..150."""
+    codes = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    scales = rng.integers(100, 151, size=(n, k // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def test_gemm2_rows_reproduces_the_layer_y_bit_for_bit():
+    """GEMM2 of the oracle's own requantised intermediate (its h codes and
+    exponents) is the y of the whole-route evaluation, bit for bit: the two
+    entry points must read the same W2 nibbles and exponents in the same
+    order."""
+    case = _case(seed=1010)
+    spec = case["spec"]
+    d = oracle.dispatch(spec, case["topk_ids"])
+    routes = np.nonzero(d["route_row"] >= 0)[0]
+    ffn = oracle.routes_ffn(case, routes)
+    experts = case["topk_ids"].reshape(-1)[routes].astype(np.int32) - spec.expert_begin
+    y = oracle.gemm2_rows(case, ffn["h_codes"], ffn["h_scale"], experts)
+    np.testing.assert_array_equal(y.view(np.uint32), ffn["y"].view(np.uint32))
+
+
+def test_gemm2_rows_against_float64_matmul():
+    """GEMM2 of random MX FP8 rows (every finite code, exponents 100..150)
+    against a float64 matmul of torch-decoded rows and table-decoded W2
+    (weight exponents also spread): a sequential float32 sum of n terms is
+    within n * 2^-24 * sum|terms| of the exact sum.  A swapped nibble, a
+    wrong exponent index or a transposed operand moves results by a sizable
+    fraction of sum|terms| and fails."""
+    rng = np.random.default_rng(11)
+    case = _case(seed=1011)
+    spec = case["spec"]
+    case["w2_scale"] = rng.integers(110, 141, size=case["w2_scale"].shape, dtype=np.uint8)
+    n = 40
+    codes, scales = _fp8_rows_wide(rng, n, spec.I)
+    experts = rng.integers(0, spec.E_local, size=n).astype(np.int32)
+    y = oracle.gemm2_rows(case, codes, scales, experts).astype(np.float64)
+    hq = dec_fp8_rows(codes, scales)
+    for i, e in enumerate(experts):
+        W2 = dec_fp4_rows(case["w2"][e], case["w2_scale"][e])     # [H, I]
+        exact = W2 @ hq[i]
+        mag = np.abs(W2) @ np.abs(hq[i])
+        assert (np.abs(y[i] - exact) <= spec.I * 2.0 ** -24 * mag + 1e-300).all(), i
+    # a row with one nonzero term is that product exactly
+    one = np.zeros((1, spec.I), np.uint8)
+    one[0, 37] = 0x4C                      # e4m3 1.5 * 2^2 = 6
+    osc = np.full((1, spec.I // 32), 127, np.uint8)
+    y1 = oracle.gemm2_rows(case, one, osc, np.array([3], np.int32)).astype(np.float64)[0]
+    W2 = dec_fp4_rows(case["w2"][3], case["w2_scale"][3])
+    np.testing.assert_array_equal(y1, W2[:, 37] * dec_fp8_rows(one, osc)[0, 37])
+
+
+def _combine_numpy(spec, w, route_row, y):
+    """out[t] = bf16(sum over k ascending of w[t,k] * y[row]) in numpy float32
+    (one rounded product, one rounded add per term), rounded to bf16 by
+    torch's cast (nearest even)."""
+    K = spec.K
+    o = np.zeros((spec.T, spec.H), np.float32)
+    rr = route_row.reshape(spec.T, K)
+    for k in range(K):
+        for t in range(spec.T):
+            row = rr[t, k]
+            if row < 0:
+                continue
+            p = np.float32(w[t, k]) * y[row]
+            o[t] = o[t] + p
+    bits = torch.from_numpy(o).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits
+
+
+def test_combine_reproduces_the_layer_bit_for_bit():
+    """The combine of the per-route y rows placed by the dispatch's
+    route_row is the whole-layer oracle, bit for bit (same k order, same
+    float32 product-then-add, same single bf16 rounding)."""
+    case = _case(seed=1012)
+    spec = case["spec"]
+    d = oracle.dispatch(spec, case["topk_ids"])
+    rr = d["route_row"]
+    routes = np.nonzero(rr >= 0)[0]
+    ffn = oracle.routes_ffn(case, routes)
+    R = oracle.row_capacity(spec)
+    y = np.full((R, spec.H), np.nan, np.float32)    # unused rows must not be read
+    y[rr[routes]] = ffn["y"]
+    out = oracle.combine(spec, case["topk_w"], rr, y)
+    np.testing.assert_array_equal(out, oracle.moe_layer(case))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_combine_matches_a_numpy_float32_loop(seed):
+    """The combine against a numpy float32 loop over ascending k on random y
+    rows (a reordered k, a fused multiply-add or a second rounding would
+    change bits), with -1, invalid and foreign slots skipped."""
+    rng = np.random.default_rng(seed)
+    # most slots local (three or more terms per token, where the order of
+    # float32 adds matters), some -1, invalid or foreign
+    spec = synth.CaseSpec("comb", T=37, H=256, I=256, E_total=9, E_local=7, expert_begin=1,
+                          K=8, dispatch_mode=seed, capacity=40)
+    ids = rng.integers(-1, spec.E_total + 2, size=(spec.T, spec.K)).astype(np.int32)
+    ids[0] = -1
+    w = (rng.standard_normal((spec.T, spec.K)) * 3).astype(np.float32)
+    d = oracle.dispatch(spec, ids)
+    R = oracle.row_capacity(spec)
+    y = (rng.standard_normal((R, spec.H)) * np.exp2(rng.integers(-20, 20, size=(R, 1)))).astype(
+        np.float32)
+    # per token, the first three kept slots carry s, then w*Y and w*(-Y)
+    # with |Y| near 2^22: summed in k order the large terms cancel after s
+    # was rounded to their grid; any other order, a fused multiply-add or an
+    # extra rounding changes the bf16 result
+    rr = d["route_row"].reshape(spec.T, spec.K)
+    for t in range(spec.T):
+        kept = np.nonzero(rr[t] >= 0)[0]
+        if kept.size < 3:
+            continue
+        ka, kb, kc = kept[:3]
+        big = (rng.choice([-1.0, 1.0], spec.H) * rng.uniform(1, 2, spec.H) * 2.0 ** 22)
+        y[rr[t, ka]] = rng.standard_normal(spec.H).astype(np.float32)
+        y[rr[t, kb]] = big.astype(np.float32)
+        y[rr[t, kc]] = (-big).astype(np.float32)
+        w[t, kc] = w[t, kb]
+    got = oracle.combine(spec, w, d["route_row"], y)
+    np.testing.assert_array_equal(got, _combine_numpy(spec, w, d["route_row"], y))
+    # a token with no kept route is +0
+    none = (d["route_row"].reshape(spec.T, spec.K) < 0).all(axis=1)
+    assert none.any() and not got[none].any()
