@@ -8,9 +8,12 @@ W warmup replays, then exactly K timed replays between two device
 synchronisations.
 
 Reported (one JSON line):
-  value        weight GB/s: touched-expert W13+W2 bytes per step / step time
-  us_per_layer, routed_tflops, hbm_frac (all algorithmic bytes / 8 TB/s),
-  mfma_frac (routed FLOP / 5.0 PFLOP/s dense FP8)
+  value        routed TFLOP/s (6*H*I FLOP per valid local route / step time)
+               on a workload whose GEMMs are MFMA-bound (above the ridge
+               point of 5.0 PFLOP/s over 8 TB/s), else weight GB/s
+               (touched-expert W13+W2 bytes per step / step time)
+  us_per_layer, routed_tflops, weight_gbps, hbm_frac (all algorithmic bytes
+  / 8 TB/s), mfma_frac (routed FLOP / 5.0 PFLOP/s dense FP8)
   roofline     the dominant kernel (GEMM1 + SwiGLU + requant): its
                algorithmic bytes (HBM-bound workloads) or FLOP (MFMA-bound,
                above the ridge point) per launch / its mean launch time, the
@@ -43,7 +46,8 @@ METRIC = ("MoE layer µs + routed TFLOP/s + weight GB/s, fraction of roofline, "
           "1 MI355X")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
-DEFAULT_WORKLOAD = "v4_decode_t128_fixed"
+# the largest single-GPU workload: V4 prefill share, 8 x 8192 source tokens
+DEFAULT_WORKLOAD = "v4_prefill_t65536_uniform"
 
 
 def parse():
@@ -53,7 +57,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-routes", type=int, default=32,
+    p.add_argument("--cpu-routes", type=int, default=128,
                    help="routes in the oracle's timed sample")
     p.add_argument("--kernel-iters", type=int, default=0,
                    help="launches per kernel for the roofline timing (default: steps)")
@@ -126,13 +130,25 @@ def recorded_traffic(workload: str):
 
 
 def gemm1_algorithmic_bytes(spec, work) -> int:
-    """W13 codes + exponents of each touched expert, the MX FP8 x row of each
-    token with a local route, the MX FP8 h row written per route."""
+    """What GEMM1 must read by the layer's own accounting (intermediates are
+    implementation traffic and not counted): the W13 codes + exponents of
+    each touched expert and the MX FP8 x row of each token with a local
+    route."""
     H, I = spec.H, spec.I
     w13 = work["touched"] * (2 * I * H // 2 + 2 * I * H // 32)
     xin = work["tokens_with_route"] * (H + H // 32)
-    hout = work["routes"] * (I + I // 32)
-    return w13 + xin + hout
+    return w13 + xin
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -269,10 +285,12 @@ def main():
                 "unit": "GB/s", "frac": round(g1_bytes / g1_s / 1e9 / HBM_PEAK_GBS, 4)}
     roof["traffic"] = recorded_traffic(spec_name)
     roof["bytes_per_launch"] = int(g1_bytes)
+    mfma_bound = roof["bound"] == "mfma"
     result = {
         "metric": METRIC,
-        "value": round(weight_gbs, 2),
-        "unit": "GB/s",
+        "value": round(tflops, 2) if mfma_bound else round(weight_gbs, 2),
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "value_is": "routed TFLOP/s" if mfma_bound else "weight GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -316,7 +334,8 @@ def main():
         if take.size == 0:
             take = toks[:1]
         n_routes = int(per_tok[take].sum())
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        omp_env = os.environ.get("OMP_NUM_THREADS")
+        threads = int(omp_env or os.cpu_count() or 1)
         threads = max(1, min(threads, take.size))
         os.environ["OMP_NUM_THREADS"] = str(threads)
         oracle.lib()
@@ -324,12 +343,17 @@ def main():
         oracle.moe_layer(case, np.sort(take))
         cpu_s = time.perf_counter() - c0
         full_s = cpu_s * work["routes"] / max(n_routes, 1)
+        full_us = full_s * 1e6
         result["cpu_baseline"] = {
-            "value": round(work["weight_bytes"] / full_s / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "%d tokens / %d of %d routes, %.2f s wall, scaled by routes to the "
-                      "full batch (%.1f s)" % (take.size, n_routes, work["routes"], cpu_s,
-                                               full_s)}
+            "value": (round(work["flop"] / full_s / 1e12, 6) if mfma_bound
+                      else round(work["weight_bytes"] / full_s / 1e9, 4)),
+            "unit": result["unit"], "cores": threads, "kind": "oracle",
+            "us_per_layer": round(full_us, 1),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "omp_num_threads": omp_env,
+            "sample": "%d whole tokens holding %d of the batch's %d routes, %.2f s wall on %d "
+                      "threads; time scaled by routes to the full batch (%.1f s)" % (
+                          take.size, n_routes, work["routes"], cpu_s, threads, full_s)}
     print(json.dumps(result), flush=True)
 
 

@@ -23,7 +23,8 @@ import torch
 
 __all__ = [
     "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
-    "moe_dispatch_workspace_size", "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu",
+    "moe_dispatch_workspace_size", "moe_workspace_size", "moe_workspace_status_offset",
+    "workspace_status", "moe_dispatch", "moe_gemm1_swiglu",
     "moe_gemm2", "moe_combine", "moe_forward", "moe_forward_persistent", "moe_strerror",
     "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT",
@@ -36,7 +37,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
-            "moe_workspace_size", "moe_dispatch", "moe_gemm1_swiglu", "moe_gemm2",
+            "moe_workspace_size", "moe_workspace_status_offset", "moe_dispatch",
+            "moe_gemm1_swiglu", "moe_gemm2",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
             "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_set_tile_table",
             "moe_get_tile_config", "moe_strerror"]
@@ -123,6 +125,8 @@ def lib() -> ctypes.CDLL:
         h.moe_dispatch_workspace_size.restype = ctypes.c_size_t
         h.moe_workspace_size.argtypes = [S]
         h.moe_workspace_size.restype = ctypes.c_size_t
+        h.moe_workspace_status_offset.argtypes = [S]
+        h.moe_workspace_status_offset.restype = ctypes.c_int64
         h.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         h.moe_dispatch.restype = ctypes.c_int
         h.moe_gemm1_swiglu.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
@@ -207,6 +211,20 @@ def moe_dispatch_workspace_size(shape: MoeShape) -> int:
 def moe_workspace_size(shape: MoeShape) -> int:
     c = shape.c()
     return int(lib().moe_workspace_size(ctypes.byref(c)))
+
+
+def moe_workspace_status_offset(shape: MoeShape) -> int:
+    c = shape.c()
+    return int(lib().moe_workspace_status_offset(ctypes.byref(c)))
+
+
+def workspace_status(shape: MoeShape, workspace: torch.Tensor) -> torch.Tensor:
+    """The int32[4] dispatch status the forward entry points leave in their
+    workspace (a view; read it after the call's stream has finished)."""
+    off = moe_workspace_status_offset(shape)
+    if off < 0:
+        raise MoeError(-1, "moe_workspace_status_offset")
+    return workspace[off:off + 16].view(torch.int32)
 
 
 # ---- tensor checks -------------------------------------------------------------

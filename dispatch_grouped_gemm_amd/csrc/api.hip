@@ -43,10 +43,7 @@ Layout layout_of(const moe_shape &s)
     L.status = p;
     p = align_up(p + sizeof(int32_t) * 4);
     L.sync = p;
-    const int sync_words = moe::fused_sync_words(s) > moe::persistent_sync_words(s)
-                               ? moe::fused_sync_words(s)
-                               : moe::persistent_sync_words(s);
-    p = align_up(p + sizeof(int32_t) * (size_t)sync_words);
+    p = align_up(p + sizeof(int32_t) * (size_t)moe::persistent_sync_words(s));
     L.scratch = p;
     p = align_up(p + moe::dispatch_scratch_bytes(s));
     L.h = p;
@@ -93,6 +90,11 @@ int moe_check_shape(const moe_shape *s)
         return MOE_ENOTSUP;
     if ((long long)s->T * s->K >= (1ll << 31))
         return MOE_ENOTSUP;
+    // the kernels address a gathered activation row (token t of x) and a row
+    // of one expert's weights with 32-bit byte offsets from a wavefront-
+    // uniform base: x itself, and the expert's first weight row
+    if ((long long)s->T * s->H >= (1ll << 32) || (long long)s->I * s->H >= (1ll << 32))
+        return MOE_ENOTSUP;
     if (s->dispatch_mode == MOE_DISPATCH_FIXED_SLOT &&
         (long long)s->E_local * s->capacity >= (1ll << 31))
         return MOE_ENOTSUP;
@@ -120,6 +122,13 @@ size_t moe_workspace_size(const moe_shape *s)
     if (moe_check_shape(s) != MOE_OK)
         return 0;
     return layout_of(*s).total;
+}
+
+int64_t moe_workspace_status_offset(const moe_shape *s)
+{
+    if (moe_check_shape(s) != MOE_OK)
+        return -1;
+    return (int64_t)layout_of(*s).status;
 }
 
 static int dispatch_impl(const moe_shape *s, const int32_t *ids, const int32_t *valid,
@@ -274,25 +283,13 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
     uint8_t *hs = base + L.hs;
     uint16_t *y = reinterpret_cast<uint16_t *>(base + L.y);
     hipStream_t st = as_stream(stream);
-    if (moe::use_fused_decode(*s)) {
-        // dispatch (which also clears the work-queue counters), then one
-        // persistent launch for GEMM1, GEMM2 and the combine
-        int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
-        hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row,
-                                            status, scratch, st, sync,
-                                            moe::fused_sync_words(*s), qj, valid);
-        if (e == hipSuccess)
-            e = moe::launch_fused_decode(*s, x, xs, counts, offsets, row_route, route_row, tw,
-                                         w13, w13s, w2, w2s, h, hs, y, out, sync, st);
-        return hip_status(e);
-    }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st, nullptr, 0, qj, valid);
     if (persistent) {
         int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
         if (e == hipSuccess)
             e = moe::launch_layer_persistent(*s, x, xs, counts, offsets, row_route, w13, w13s, w2,
-                                             w2s, h, hs, y, sync, st);
+                                             w2s, h, hs, y, sync, status, st);
     } else {
         if (e == hipSuccess)
             e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
@@ -377,7 +374,8 @@ const char *moe_strerror(int code)
     case MOE_EINVAL:
         return "invalid argument";
     case MOE_ENOTSUP:
-        return "shape not supported (H and I multiples of 128, K <= 8, E_local <= 512)";
+        return "shape not supported (H and I multiples of 128, K <= 8, E_local <= 512, "
+               "T*H and I*H below 2^32)";
     case MOE_EWORKSPACE:
         return "workspace missing, too small or not 256-byte aligned";
     case MOE_EHIP:

@@ -205,9 +205,6 @@ struct LayerPtrs {
     const uint8_t *w13, *w13s, *w2, *w2s;
     uint8_t *h, *hs;
     uint16_t *y;
-    const float *tw;
-    const int32_t *route_row;
-    uint16_t *out;
 };
 
 // Where an item's rows are: expert e, rows [row0, row0 + nrows).
@@ -412,113 +409,6 @@ gemm2_skinny_kernel(Shape s, LayerPtrs p)
     }
 }
 
-// ---------------------------------------------------------------------------
-// The whole layer after dispatch in one persistent launch.  Workgroups take
-// tickets from one counter: first every GEMM1 item (row chunk, 32
-// intermediate columns), expert by expert, then every GEMM2 item, then the
-// combine items (one token, 2048 output columns).  A GEMM2 item of expert e
-// waits until all GEMM1 items of e have finished (a per-expert counter); a
-// combine item waits until every GEMM2 item has finished.  Tickets are
-// handed out in that order, so a wait only ever concerns items that running
-// workgroups already hold, and every wait ends; a wait that does not end
-// within kMaxSpins polls counts itself in sync[1] and gives up rather than
-// hang.
-//
-// Control flow around the barriers stays wave-uniform: the queue work is done
-// by a whole wavefront (wave 0) whose lanes all run the same atomics and
-// polls, never by one lane behind a per-lane branch.  (Per-lane branches on
-// both sides of the loop's back edge let the compiler join them into a
-// lane-divergent inner loop whose other lanes never take the next ticket.)
-// Every wavefront releases its own stores with its own increment, so a
-// finished item adds kWaves to its counter.
-//
-// sync (zeroed by the dispatch launch): [0] ticket counter, [1] wait
-// timeouts, [2] finished GEMM2 items, [3 + e] finished GEMM1 items of e.
-// Counters are released and acquired at agent scope, so h and y written by
-// one XCD are seen by the others.
-// ---------------------------------------------------------------------------
-constexpr int kWaves = kThreads / 64;
-constexpr int kMaxSpins = 1 << 20;
-
-// Whole-wavefront wait until *cnt >= need, then an agent-scope acquire.
-__device__ __forceinline__ void wait_count(int32_t *cnt, int need, int32_t *timeouts, int one)
-{
-    for (int spins = 0;; ++spins) {
-        const int v = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (v >= need)
-            break;
-        if (spins >= kMaxSpins) {
-            __hip_atomic_fetch_add(timeouts, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-template <int NMB>
-__global__ void __launch_bounds__(kThreads)
-fused_decode_kernel(Shape s, LayerPtrs p, int32_t *sync)
-{
-    constexpr int CH = 16 * NMB;
-    constexpr int kCombineCols = 2048;
-    __shared__ int prefix[kMaxLocalExperts + 1];
-    __shared__ int tok[CH];
-    __shared__ float red[NMB * 4 * 4 * 64];
-    __shared__ int ticket;
-    extern __shared__ __align__(16) uint8_t exps[];
-    const int tid = threadIdx.x;
-    // 1 in lane 0 of each wavefront, 0 elsewhere: a whole-wavefront atomic
-    // add of `one` counts once per wavefront.
-    const int one = (tid & 63) == 0 ? 1 : 0;
-    const bool leader = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
-    const int nchunks = plan_chunks(s, p.counts, CH, prefix);
-    const int NT1 = s.I / 32, NT2 = s.H / 64;
-    const int CB = (s.H + kCombineCols - 1) / kCombineCols;
-    const long items1 = (long)nchunks * NT1, items2 = (long)nchunks * NT2;
-    const long total = items1 + items2 + (long)s.T * CB;
-    int32_t *timeouts = sync + 1, *done2 = sync + 2, *done1 = sync + 3;
-
-    for (;;) {
-        if (leader) {
-            const int mine = __hip_atomic_fetch_add(sync, one, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-            ticket = __builtin_amdgcn_readfirstlane(mine);
-        }
-        __syncthreads();
-        const long t = ticket;
-        __syncthreads();
-        if (t >= total)
-            break;
-        if (t < items1) {
-            const int q = (int)(t / NT1), nt = (int)(t - (long)q * NT1);
-            const Chunk c = chunk_of(s, prefix, p.counts, p.offsets, CH, q);
-            gemm1_item<NMB>(s, p, c, nt, tok, red, exps);
-            __hip_atomic_fetch_add(done1 + c.e, one, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (t < items1 + items2) {
-            const long u = t - items1;
-            const int q = (int)(u / NT2), nt = (int)(u - (long)q * NT2);
-            const Chunk c = chunk_of(s, prefix, p.counts, p.offsets, CH, q);
-            if (leader) {
-                const int chunks_e = prefix[c.e + 1] - prefix[c.e];
-                wait_count(done1 + c.e, kWaves * chunks_e * NT1, timeouts, one);
-            }
-            __syncthreads();
-            gemm2_item<NMB>(s, p, c, nt, red, exps);
-            __hip_atomic_fetch_add(done2, one, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            const long u = t - items1 - items2;
-            const int tk = (int)(u / CB), cb = (int)(u - (long)tk * CB);
-            if (leader)
-                wait_count(done2, (int)(kWaves * items2), timeouts, one);
-            __syncthreads();
-            combine_cols(s, p.tw, p.route_row, p.y, p.out, tk,
-                         (cb * kThreads + tid) * kCombineVec);
-        }
-    }
-}
-
 int g_cu_count = 0;
 
 template <typename KernelT>
@@ -659,70 +549,6 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
     else
         MOE_LAUNCH_G2(4);
 #undef MOE_LAUNCH_G2
-    return hipGetLastError();
-}
-
-} // namespace moe
-
-namespace moe {
-
-// The persistent single-launch layer is correct but slower than the four
-// launches on every decode shape measured (7168 x 3072, 36 experts touched:
-// 1494 us against about 300 us): each item's release writes back the L2 and
-// each GEMM2 item's acquire invalidates it, which costs more than the launch
-// gaps it saves.  It stays off until that synchronisation is cheaper.
-constexpr bool kFusedDecodeEnabled = false;
-
-bool use_fused_decode(const moe_shape &s)
-{
-    return kFusedDecodeEnabled && !use_tiled_gemm1(s) && !use_tiled_gemm2(s) &&
-           dispatch_is_single_block(s);
-}
-
-int fused_sync_words(const moe_shape &s) { return 3 + s.E_local; }
-
-hipError_t launch_fused_decode(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
-                               const int32_t *counts, const int32_t *offsets,
-                               const int32_t *row_route, const int32_t *route_row,
-                               const float *tw, const uint8_t *w13, const uint8_t *w13s,
-                               const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
-                               uint16_t *y, uint16_t *out, int32_t *sync, hipStream_t st)
-{
-    const Shape s = to_dev(sh);
-    LayerPtrs p{};
-    p.x = x;
-    p.xs = xs;
-    p.counts = counts;
-    p.offsets = offsets;
-    p.row_route = row_route;
-    p.w13 = w13;
-    p.w13s = w13s;
-    p.w2 = w2;
-    p.w2s = w2s;
-    p.h = h;
-    p.hs = hs;
-    p.y = y;
-    p.tw = tw;
-    p.route_row = route_row;
-    p.out = out;
-    const int nmb = pick_nmb(sh);
-    const long upper = chunk_upper_bound(sh, 16 * nmb) * (sh.I / 32 + sh.H / 64) +
-                       (long)sh.T * ((sh.H + 2047) / 2048);
-#define MOE_LAUNCH_FUSED(N)                                                                       \
-    do {                                                                                          \
-        auto k = fused_decode_kernel<N>;                                                          \
-        const int es = exp_stride(sh.H) > exp_stride(sh.I) ? exp_stride(sh.H) : exp_stride(sh.I); \
-        const size_t lds = (size_t)(64 + 16 * N) * es;                                            \
-        const int grid = grid_for(k, upper, lds);                                                 \
-        k<<<grid, kThreads, lds, st>>>(s, p, sync);                                               \
-    } while (0)
-    if (nmb == 1)
-        MOE_LAUNCH_FUSED(1);
-    else if (nmb == 2)
-        MOE_LAUNCH_FUSED(2);
-    else
-        MOE_LAUNCH_FUSED(4);
-#undef MOE_LAUNCH_FUSED
     return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@
 // Work items are (row tile of one expert, N tile), derived on every
 // workgroup from counts as in the skinny kernels, and taken in a grid-stride
 // loop.
+#include <cstdlib>
 #include <mutex>
 
 #include "moe_common.hpp"
@@ -145,13 +146,9 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                                            const int *prefix, int *arow, uint8_t *lds, int q,
                                            int nt)
 {
-    const uint8_t *__restrict__ act = g.act;
-    const uint8_t *__restrict__ act_s = g.act_s;
     const int32_t *__restrict__ counts = g.counts;
     const int32_t *__restrict__ offsets = g.offsets;
     const int32_t *__restrict__ row_route = g.row_route;
-    const uint8_t *__restrict__ w = g.w;
-    const uint8_t *__restrict__ ws = g.ws;
     uint8_t *__restrict__ h_out = g.h_out;
     uint8_t *__restrict__ hs_out = g.hs_out;
     uint16_t *__restrict__ y_out = g.y_out;
@@ -177,27 +174,36 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
     const int KS = KT / 128;                // K steps
     const int U = (KS + KU - 1) / KU;       // stages
     {
-        const int e = chunk_expert(prefix, s.E_local, q);
+        const int e = __builtin_amdgcn_readfirstlane(chunk_expert(prefix, s.E_local, q));
         const int c = q - prefix[e];
-        const int row0 = offsets[e] + c * BM;
+        const int row0 = __builtin_amdgcn_readfirstlane(offsets[e] + c * BM);
         const int nrows = min(BM, used_rows(s, counts[e]) - c * BM);
+        // wavefront-uniform bases: expert e's weight rows and, for GEMM2, the
+        // tile's first h row, so every 32-bit lane offset below stays inside
+        // one expert's weights or one row tile (GEMM1's gathered x rows are
+        // addressed from x itself: T * H < 2^32 is checked on the host)
+        const size_t wrows = kGemm1 ? 2 * (size_t)I : (size_t)H;
+        const uint8_t *__restrict__ w = g.w + (size_t)e * wrows * (size_t)(KT / 2);
+        const uint8_t *__restrict__ ws = g.ws + (size_t)e * wrows * (size_t)(KT / 32);
+        const uint8_t *__restrict__ act = kGemm1 ? g.act : g.act + (size_t)row0 * (size_t)KT;
+        const uint8_t *__restrict__ act_s =
+            kGemm1 ? g.act_s : g.act_s + (size_t)row0 * (size_t)(KT / 32);
         if (tid < BM) {
             const int r = min(tid, nrows - 1);
-            arow[tid] = kGemm1 ? row_route[row0 + r] / s.K : row0 + r;
+            arow[tid] = kGemm1 ? row_route[row0 + r] / s.K : r;
         }
         __syncthreads();
 
-        // weight row (within the expert's rows of W) of tile row r
+        // weight row (within expert e's rows of W) of tile row r
         auto wrow_of = [&](int r) -> uint32_t {
             const int grp = r >> 4, rr = r & 15;
             if (kGemm1) {
                 // group grp: wavefront half grp / GW; within it GW/2 gate
                 // groups, then the GW/2 matching up groups
                 const int half = grp / GW, up = (grp % GW) >= GW / 2, cb = grp % (GW / 2);
-                return (uint32_t)(e * 2 * I + (up ? I : 0) + nt * (BN / 2) + (BN / 4) * half +
-                                  16 * cb + rr);
+                return (uint32_t)((up ? I : 0) + nt * (BN / 2) + (BN / 4) * half + 16 * cb + rr);
             }
-            return (uint32_t)(e * H + nt * BN + r);
+            return (uint32_t)(nt * BN + r);
         };
         // LDS layout of a stage: weight tile row r at WROW r (64 bytes of
         // each row per K step, so WROW = 64 or 128), then activation rows:
@@ -496,12 +502,14 @@ struct TileShared {
 // workgroups hold and reach first.  A GEMM1 item counts in ready[q] once
 // its h stores are in the L2; GEMM2 reads h past the CU's L1.
 // sync[32 x] is queue x's ticket counter (one 128-byte line each),
-// sync[256 + q] = ready[q], all zero at launch.  Every wait is bounded:
-// past the bound a workgroup goes on (wrong numbers, which the tests would
-// catch, rather than a GPU that never finishes).
+// sync[256 + q] = ready[q], all zero at launch.  Every wait is bounded by
+// max_polls: past the bound the workgroup counts the timeout in status[2]
+// and goes on (its GEMM2 item may then read h before it is written), so
+// the caller sees a failed layer instead of a GPU that never finishes.
 template <int BM, int BN1, int BN2, int KU>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int nq)
+layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int32_t *status,
+                        int nq, int max_polls)
 {
     // one stage ring, sized for the wider of the two weight tiles
     __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), KU> sh;
@@ -540,13 +548,18 @@ layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int 
         } else {
             const int q = x + nq * ((t - n1) / NT2), nt = (t - n1) % NT2;
             if (wave == 0) {
-                for (int it = 0; it < (1 << 22); ++it) {
+                bool done = false;
+                for (int it = 0; it < max_polls; ++it) {
                     const int v = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(&ready[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    if (v >= NT1)
+                    if (v >= NT1) {
+                        done = true;
                         break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
                 }
+                if (!done)
+                    atomicAdd(&status[2], lane == 0 ? 1 : 0);
             }
             __syncthreads();
             tiled_item<false, BM, BN2, KU, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
@@ -819,12 +832,27 @@ bool persistent_supported(const moe_shape &sh)
 
 int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 32); }
 
+// Polls of a persistent wait before it gives up (2^22 polls of s_sleep 2,
+// about a second); MOE_PERSISTENT_MAX_POLLS in the environment, read at
+// every launch, lowers it (0: no poll, every wait gives up at once), so a
+// test can make the waits give up while every kernel still exits normally.
+static int persistent_max_polls()
+{
+    constexpr int kDefault = 1 << 22;
+    const char *v = getenv("MOE_PERSISTENT_MAX_POLLS");
+    if (!v || !*v)
+        return kDefault;
+    char *end = nullptr;
+    const long n = strtol(v, &end, 10);
+    return *end == 0 && n >= 0 && n < kDefault ? (int)n : kDefault;
+}
+
 hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
                                    const int32_t *counts, const int32_t *offsets,
                                    const int32_t *row_route, const uint8_t *w13,
                                    const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
                                    uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
-                                   hipStream_t st)
+                                   int32_t *status, hipStream_t st)
 {
     const int nsync = persistent_sync_words(sh);
     fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
@@ -838,7 +866,8 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
     auto go = [&](auto k, int bm, int b1, int b2) {
         const long items = tile_upper_bound(sh, bm) * (long)(sh.I / (b1 / 2) + sh.H / b2);
         const int grid = tiled_grid(k, items);
-        k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, nq);
+        k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, status, nq,
+                                                        persistent_max_polls());
     };
     if (c1.bm == 32)
         go(layer_persistent_kernel<32, 128, 128, 2>, 32, 128, 128);

@@ -327,14 +327,6 @@ hipError_t launch_dispatch(const moe_shape &s, const int32_t *ids, int32_t *coun
 // workgroups of `threads` threads that the quant job wants (at least one)
 int quant_blocks(const QuantJob &q, int threads);
 hipError_t launch_quant_mxfp8(const QuantJob &q, hipStream_t st);
-bool use_fused_decode(const moe_shape &s);
-int fused_sync_words(const moe_shape &s);
-hipError_t launch_fused_decode(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
-                               const int32_t *counts, const int32_t *offsets,
-                               const int32_t *row_route, const int32_t *route_row,
-                               const float *tw, const uint8_t *w13, const uint8_t *w13s,
-                               const uint8_t *w2, const uint8_t *w2s, uint8_t *h, uint8_t *hs,
-                               uint16_t *y, uint16_t *out, int32_t *sync, hipStream_t st);
 hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
                         const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
@@ -360,12 +352,14 @@ hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_
 bool persistent_supported(const moe_shape &s);
 int persistent_sync_words(const moe_shape &s);
 // GEMM1 + SwiGLU + requant and GEMM2 in one persistent launch (after a
-// zero-fill of sync[0 .. persistent_sync_words)).
+// zero-fill of sync[0 .. persistent_sync_words)); a wait that gives up
+// counts in status[2].
 hipError_t launch_layer_persistent(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                                    const int32_t *counts, const int32_t *offsets,
                                    const int32_t *row_route, const uint8_t *w13,
                                    const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
                                    uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
+                                   int32_t *status,
                                    hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
                           const uint16_t *y, uint16_t *out, hipStream_t st);

@@ -39,15 +39,17 @@
  *                           -1, not local, invalid or dropped
  *   status    int32 [4]     [0] ids outside [-1, E_total) (skipped),
  *                           [1] fixed-slot routes dropped for capacity,
- *                           [2], [3] zero
+ *                           [2] persistent-layer waits that gave up (the
+ *                               layer's output is then not valid),
+ *                           [3] zero; the dispatch writes all four
  * Intermediates, indexed by row:
- *   h_fp8 [R, I], h_scale [R, I/32], y_f32 [R, H] (float32)
+ *   h_fp8 [R, I], h_scale [R, I/32], y_bf16 [R, H] (bf16 bit patterns)
  *
  * Rows inside a compact segment are in ascending r (a stable scatter);
  * inside a fixed-slot segment their order is unspecified.
  *
  * Alignment: the FP8, MXFP4 and E8M0 arrays (x_fp8, x_scale, w13,
- * w13_scale, w2, w2_scale, h_fp8, h_scale), y_f32 and out_bf16 must start on
+ * w13_scale, w2, w2_scale, h_fp8, h_scale), y_bf16 and out_bf16 must start on
  * a 16-byte boundary (PyTorch allocations do); a misaligned one is refused
  * with MOE_EINVAL.
  *
@@ -82,9 +84,10 @@ extern "C" {
 #define MOE_DISPATCH_FIXED_SLOT 1 /* atomic claim into per-expert capacity */
 
 typedef struct moe_shape {
-    int32_t T;             /* source tokens (0 is a valid no-op) */
+    int32_t T;             /* source tokens (0 is a valid no-op); T*H < 2^32 */
     int32_t H;             /* hidden size, a multiple of 128 */
-    int32_t I;             /* expert intermediate size, a multiple of 128 */
+    int32_t I;             /* expert intermediate size, a multiple of 128;
+                              I*H < 2^32 */
     int32_t K;             /* top-k slots per token, 1..8 */
     int32_t E_total;       /* experts in the model */
     int32_t expert_begin;  /* first global id owned here */
@@ -107,6 +110,11 @@ size_t moe_dispatch_workspace_size(const moe_shape *shape);
 /* Device scratch bytes moe_forward needs (dispatch results, h, y, and the
  * MX FP8 activations of moe_forward_bf16). */
 size_t moe_workspace_size(const moe_shape *shape);
+
+/* Byte offset inside the moe_forward workspace of the dispatch's int32[4]
+ * status array (see "status" above), which the forward entry points leave
+ * there for the caller to read; -1 for a refused shape. */
+int64_t moe_workspace_status_offset(const moe_shape *shape);
 
 /*
  * Dispatch ("AITER MegaMoEV2 ... two dispatch schemes": compact packs the
@@ -188,10 +196,19 @@ int moe_combine(const moe_shape *shape, const float *topk_w, const int32_t *rout
                 const uint16_t *y_bf16, uint16_t *out_bf16, void *stream);
 
 /*
- * The whole layer: dispatch, GEMM1 + SwiGLU + requant, GEMM2, combine, with
- * the dispatch results and intermediates in `workspace`
- * (>= moe_workspace_size(shape) bytes, 256-byte aligned).  Equal to calling
- * the four steps above in order.
+ * The whole layer ("MegaMoEV2: fuse Dispatch, GEMM1, GEMM2 and Combine into
+ * one kernel", Technical Details: dispatch, the two expert GEMMs and the
+ * combine as one call on one stream; "full-expert DeepSeek V4.1 Flash
+ * MegaMoE tuning", Summary: W13 GEMM, clamp-10 SwiGLU, FP8 requant, W2 GEMM,
+ * weighted combine): for every token t,
+ *   out[t,:] = bf16( sum over k ascending with a local id of
+ *                    topk_w[t,k] * W2_e . Q8( SwiGLU( W13_e . x_t ) ) )
+ * computed as moe_dispatch, moe_gemm1_swiglu, moe_gemm2 and moe_combine in
+ * that order (the result is bit-identical to calling them), with the
+ * dispatch results and intermediates in `workspace` (>=
+ * moe_workspace_size(shape) bytes, 256-byte aligned; its contents are
+ * scratch, nothing in it needs clearing).  The kernel of each step is chosen
+ * from host-known sizes only.  Calls that overlap on one workspace race.
  */
 int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
                 const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,
@@ -210,7 +227,11 @@ int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_s
  * does not cover (H or I below 512, or a tuned table giving GEMM1 and GEMM2
  * different row tiles) and on a device whose CU count is not that of 1, 2,
  * 4 or 8 MI355X XCDs.  Calls that overlap on one workspace
- * race, as for moe_forward.
+ * race, as for moe_forward.  Every wait of a GEMM2 item is bounded; one that
+ * gives up counts in the workspace's status[2] (the int32[4] status
+ * array at byte moe_workspace_status_offset(shape) of the workspace), and
+ * the output is then not valid.  MOE_PERSISTENT_MAX_POLLS in the environment (read at
+ * every launch) lowers the bound, which tests use to force the timeout.
  */
 int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
                            const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,

@@ -54,6 +54,12 @@ class CaseSpec:
     gate_limit: float = 10.0
     up_limit: float = 10.0
     seed: int = 0
+    # E8M0 bytes of the weights, drawn uniformly from [w_exp_lo, w_exp_hi]
+    w_exp_lo: int = 121
+    w_exp_hi: int = 124
+    # each x row is scaled by 2^j, j uniform in [-x_row_exp, x_row_exp], before
+    # its MX FP8 quantisation (0: N(0,1) rows as drawn)
+    x_row_exp: int = 0
 
     def with_(self, **kw) -> "CaseSpec":
         return dataclasses.replace(self, **kw)
@@ -212,7 +218,11 @@ def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> 
         ids.reshape(-1)[flat] = -1
     # the draws above are the same as make_routing's
 
-    xf = _bf16_round(rng.standard_normal((T, H), dtype=np.float32))
+    xf = rng.standard_normal((T, H), dtype=np.float32)
+    if spec.x_row_exp:
+        j = rng.integers(-spec.x_row_exp, spec.x_row_exp + 1, size=(T, 1))
+        xf = np.ldexp(xf, j.astype(np.int32)).astype(np.float32)
+    xf = _bf16_round(xf)
     x_fp8, x_scale = _quant_x(xf)
     x_bf16 = (xf.view(np.uint32) >> 16).astype(np.uint16)
     del xf
@@ -220,10 +230,11 @@ def make_case(spec: CaseSpec | str, seed: Optional[int] = None, **overrides) -> 
     def codes(n):
         return np.frombuffer(rng.bytes(n), dtype=np.uint8).copy()
 
+    lo, hi = spec.w_exp_lo, spec.w_exp_hi + 1
     w13 = codes(EL * 2 * I * (H // 2)).reshape(EL, 2 * I, H // 2)
-    w13_scale = rng.integers(121, 125, size=(EL, 2 * I, H // 32), dtype=np.uint8)
+    w13_scale = rng.integers(lo, hi, size=(EL, 2 * I, H // 32), dtype=np.uint8)
     w2 = codes(EL * H * (I // 2)).reshape(EL, H, I // 2)
-    w2_scale = rng.integers(121, 125, size=(EL, H, I // 32), dtype=np.uint8)
+    w2_scale = rng.integers(lo, hi, size=(EL, H, I // 32), dtype=np.uint8)
     return dict(spec=spec, x_bf16=x_bf16, x_fp8=x_fp8, x_scale=x_scale, topk_ids=ids, topk_w=w,
                 w13=w13, w13_scale=w13_scale, w2=w2, w2_scale=w2_scale)
 

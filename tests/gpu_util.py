@@ -99,6 +99,23 @@ def sample_tokens(case: dict, n_routed: int = 6, n_empty: int = 2) -> np.ndarray
     return np.unique(np.array(pick, dtype=np.int64))
 
 
+def log_parity(what: str, **fields):
+    """Append one JSON record of a layer check to $MOE_PARITY_LOG (if set):
+    the literal max|err|/RMS against the oracle and how many elements lie
+    beyond 2e-2 * RMS(ref)."""
+    import json
+    import os
+    path = os.environ.get("MOE_PARITY_LOG")
+    if not path:
+        return
+    rec = {"check": what}
+    rec.update({k: (float(v) if isinstance(v, (np.floating, float)) else
+                    int(v) if isinstance(v, (np.integer, int)) else v)
+                for k, v in fields.items()})
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
+
+
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
     """Spacing of bf16 values at |v| (8 significant bits)."""
     a = np.maximum(np.abs(v), 2.0 ** -126)
@@ -121,8 +138,12 @@ def assert_layer_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = "
     allowed = np.maximum(2e-2 * rms, bf16_ulp(ref))
     bad = err > allowed
     lit = float(err.max()) / rms
-    say("%s: %d of %d elements differ, max|err|/RMS %.4g, RMS %.4g, over the bar %d" % (
-        what, int((got != ref).sum()), got.size, lit, rms, int(bad.sum())))
+    over = int((err > 2e-2 * rms).sum())
+    say("%s: %d of %d elements differ, max|err|/RMS %.4g, RMS %.4g, beyond 2e-2*RMS %d, "
+        "over the bar %d" % (what, int((got != ref).sum()), got.size, lit, rms, over,
+                             int(bad.sum())))
+    log_parity(what, elements=got.size, differ=int((got != ref).sum()), max_err_over_rms=lit,
+               beyond_2e2_rms=over)
     assert not bad.any(), "%s: %d elements beyond max(2e-2 * RMS, 1 bf16 step), worst %.4g * RMS" % (
         what, int(bad.sum()), float((err - allowed).max() + 2e-2 * rms) / rms)
     return lit
@@ -242,10 +263,14 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
     bar = np.maximum(2e-2 * rms, bf16_ulp(ref))
     beyond = err > bar + allowance * 1.0001 + 1e-6 * rms
     lit = float(err.max()) / rms
-    say("%s: %d tokens, %d of %d elements differ, max|err|/RMS %.4g (RMS %.4g); "
-        "requant flips %d of %d codes; beyond the bar without a flip to explain it: %d" % (
-            what, tokens.size, int((got != ref).sum()), got.size, lit, rms, n_flips, n_codes,
-            int(beyond.sum())))
+    over = int((err > 2e-2 * rms).sum())
+    say("%s: %d tokens, %d routes, %d of %d elements differ, max|err|/RMS %.4g (RMS %.4g), "
+        "beyond 2e-2*RMS %d; requant flips %d of %d codes; beyond the bar without a flip to "
+        "explain it: %d" % (what, tokens.size, len(slots), int((got != ref).sum()), got.size, lit,
+                            rms, over, n_flips, n_codes, int(beyond.sum())))
+    log_parity(what, tokens=tokens.size, routes=len(slots), elements=got.size,
+               differ=int((got != ref).sum()), max_err_over_rms=lit, beyond_2e2_rms=over,
+               requant_flips=n_flips, requant_codes=n_codes)
     assert not beyond.any(), what + ": elements beyond the bar"
     if n_codes:
         assert n_flips <= max(4, max_flip_rate * n_codes), what + ": too many requant flips"
@@ -275,9 +300,80 @@ def check_dispatch(spec, ids: np.ndarray, d, num_valid=None):
             if counts[e] <= C:
                 np.testing.assert_array_equal(np.sort(seg), np.sort(refseg))
             else:
+                # an overflowing segment holds `kept` distinct routes, each a
+                # valid slot of this expert (which of them win is a race)
                 assert len(set(seg.tolist())) == kept
+                eff = ids if num_valid is None else oracle.pad_rows(ids, num_valid)
+                mine = np.nonzero(eff.reshape(-1) == spec.expert_begin + e)[0]
+                assert np.isin(seg, mine).all(), e
             assert (row_route[e * C + kept:(e + 1) * C] == -1).all()  # untouched
         kept_r = np.nonzero(rr >= 0)[0]
         np.testing.assert_array_equal(row_route[rr[kept_r]], kept_r)
         assert ((rr >= 0) == (ref["route_row"] >= 0)).all() or status[1] > 0
     return ref
+
+
+def boundary_tokens(case: dict, d, route_budget: int = 160, bms=(32, 64, 128, 256),
+                    seed: int = 0) -> np.ndarray:
+    """Tokens whose routes sit at the edges of the row tiles the GEMMs cut
+    (first and last row of a tile of every row count in `bms`, the last row
+    of each expert's segment), the most loaded expert first, then the other
+    experts in turn, until the tokens hold about `route_budget` local routes;
+    plus two tokens without a local route.  `d` holds the GPU's dispatch
+    buffers (checked against the oracle's elsewhere)."""
+    spec = case["spec"]
+    K = spec.K
+    rng = np.random.default_rng(seed)
+    counts, offsets = host(d.counts), host(d.offsets)
+    row_route = host(d.row_route)
+    used = np.minimum(counts, spec.capacity) if spec.dispatch_mode == 1 else counts
+    ids = case["topk_ids"]
+    e_of = ids.astype(np.int64) - spec.expert_begin
+    loc = (ids >= 0) & (ids < spec.E_total) & (e_of >= 0) & (e_of < spec.E_local)
+    per_tok = loc.sum(axis=1)
+    rows_by_expert = []
+    for e in np.argsort(-used, kind="stable"):
+        n = int(used[e])
+        if n == 0:
+            continue
+        cand = [n - 1]
+        for bm in bms:
+            tiles = (n + bm - 1) // bm
+            picks = {0, tiles - 1}
+            if tiles > 2:
+                picks.add(int(rng.integers(1, tiles - 1)))
+            for c in sorted(picks):
+                cand += [c * bm, min((c + 1) * bm, n) - 1]
+        rows_by_expert.append([int(offsets[e]) + r for r in dict.fromkeys(cand)])
+    toks, routes = [], 0
+    depth = 0
+    while routes < route_budget and any(depth < len(r) for r in rows_by_expert):
+        for rows in rows_by_expert:
+            if depth < len(rows) and routes < route_budget:
+                t = int(row_route[rows[depth]]) // K
+                if t not in toks:
+                    toks.append(t)
+                    routes += int(per_tok[t])
+        depth += 1
+    empty = np.nonzero(per_tok == 0)[0]
+    if empty.size:
+        toks += [int(empty[0]), int(empty[-1])]
+    return np.unique(np.array(toks, dtype=np.int64))
+
+
+CANARY = 0x5A
+
+
+def with_canary(t: torch.Tensor, nbytes: int = 4096):
+    """(view, guard): `view` is t's shape over a buffer `nbytes` longer whose
+    tail holds the canary byte; guard() asserts the tail is untouched."""
+    n = t.numel() * t.element_size()
+    buf = torch.full((n + nbytes,), CANARY, dtype=torch.uint8, device=t.device)
+    buf[:n].copy_(t.reshape(-1).view(torch.uint8) if n else buf[:0])
+    view = buf[:n].view(t.dtype).reshape(t.shape)
+
+    def guard(what=""):
+        tail = buf[n:].cpu().numpy()
+        assert (tail == CANARY).all(), "%s: %d bytes written past the end" % (
+            what, int((tail != CANARY).sum()))
+    return view, guard

@@ -47,9 +47,24 @@ def test_shape_checks(lib):
         ({"dispatch_mode": 1, "capacity": 0}, -1), ({"K": 9}, -2), ({"H": 7168 + 64}, -2),
         ({"I": 3072 + 32}, -2), ({"E_local": 513, "E_total": 1024}, -2),
         ({"gate_limit": float("nan")}, -1),
+        # 32-bit byte offsets: a gathered x row (t * H) and a row of one
+        # expert's weights (I * H bytes of W13 per expert)
+        ({"T": (1 << 32) // 7168 + 1}, -2), ({"I": 1 << 19, "H": 8192}, -2),
     ]
     for kw, code in bad:
         assert moe.moe_check_shape(moe.MoeShape(**{**V4, **kw})) == code, kw
+
+
+def test_32bit_offset_limits(lib):
+    """Largest accepted sizes sit just below the 32-bit offset limits; the
+    weights are addressed per expert, so any number of local experts of the
+    V4 shape is accepted (all 384 on one GPU: 8.4 GB of W13)."""
+    t_max = ((1 << 32) - 1) // 7168
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "T": t_max})) == 0
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "T": t_max + 1})) == -2
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "E_local": 384})) == 0
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "H": 1 << 16, "I": (1 << 16) - 128})) == 0
+    assert moe.moe_check_shape(moe.MoeShape(**{**V4, "T": 1, "H": 1 << 16, "I": 1 << 16})) == -2
 
 
 def test_sizes(lib):
@@ -63,6 +78,9 @@ def test_sizes(lib):
     R = 128 * 6
     assert moe.moe_workspace_size(c) >= R * (3072 + 96 + 2 * 7168)
     assert moe.moe_workspace_size(moe.MoeShape(**{**V4, "K": 0})) == 0
+    off = moe.moe_workspace_status_offset(c)
+    assert off > 0 and off % 16 == 0 and off + 16 <= moe.moe_workspace_size(c)
+    assert moe.moe_workspace_status_offset(moe.MoeShape(**{**V4, "K": 0})) == -1
 
 
 def test_refusals_return_before_any_launch(lib):

@@ -13,6 +13,8 @@ small one; a spread sample of tokens on the full sizes, each of which the
 oracle computes on its own).
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,9 +22,9 @@ import torch
 import dispatch_grouped_gemm_amd as moe
 import oracle
 import synth
-from gpu_util import (DEV, bf16_f64, bf16_ulp, cached_case, check_dispatch, check_layer, dev,
-                      gemm1_mfma_bound, host, run_dispatch, run_forward, run_steps, say,
-                      sample_tokens, shape_of, upload)
+from gpu_util import (DEV, bf16_f64, bf16_ulp, boundary_tokens, cached_case, check_dispatch,
+                      check_layer, dev, gemm1_mfma_bound, host, run_dispatch, run_forward,
+                      run_steps, say, sample_tokens, shape_of, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -270,24 +272,51 @@ def test_persistent_layer_small(T, H, I):
     ref = host(run_forward(case, g, ws))
     for _ in range(2):
         np.testing.assert_array_equal(host(run_forward(case, g, ws, persistent=True)), ref)
+        assert host(moe.workspace_status(shape, ws))[2] == 0     # no wait gave up
     steps = run_steps(case, g)
     torch.cuda.synchronize()
     check_layer(case, np.arange(T), ref, steps, "persistent T=%d H=%d I=%d" % (T, H, I))
 
 
+def test_persistent_wait_timeout_is_reported():
+    """With the poll bound forced to zero every GEMM2 item of the persistent
+    layer gives up its wait at once: the kernels still finish and status[2]
+    of the workspace counts the timeouts; with the bound restored the count
+    is zero again and the bits are moe_forward's."""
+    case = synth.make_case("tiny", T=1200, H=512, I=512, seed=1310)
+    shape = shape_of(case["spec"])
+    g = upload(case)
+    ws = moe.alloc_workspace(shape, DEV)
+    ref = host(run_forward(case, g, ws))
+    say("persistent forced timeout")
+    os.environ["MOE_PERSISTENT_MAX_POLLS"] = "0"
+    try:
+        run_forward(case, g, ws, persistent=True)
+        torch.cuda.synchronize()
+        assert host(moe.workspace_status(shape, ws))[2] > 0
+    finally:
+        del os.environ["MOE_PERSISTENT_MAX_POLLS"]
+    np.testing.assert_array_equal(host(run_forward(case, g, ws, persistent=True)), ref)
+    assert host(moe.workspace_status(shape, ws))[2] == 0
+
+
 @pytest.mark.parametrize("name", ["v4_decode_t128_fixed", "v4_t1024_compact", "v4_t2048_fixed",
                                   "flash_t4096_compact", "v4_prefill_t65536_uniform",
-                                  "v4_prefill_t65536_hot30"])
+                                  "v4_prefill_t65536_zipf", "v4_prefill_t65536_hot30"])
 def test_persistent_layer_full_size(name):
     """The persistent layer on the full-size workloads (64-row tiles with two
-    K steps up to T=4096, 128-row tiles at 65,536 tokens): every output
-    element equals moe_forward's (which the sampled oracle checks cover)."""
+    K steps up to T=4096, 128-row tiles at 65,536 tokens, skewed routing
+    included): every output element equals moe_forward's (which the sampled
+    oracle checks cover) and no wait gave up."""
     case = cached_case(name)
+    shape = shape_of(case["spec"])
     say("persistent", name)
     g = upload(case)
-    ref = host(run_forward(case, g))
-    got = host(run_forward(case, g, persistent=True))
+    ws = moe.alloc_workspace(shape, DEV)
+    ref = host(run_forward(case, g, ws))
+    got = host(run_forward(case, g, ws, persistent=True))
     np.testing.assert_array_equal(got, ref)
+    assert host(moe.workspace_status(shape, ws))[2] == 0
 
 
 def test_forward_tiny_in_a_graph():
@@ -325,7 +354,10 @@ def test_forward_full_size_sampled(name):
     status = host(steps["d"].status)
     assert status[0] == 0 and status[1] == 0
     np.testing.assert_array_equal(host(steps["out"]), out)
-    tok = sample_tokens(case)
+    # tokens spread over the batch, then the tokens whose routes sit on the
+    # first and last rows of the row tiles (32 to 256 rows) and on each
+    # expert's last row, most loaded expert first: about 160 routes
+    tok = np.union1d(sample_tokens(case), boundary_tokens(case, steps["d"]))
     check_layer(case, tok, out[tok], steps, name)
     # tokens with no local route are exactly +0
     e = case["topk_ids"].astype(np.int64) - spec.expert_begin
