@@ -35,6 +35,7 @@
 // loop.
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "moe_common.hpp"
 
@@ -331,8 +332,19 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
 
         // 16-row activation blocks of this wavefront that hold dispatched
         // rows (the MFMAs of the others would only feed discarded columns)
-        const int nlive = min(TB, max(0, (nrows - wm * (BM / NWM) + 15) >> 4));
+        // (wavefront-uniform: read into a scalar register, so the guards
+        // below are scalar branches, not lane masks around every MFMA)
+        const int nlive_lane = min(TB, max(0, (nrows - wm * (BM / NWM) + 15) >> 4));
+        const int nlive = __builtin_amdgcn_readfirstlane(nlive_lane);
 
+        // The K loop, instantiated per count NL of this wavefront's live
+        // 16-row blocks (NL = TB in all but an expert's last row tile): it
+        // reads the fragments and exponents of a K step and issues its
+        // GW x NL MFMAs with no branch between them.  Per-block guards
+        // inside the loop would split it into one basic block per MFMA and
+        // serialise every LDS read with the MFMAs that use it.
+        auto k_loop = [&](auto nl_tag) {
+            constexpr int NL = decltype(nl_tag)::value;   // live 16-row blocks
         issue(0);
         if (NS == 3 && U > 1)
             issue(1);
@@ -370,29 +382,64 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                 const uint8_t *ex = lds + ((ks >> 2) % L::kExpSlots) * L::kExp + (4 * ks - ebase(ks >> 2));
                 const uint8_t *sx = st + kk * (BM * 128);
                 const int afrag = arow0 + 16 * ((4 * kk + kq) ^ ((i16 >> 1) & WSWZ));
-                v8i b[TB];
-                int sb[TB];
+                // the activation fragments of the NL live blocks, then per
+                // weight group its fragment and NL MFMAs; weight fragments
+                // double-buffered, so group i + 1's read is in flight while
+                // group i's MFMAs issue
+                if constexpr (NL > 0) {
+                v8i b[NL];
+                int sb[NL];
 #pragma unroll
-                for (int j = 0; j < TB; ++j) {
-                    if (j >= nlive)
-                        break;
+                for (int j = 0; j < NL; ++j) {
                     const u32x4 lo = lds_read16(sx + bfrag_lo + j * 2048);
                     const u32x4 hi = lds_read16(sx + bfrag_hi + j * 2048);
                     b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                     sb[j] = ex[xexp + j * 256];
                 }
+                u32x4 a_cur = lds_read16(st + afrag);
+                int sa_cur = ex[wexp];
 #pragma unroll
                 for (int i = 0; i < GW; ++i) {
-                    const u32x4 a4 = lds_read16(st + afrag + i * 16 * WROW);
-                    const v8i a = v8i{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-                    const int sa = ex[wexp + i * 256];
+                    u32x4 a_nxt = a_cur;
+                    int sa_nxt = sa_cur;
+                    if (i + 1 < GW) {
+                        a_nxt = lds_read16(st + afrag + (i + 1) * 16 * WROW);
+                        sa_nxt = ex[wexp + (i + 1) * 256];
+                    }
+                    const v8i a = v8i{(int)a_cur[0], (int)a_cur[1], (int)a_cur[2],
+                                      (int)a_cur[3], 0, 0, 0, 0};
 #pragma unroll
-                    for (int j = 0; j < TB; ++j)
-                        if (j < nlive)
-                            acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa, sb[j]);
+                    for (int j = 0; j < NL; ++j)
+                        acc[i][j] = mfma_w4a8(a, b[j], acc[i][j], sa_cur, sb[j]);
+                    a_cur = a_nxt;
+                    sa_cur = sa_nxt;
+                }
                 }
             }
+        }
+        };
+        // one instance per count of live blocks (each straight-line; a
+        // wavefront whose blocks all lie past the tile's rows still loads
+        // its share of the stages and keeps the barriers, without MFMAs)
+        if (__builtin_expect(nlive == TB, 1))
+            k_loop(std::integral_constant<int, TB>{});
+        else if constexpr (TB >= 4) {
+            if (nlive == 3)
+                k_loop(std::integral_constant<int, (TB >= 4 ? 3 : 0)>{});
+            else if (nlive == 2)
+                k_loop(std::integral_constant<int, (TB >= 4 ? 2 : 0)>{});
+            else if (nlive == 1)
+                k_loop(std::integral_constant<int, 1>{});
+            else
+                k_loop(std::integral_constant<int, 0>{});
+        } else if constexpr (TB == 2) {
+            if (nlive == 1)
+                k_loop(std::integral_constant<int, 1>{});
+            else
+                k_loop(std::integral_constant<int, 0>{});
+        } else {
+            k_loop(std::integral_constant<int, 0>{});
         }
 
         // epilogue: lane holds tile row (wm BM/NWM + 16j + i16), weight rows
@@ -576,16 +623,52 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(int32_t *p, int n)
         p[i] = 0;
 }
 
+// Row chunk q and N tile nt of grid-stride item `item` (workgroup blockIdx.x
+// of a launch whose workgroup b runs on XCD b mod 8).  With bq = 0 items go
+// chunk-major (item = q * NT + nt).  With bq > 0 the (chunk, N tile) grid is
+// cut into blocks of bq chunks x bnt N tiles (clipped at the edges), blocks
+// row-major, items row-major inside a block; in every full round of the
+// grid-stride loop the G / 8 workgroups of one XCD take consecutive items
+// of that order, so the workgroups that share an XCD's L2 work on one block
+// at a time: each activation tile is read by bnt of them, each weight tile
+// by bq (chunk-major, an XCD's workgroups hold ~G / 8 / 3 chunks x 3 N
+// tiles of each round).  The last, partial round keeps the plain order.
+// A bijection of [0, items) onto the grid, every q < nchunks and nt < NT.
+__device__ __forceinline__ void tile_of_item(long item, long items, int nchunks, int NT, int bq,
+                                             int bnt, int &q, int &nt)
+{
+    long e = item;
+    const long G = gridDim.x;
+    const long base = item - blockIdx.x;
+    if (bq > 0 && (G & 7) == 0 && base + G <= items)
+        e = base + (long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (bq <= 0) {
+        q = (int)(e / NT);
+        nt = (int)(e - (long)q * NT);
+        return;
+    }
+    const long per_row = (long)bq * NT;
+    const int qb = (int)(e / per_row);
+    long rem = e - (long)qb * per_row;
+    const int rows_q = min(bq, nchunks - qb * bq);
+    const int nb = (int)(rem / (rows_q * bnt));
+    rem -= (long)nb * rows_q * bnt;
+    const int w = min(bnt, NT - nb * bnt);
+    q = qb * bq + (int)(rem / w);
+    nt = nb * bnt + (int)(rem % w);
+}
+
 template <bool kGemm1, int BM, int BN, int KU, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_tiled_kernel(Shape s, TiledArgs g)
+gemm_tiled_kernel(Shape s, TiledArgs g, int bq, int bnt)
 {
     __shared__ TileShared<BM, BN, KU> sh;
     const int NT = kGemm1 ? s.I / (BN / 2) : s.H / BN;
     const int nchunks = plan_chunks<NW * 64>(s, g.counts, BM, sh.prefix);
     const long items = (long)nchunks * NT;
     for (long item = blockIdx.x; item < items; item += gridDim.x) {
-        const int q = (int)(item / NT), nt = (int)(item - (long)q * NT);
+        int q, nt;
+        tile_of_item(item, items, nchunks, NT, bq, bnt, q, nt);
         tiled_item<kGemm1, BM, BN, KU, false, NW>(s, g, sh.prefix, sh.arow, sh.ring, q, nt);
         __syncthreads();
     }
@@ -729,8 +812,17 @@ hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *
     auto k = gemm_tiled_kernel<kGemm1, BM, BN, KU, NW>;
     const long nt = kGemm1 ? sh.I / (BN / 2) : sh.H / BN;
     const int grid = tiled_grid(k, tile_upper_bound(sh, BM) * nt, NW * 64);
+    // MFMA-bound tiles (weight tiles reused by several row chunks) take the
+    // blocked item order: an XCD's grid / 8 workgroups of a round share
+    // 8 N tiles (or all, when fewer) and grid / 64 row chunks
+    int bq = 0, bnt = 0;
+    if (BM >= 128 && grid % 8 == 0) {
+        bnt = nt < 8 ? (int)nt : 8;
+        bq = grid / 8 / bnt > 1 ? grid / 8 / bnt : 1;
+    }
     k<<<grid, NW * 64, 0, st>>>(to_dev(sh),
-                                 TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs, y});
+                                 TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs, y},
+                                 bq, bnt);
     return hipGetLastError();
 }
 

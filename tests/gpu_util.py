@@ -192,7 +192,8 @@ def gemm1_mfma_bound(case: dict, routes: np.ndarray) -> np.ndarray:
         au[sel] = np.abs(x[sel]) @ np.abs(W[I:]).T
     gc = np.minimum(g, spec.gate_limit)
     uc = np.clip(u, -spec.up_limit, spec.up_limit)
-    silu = gc / (1.0 + np.exp(-gc))
+    with np.errstate(over="ignore"):
+        silu = gc / (1.0 + np.exp(-gc))
     return 1.1 * np.abs(uc) * 2.0 ** -9 * ag + np.abs(silu) * 2.0 ** -9 * au
 
 
