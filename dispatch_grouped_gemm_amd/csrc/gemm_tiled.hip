@@ -21,9 +21,9 @@
 // stages in LDS at two workgroups per CU, two of them in flight: a stage's
 // weight loads go out last, and the wait before a stage leaves the next
 // stage's weight loads outstanding.
-// GEMM1 past 512 expected rows per expert takes 256 x 256 tiles on eight
-// wavefronts, one workgroup per CU: the two 128-row halves share one weight
-// stage, so a CU moves 48 KB per K step for 256 MFMAs instead of 64 KB.
+// Past 512 expected rows per expert both GEMMs take 256 x 256 tiles on
+// eight wavefronts, one workgroup per CU: the two 128-row halves share one
+// weight stage, so a CU moves 48 KB per K step for 256 MFMAs instead of 64 KB.
 //
 // GEMM1 tile: BN/2 intermediate columns.  Each wavefront holds BN/4 of them
 // as BN/64 gate groups and the matching up groups, so the clamped SwiGLU and
@@ -713,12 +713,9 @@ static double per_expert_rows(const moe_shape &s)
 //   tenth of the slots -1 (57 rows per expert on average) the 64-row tiles
 //   still win, 334 against 360 us for GEMM1; with no -1 slots (64 rows) the
 //   128-row tiles win, 354 against 434 us;
-// - 128-row tiles above, and 256-row tiles for GEMM1 from 512 (measured in
-//   the layer at 65,536 tokens: GEMM1 -8% with Zipf routing, +4 to +6% with
-//   uniform routing or one hot expert, where GEMM2 then runs 5-6% faster; the
-//   layer -5%, +0.5%, -0.5%).  GEMM2 keeps 128-row tiles: its 256-row tile
-//   (ring grown to the 135 KB y tile) took the layer -4% with Zipf routing
-//   but +1.5% with uniform routing; the tuned table can name it.
+// - 128-row tiles above, and 256-row tiles from 512 (eight wavefronts, one
+//   workgroup per CU; at 65,536 tokens, GEMM alone: GEMM1 1,999 against
+//   2,151 us for 128 x 256 tiles, GEMM2 1,115 against 1,186).
 // The host sees neither the -1 slots nor the skew, so shapes near the bounds
 // are left to the tuned table.  tiled_bm gives the class (64 or 128),
 // tiled_config the tile.
@@ -796,7 +793,7 @@ TiledConfig tiled_config(const moe_shape &s, bool gemm1)
     const double per_expert = per_expert_rows(s);
     if (bm == 64)
         return per_expert <= 16.0 ? TiledConfig{32, 128, 2} : TiledConfig{64, 128, 2};
-    if (gemm1 && bn == 256 && per_expert >= 512.0)
+    if (bn == 256 && per_expert >= 512.0)
         return {256, 256, 1};
     return {bm, bn, 1};
 }

@@ -291,7 +291,7 @@ int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *w
  * (128, 256, 1), (256, 256, 1).  A call takes the entry of its GEMM and
  * shape with the smallest max_tokens >= T; with none, the built-in rule
  * (by the expected rows per expert T*K/E_total: 32-row tiles up to 16,
- * 64-row up to 96, else 128-row, and 256-row for GEMM1 from 512).  Every
+ * 64-row up to 96, else 128-row, and 256-row from 512).  Every
  * tile gives the same bits (the K order of each sum does not depend on it).  The table applies where the tiled kernels run (H or I at
  * least 512); an entry whose N tile does not divide the output columns
  * (GEMM1: I by bn/2, GEMM2: H by bn) is passed over.

@@ -174,9 +174,10 @@ def test_tile_table(lib):
     t2k = moe.MoeShape(**{**V4, "T": 2048})                  # 32 rows per expert: 64-row tiles
     assert tuple(moe.get_tile_config(t2k, 2)[k] for k in ("bm", "bn", "ku")) == (64, 128, 2)
     pre = moe.MoeShape(**{**V4, "T": 65536})
-    assert moe.get_tile_config(pre, 2)["bm"] == 128
-    # GEMM1 from 512 expected rows per expert: 256 x 256 tiles (GEMM2 by the table only)
-    assert tuple(moe.get_tile_config(pre, 1)[k] for k in ("bm", "bn", "ku")) == (256, 256, 1)
+    # both GEMMs from 512 expected rows per expert: 256 x 256 tiles
+    for gemm in (1, 2):
+        assert tuple(moe.get_tile_config(pre, gemm)[k] for k in ("bm", "bn", "ku")) == \
+            (256, 256, 1)
     mid = moe.MoeShape(**{**V4, "T": 16384})                 # 256 rows per expert
     assert tuple(moe.get_tile_config(mid, 1)[k] for k in ("bm", "bn", "ku")) == (128, 256, 1)
     base = dict(gemm=1, H=7168, I=3072, K=6, E_total=384, E_local=48)
