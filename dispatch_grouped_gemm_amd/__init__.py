@@ -25,7 +25,8 @@ __all__ = [
     "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
     "moe_dispatch_workspace_size", "moe_workspace_size", "moe_workspace_status_offset",
     "workspace_status", "moe_dispatch", "moe_gemm1_swiglu",
-    "moe_gemm2", "moe_combine", "moe_forward", "moe_forward_persistent", "moe_strerror",
+    "moe_gemm2", "moe_combine", "moe_forward", "moe_forward_persistent", "moe_forward_static",
+    "moe_static_scratch_bytes", "moe_forward_static_need", "moe_strerror",
     "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT",
 ]
@@ -40,7 +41,8 @@ EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size"
             "moe_workspace_size", "moe_workspace_status_offset", "moe_dispatch",
             "moe_gemm1_swiglu", "moe_gemm2",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
-            "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_set_tile_table",
+            "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_forward_static",
+            "moe_static_scratch_bytes", "moe_forward_static_need", "moe_set_tile_table",
             "moe_get_tile_config", "moe_strerror"]
 
 
@@ -151,6 +153,12 @@ def lib() -> ctypes.CDLL:
         h.moe_set_tile_table.restype = ctypes.c_int
         h.moe_get_tile_config.argtypes = [S, ctypes.c_int32, ctypes.POINTER(TileEntry)]
         h.moe_get_tile_config.restype = ctypes.c_int
+        h.moe_forward_static.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        h.moe_forward_static.restype = ctypes.c_int
+        h.moe_static_scratch_bytes.argtypes = []
+        h.moe_static_scratch_bytes.restype = ctypes.c_size_t
+        h.moe_forward_static_need.argtypes = [S]
+        h.moe_forward_static_need.restype = ctypes.c_size_t
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -438,6 +446,36 @@ def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scal
     fn, name = ((lib().moe_forward_persistent, "moe_forward_persistent") if persistent
                 else (lib().moe_forward, "moe_forward"))
     _check(fn(ctypes.byref(c), *args, ws, workspace.numel(), _stream(stream, dev)), name)
+
+
+def moe_forward_static(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2,
+                       w2_scale, out_bf16, stream=None):
+    """moe_forward with the library's static device scratch as its workspace
+    (the entry point for callers that cannot allocate)."""
+    dev = x_fp8.device
+    T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev),
+            _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev),
+            _ptr(topk_ids, "topk_ids", (T, K), {torch.int32}, dev),
+            _ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
+            _ptr(w13, "w13", (E, 2 * I, H // 2), _fp4(), dev),
+            _ptr(w13_scale, "w13_scale", (E, 2 * I, H // 32), _e8m0("w13_scale"), dev),
+            _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
+            _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
+            _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
+    c = shape.c()
+    _check(lib().moe_forward_static(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_forward_static")
+
+
+def moe_static_scratch_bytes() -> int:
+    return int(lib().moe_static_scratch_bytes())
+
+
+def moe_forward_static_need(shape: MoeShape) -> int:
+    c = shape.c()
+    return int(lib().moe_forward_static_need(ctypes.byref(c)))
 
 
 def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out_bf16,

@@ -2,6 +2,8 @@
 // launch), workspace layout and the launch sequence.
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_common.hpp"
 
 namespace {
@@ -62,6 +64,38 @@ Layout layout_of(const moe_shape &s)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// ---------------------------------------------------------------------------
+// Scratch of moe_forward_static: the moe_forward workspace as a file-scope
+// device array, for callers that cannot allocate.  Each device the library
+// runs on holds its own copy until the process ends.  On the host the
+// array's name stands for no device address: its address on a device comes
+// from hipGetSymbolAddress with that device current, once per device, and
+// only that pointer is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, or nullptr.
+void *static_scratch(int *dev_out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 hipStream_t as_stream(void *p) { return static_cast<hipStream_t>(p); }
 
@@ -245,7 +279,7 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
                  const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                  const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
                  bool persistent, const uint16_t *x_bf16 = nullptr,
-                 const int32_t *valid = nullptr)
+                 const int32_t *valid = nullptr, size_t need_bytes = 0)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
@@ -268,7 +302,7 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
     }
     if (!ids || !tw || !w13 || !w13s || !w2 || !w2s || !out || (!x_bf16 && (!x || !xs)))
         return MOE_EINVAL;
-    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
+    if (!ws || ws_bytes < (need_bytes ? need_bytes : L.total) || ((uintptr_t)ws % kAlign) != 0)
         return MOE_EWORKSPACE;
     if (!all_aligned16(x, xs, w13, w13s, w2, w2s, out))
         return MOE_EINVAL;
@@ -310,6 +344,36 @@ int moe_forward(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const i
                 const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
 {
     return forward_impl(s, x, xs, ids, tw, w13, w13s, w2, w2s, out, ws, ws_bytes, stream, false);
+}
+
+size_t moe_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+size_t moe_forward_static_need(const moe_shape *s)
+{
+    if (moe_check_shape(s) != MOE_OK)
+        return 0;
+    // the MX FP8 path uses the workspace up to the bf16-input area
+    return layout_of(*s).xq;
+}
+
+int moe_forward_static(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
+                       const int32_t *ids, const float *tw, const uint8_t *w13,
+                       const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s, uint16_t *out,
+                       void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (layout_of(*s).xq > kStaticScratchBytes)
+        return MOE_ESCRATCH;
+    int dev = -1;
+    void *ws = static_scratch(&dev);
+    if (!ws)
+        return MOE_EHIP;
+    return forward_impl(s, x, xs, ids, tw, w13, w13s, w2, w2s, out, ws, kStaticScratchBytes,
+                        stream, false, nullptr, nullptr, layout_of(*s).xq);
 }
 
 int moe_forward_persistent(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
@@ -380,6 +444,9 @@ const char *moe_strerror(int code)
         return "workspace missing, too small or not 256-byte aligned";
     case MOE_EHIP:
         return "HIP launch failed";
+    case MOE_ESCRATCH:
+        return "shape needs more than the static scratch of moe_forward_static "
+               "(moe_forward_static_need > moe_static_scratch_bytes)";
     default:
         return "unknown error";
     }

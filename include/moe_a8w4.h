@@ -79,6 +79,7 @@ extern "C" {
 #define MOE_ENOTSUP (-2)    /* shape outside what the kernels support */
 #define MOE_EWORKSPACE (-3) /* workspace missing or too small */
 #define MOE_EHIP (-4)       /* a HIP launch or query failed */
+#define MOE_ESCRATCH (-5)   /* moe_forward_static: shape too large for its scratch */
 
 #define MOE_DISPATCH_COMPACT 0    /* histogram, scan, stable scatter */
 #define MOE_DISPATCH_FIXED_SLOT 1 /* atomic claim into per-expert capacity */
@@ -238,6 +239,34 @@ int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const u
                            const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
                            uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and result as moe_forward without the workspace, which
+ * is a file-scope device array of moe_static_scratch_bytes() (128 MiB)
+ * inside the library instead.  Each GPU the library runs on holds its own
+ * copy of that array until the process ends; the first call on a device
+ * looks up its address there.  The call allocates nothing and launches the
+ * kernels of moe_forward on `stream`.  Shapes whose workspace
+ * (moe_forward_static_need) exceeds the array are refused with
+ * MOE_ESCRATCH before any launch: the V4 shape (H 7168, I 3072, 48 local
+ * experts) fits up to 159 fixed slots per expert, or 1,277 tokens with
+ * compact dispatch.  Every call on one GPU shares that GPU's array (no part of which
+ * needs clearing: each call writes what it reads), so calls that overlap
+ * on one GPU -- on two streams, or from two threads -- race.
+ */
+int moe_forward_static(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
+                       const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,
+                       const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
+                       uint16_t *out_bf16, void *stream);
+
+/* Bytes of moe_forward_static's scratch array. */
+size_t moe_static_scratch_bytes(void);
+
+/* Scratch bytes moe_forward_static needs for a shape (0 for a refused
+ * shape); the call is refused when this exceeds moe_static_scratch_bytes(). */
+size_t moe_forward_static_need(const moe_shape *shape);
 
 /*
  * The layer from bf16 activations (the pages' small-input path fuses the

@@ -67,6 +67,22 @@ def test_32bit_offset_limits(lib):
     assert moe.moe_check_shape(moe.MoeShape(**{**V4, "T": 1, "H": 1 << 16, "I": 1 << 16})) == -2
 
 
+def test_static_scratch_sizes_and_refusal(lib):
+    """moe_forward_static: its scratch size, the bytes a shape needs, and the
+    refusal of a shape past it, before any launch (no GPU is touched: the
+    check runs first, so null buffers are never read)."""
+    cap = moe.moe_static_scratch_bytes()
+    assert cap == 128 << 20
+    dec = moe.MoeShape(**V4, dispatch_mode=1, capacity=128)
+    assert 0 < moe.moe_forward_static_need(dec) <= cap
+    assert moe.moe_forward_static_need(moe.MoeShape(**{**V4, "K": 0})) == 0
+    big = moe.MoeShape(**{**V4, "T": 2048})
+    assert moe.moe_forward_static_need(big) > cap
+    c = big.c()
+    assert lib.moe_forward_static(ctypes.byref(c), *([None] * 9), None) == -5
+    assert "static scratch" in moe.moe_strerror(-5)
+
+
 def test_sizes(lib):
     s = moe.MoeShape(**V4, dispatch_mode=1, capacity=128)
     assert moe.moe_row_capacity(s) == 48 * 128
