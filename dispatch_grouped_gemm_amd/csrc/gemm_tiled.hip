@@ -443,7 +443,18 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         }
 
         // epilogue: lane holds tile row (wm BM/NWM + 16j + i16), weight rows
-        // 4kq..4kq+3 of each of its GW groups
+        // 4kq..4kq+3 of each of its GW groups.  On the 128- and 256-row
+        // tiles its thread indices come from an opaque copy of the thread id,
+        // so the compiler recomputes the epilogue's LDS and global addresses
+        // here instead of hoisting them out of the item loop and holding them
+        // (spilled, 4 to 46 registers) across the K loop.
+        int tid_e = tid;
+        if constexpr (BM >= 128)
+            asm volatile("" : "+v"(tid_e));
+        {
+        const int tid = tid_e, lane = tid & 63, wave = tid >> 6;
+        const int i16 = lane & 15, kq = lane >> 4;
+        const int wn = wave & 1, wm = wave >> 1;
         if constexpr (kGemm1) {
             constexpr int CB = GW / 2;   // 16-column blocks of h per wavefront
             // the h codes go through LDS (rows of BN/2 + 16 bytes, so the
@@ -521,6 +532,7 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                     *reinterpret_cast<u32x4 *>(y_out + (size_t)(row0 + r) * (size_t)H +
                                                (size_t)nt * BN + 8 * c) = lds_read16(lds + r * PITCH + 16 * c);
             }
+        }
         }
     }
 }
