@@ -7,8 +7,9 @@ float32 accumulation, no fast-math); this module only loads it and marshals
 numpy arrays.
 
 Parity status: decode tables, the e4m3 encoder, bf16 rounding, dispatch,
-the single-step checkers (GEMM2 of given rows, combine of given rows) and
-the whole layer are pinned by the ``-m "not gpu"`` tests (closed forms,
+the single-step checkers (GEMM2 of given rows, combine of given rows, the
+MX FP8 quant of float32 rows and the combine of MX FP8 rows) and the whole
+layer, with float32 or MX FP8 expert output rows, are pinned by the ``-m "not gpu"`` tests (closed forms,
 exhaustive code sweeps, torch's own float8/bfloat16 casts, brute-force
 nearest search, a float64 dense evaluation, a numpy float32 combine loop
 and invariants).
@@ -213,9 +214,11 @@ def expert_ffn_gu(case: dict, t: int, e: int) -> np.ndarray:
 
 
 def moe_layer(case: dict, tokens: Optional[np.ndarray] = None,
-              num_valid: Optional[int] = None) -> np.ndarray:
+              num_valid: Optional[int] = None, y_fp8: bool = False) -> np.ndarray:
     """bf16 bits (uint16) of the layer output rows of ``tokens`` (all if None);
-    num_valid marks rows past it as padding (no routes, +0 rows)."""
+    num_valid marks rows past it as padding (no routes, +0 rows).  y_fp8:
+    every route's expert output row reaches the combine as MX FP8 (1x32)
+    instead of float32 (orc_moe_layer_y8)."""
     if num_valid is not None:
         case = dict(case, topk_ids=pad_rows(case["topk_ids"], num_valid))
     spec = case["spec"]
@@ -227,9 +230,10 @@ def moe_layer(case: dict, tokens: Optional[np.ndarray] = None,
         tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
         n, tok_p = tok.size, _p(tok)
     out = np.zeros((max(n, 1), spec.H), np.uint16)
-    rc = lib().orc_moe_layer(ctypes.byref(s), _p(case["x_fp8"]), _p(case["x_scale"]),
-                             _p(case["topk_ids"]), _p(case["topk_w"]), _p(w13), _p(w13s),
-                             _p(w2), _p(w2s), tok_p, ctypes.c_int(n), _p(out))
+    fn = lib().orc_moe_layer_y8 if y_fp8 else lib().orc_moe_layer
+    rc = fn(ctypes.byref(s), _p(case["x_fp8"]), _p(case["x_scale"]), _p(case["topk_ids"]),
+            _p(case["topk_w"]), _p(w13), _p(w13s), _p(w2), _p(w2s), tok_p, ctypes.c_int(n),
+            _p(out))
     assert rc == 0
     return out[:n]
 
@@ -264,4 +268,29 @@ def combine(spec, topk_w: np.ndarray, route_row: np.ndarray, y: np.ndarray) -> n
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.zeros((max(spec.T, 1), spec.H), np.uint16)
     lib().orc_combine(ctypes.byref(s), _p(tw), _p(rr), _p(y), _p(out))
+    return out[:spec.T]
+
+
+def quant_rows_f32(y: np.ndarray):
+    """MX FP8 of float32 rows y [n, H] (the 1x32 rule of the requant): e4m3
+    codes [n, H] and exponent bytes [n, H/32]."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    n, H = y.shape
+    codes = np.zeros((max(n, 1), H), np.uint8)
+    scales = np.zeros((max(n, 1), H // 32), np.uint8)
+    lib().orc_quant_rows_f32(_p(y), ctypes.c_int64(n), ctypes.c_int32(H), _p(codes), _p(scales))
+    return codes[:n], scales[:n]
+
+
+def combine_fp8(spec, topk_w: np.ndarray, route_row: np.ndarray, y_codes: np.ndarray,
+                y_scale: np.ndarray) -> np.ndarray:
+    """bf16 bits [T, H] of the combine of given MX FP8 rows (codes [R, H],
+    exponent bytes [R, H/32])."""
+    s = shape_of(spec)
+    tw = np.ascontiguousarray(topk_w, dtype=np.float32)
+    rr = np.ascontiguousarray(route_row, dtype=np.int32)
+    yc = np.ascontiguousarray(y_codes, dtype=np.uint8)
+    ys = np.ascontiguousarray(y_scale, dtype=np.uint8)
+    out = np.zeros((max(spec.T, 1), spec.H), np.uint16)
+    lib().orc_combine_fp8(ctypes.byref(s), _p(tw), _p(rr), _p(yc), _p(ys), _p(out))
     return out[:spec.T]

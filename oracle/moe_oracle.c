@@ -21,7 +21,11 @@
  *   out[t,:] = bf16( sum over k ascending, id local:
  *                    w[t,k] * W2_e . Q8( SwiGLU_clamp( W13_e . x_t ) ) )
  * with x, W13, W2 the MX-decoded values and Q8 the FP8 1x32 quantise /
- * dequantise of the intermediate.  Readings where the pages are silent:
+ * dequantise of the intermediate.  orc_moe_layer_y8 also passes each
+ * route's expert output row through Q8 (per 32 output columns) before the
+ * weighted sum: the FP8 rows a rank with many rows sends to the combine
+ * ("MegaMoEV2 ...", Technical Details, skewed routing, small input).
+ * Readings where the pages are silent:
  *   - W13 rows 0..I-1 are the gate, I..2I-1 the up projection;
  *   - FP4 pairs: the low nibble holds the even K index;
  *   - FP8 is OCP E4M3FN (bias 7, no infinities, max 448);
@@ -183,6 +187,20 @@ ORC_EXPORT void orc_quant_mxfp8(const uint16_t *x, int64_t rows, int32_t H, uint
             orc_mx8_quant_block(v, codes + t * H + 32 * b, scales + t * (H / 32) + b);
         }
     }
+}
+
+/* float32 rows to MX FP8 by the same 1x32 rule: every 32 consecutive
+ * values of a row through orc_mx8_quant_block (codes [rows, H], exponent
+ * bytes [rows, H/32]). */
+ORC_EXPORT void orc_quant_rows_f32(const float *y, int64_t rows, int32_t H, uint8_t *codes,
+                                   uint8_t *scales)
+{
+    int64_t t;
+    int32_t b;
+    for (t = 0; t < rows; ++t)
+        for (b = 0; b < H / 32; ++b)
+            orc_mx8_quant_block(y + t * H + 32 * b, codes + t * H + 32 * b,
+                                scales + t * (H / 32) + b);
 }
 
 /* Clamped SwiGLU of one (gate, up) pair. */
@@ -386,10 +404,10 @@ ORC_EXPORT void orc_expert_ffn_hv(const orc_shape *s, const uint8_t *xrow, const
  * into out[ntok, H] as bf16 bits.  Each route is evaluated on its own, in k
  * order; the weighted sum is kept in float32 and rounded once.  Fixed-slot
  * capacity is not modelled: callers check that no route overflowed. */
-ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
-                             const int32_t *ids, const float *tw, const uint8_t *w13,
-                             const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
-                             const int32_t *tok, int ntok, uint16_t *out)
+static int moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
+                     const int32_t *ids, const float *tw, const uint8_t *w13,
+                     const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                     const int32_t *tok, int ntok, int y_fp8, uint16_t *out)
 {
     const int H = s->H, K = s->K;
     int n_items = tok ? ntok : s->T;
@@ -399,6 +417,8 @@ ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t
         int t = tok ? tok[it] : it;
         float *o = (float *)calloc((size_t)H, sizeof(float));
         float *y = (float *)malloc(sizeof(float) * (size_t)H);
+        uint8_t *yc = (uint8_t *)malloc((size_t)H);
+        uint8_t *ys = (uint8_t *)malloc((size_t)H / 32);
         int k, n;
         for (k = 0; k < K; ++k) {
             int e = route_expert(s, ids[(size_t)t * K + k]);
@@ -407,6 +427,13 @@ ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t
                 continue;
             orc_expert_ffn(s, x + (size_t)t * H, xs + (size_t)t * (H / 32), e, w13, w13s, w2,
                            w2s, NULL, NULL, NULL, y);
+            if (y_fp8) {
+                /* the route's row goes to the combine as MX FP8: quantise
+                 * per 32 columns, then every value decoded exactly */
+                orc_quant_rows_f32(y, 1, H, yc, ys);
+                for (n = 0; n < H; ++n)
+                    y[n] = orc_e4m3_decode(yc[n]) * orc_e8m0_decode(ys[n / 32]);
+            }
             for (n = 0; n < H; ++n) {
                 float p = w * y[n];
                 o[n] = o[n] + p;
@@ -416,8 +443,35 @@ ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t
             out[(size_t)it * H + n] = orc_bf16_encode(o[n]);
         free(o);
         free(y);
+        free(yc);
+        free(ys);
     }
     return 0;
+}
+
+ORC_EXPORT int orc_moe_layer(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
+                             const int32_t *ids, const float *tw, const uint8_t *w13,
+                             const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                             const int32_t *tok, int ntok, uint16_t *out)
+{
+    return moe_layer(s, x, xs, ids, tw, w13, w13s, w2, w2s, tok, ntok, 0, out);
+}
+
+/* The layer with each route's expert output row sent to the combine as MX
+ * FP8 instead of float32 ("MegaMoEV2: fuse Dispatch, GEMM1, GEMM2 and
+ * Combine into one kernel", Technical Details, skewed routing on the small
+ * input: a rank with many rows or a large expert sends its GEMM2 rows to
+ * the combine in the main path's 1x32 FP8 format instead of BF16).  Read
+ * here as: the float32 row y of a route through orc_quant_rows_f32 (the
+ * rule of the intermediate's requant, per 32 consecutive output columns),
+ * then the decoded values take y's place in the same weighted float32 sum,
+ * rounded once. */
+ORC_EXPORT int orc_moe_layer_y8(const orc_shape *s, const uint8_t *x, const uint8_t *xs,
+                                const int32_t *ids, const float *tw, const uint8_t *w13,
+                                const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
+                                const int32_t *tok, int ntok, uint16_t *out)
+{
+    return moe_layer(s, x, xs, ids, tw, w13, w13s, w2, w2s, tok, ntok, 1, out);
 }
 
 /* Per-route intermediates for step checks: for the routes r_list[0..n),
@@ -500,6 +554,35 @@ ORC_EXPORT int orc_gemm2_rows(const orc_shape *s, const uint8_t *h_codes, const 
         free(hq);
     }
     return bad ? -1 : 0;
+}
+
+/* Combine of given MX FP8 rows (codes [R, H], exponent bytes [R, H/32]):
+ * as orc_combine on the decoded values, each decoded exactly in float32
+ * (e4m3 value times 2^(byte - 127)). */
+ORC_EXPORT int orc_combine_fp8(const orc_shape *s, const float *tw, const int32_t *route_row,
+                               const uint8_t *y_codes, const uint8_t *y_scale, uint16_t *out)
+{
+    const int H = s->H, K = s->K;
+    int t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < s->T; ++t) {
+        int n, k;
+        for (n = 0; n < H; ++n) {
+            float o = 0.0f;
+            for (k = 0; k < K; ++k) {
+                int32_t row = route_row[(size_t)t * K + k];
+                float v, p;
+                if (row < 0)
+                    continue;
+                v = orc_e4m3_decode(y_codes[(size_t)row * H + n]) *
+                    orc_e8m0_decode(y_scale[(size_t)row * (H / 32) + n / 32]);
+                p = tw[(size_t)t * K + k] * v;
+                o = o + p;
+            }
+            out[(size_t)t * H + n] = orc_bf16_encode(o);
+        }
+    }
+    return 0;
 }
 
 /* Combine of given float32 rows y[R, H]: out[t] = bf16(sum over k

@@ -565,3 +565,179 @@ def test_combine_matches_a_numpy_float32_loop(seed):
     # a token with no kept route is +0
     none = (d["route_row"].reshape(spec.T, spec.K) < 0).all(axis=1)
     assert none.any() and not got[none].any()
+
+
+# ------------------------------------------------------ FP8 y rows ----
+
+def _torch_e4m3(codes):
+    """float32 values of e4m3 codes by torch's own float8_e4m3fn cast."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).float().numpy()
+
+
+def _mx8_rows_decoded(codes, scales):
+    """float32 values of MX FP8 rows: torch's e4m3 decode times 2^(byte - 127)
+    by numpy's ldexp (exact here: every value used is a float32)."""
+    e = np.repeat(scales.astype(np.int32) - 127, 32, axis=1)
+    return np.ldexp(_torch_e4m3(codes), e).astype(np.float32)
+
+
+def _mx8_rows_top_binade(rng, n, H, lo=0, hi=246):
+    """Random MX FP8 rows whose every block has its largest magnitude in
+    [256, 448], the top e4m3 binade, where the 1x32 rule puts the block's
+    exponent; exponent bytes in [lo, hi] (448 * 2^119 is below the float32
+    maximum)."""
+    codes = rng.integers(0, 256, size=(n, H)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01      # no NaN codes
+    for r in range(n):
+        for b in range(H // 32):
+            j = 32 * b + rng.integers(0, 32)
+            codes[r, j] = (0x78 | rng.integers(0, 7)) | (0x80 * rng.integers(0, 2))
+    scales = rng.integers(lo, hi + 1, size=(n, H // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def test_quant_rows_f32_round_trips_mx8_rows():
+    """Rows of e4m3 values times 2^E per block, each block topping out in
+    [256, 448], come back as the same codes and exponent bytes (a misplaced
+    exponent index, a transposed block, another exponent rule or another
+    rounding changes them), and their FP8 combine is the float32 combine of
+    the same values, bit for bit."""
+    rng = np.random.default_rng(21)
+    codes, scales = _mx8_rows_top_binade(rng, 11, 256)
+    scales[0, 0], scales[0, 1], scales[1, 2] = 0, 246, 127
+    y = _mx8_rows_decoded(codes, scales)
+    c2, s2 = oracle.quant_rows_f32(y)
+    np.testing.assert_array_equal(s2, scales)
+    np.testing.assert_array_equal(c2, codes)
+    spec = synth.CaseSpec("comb8", T=5, H=256, I=256, E_total=4, E_local=4, K=3)
+    rr = np.array([0, 1, 2, 3, -1, 4, 5, 6, 7, 8, -1, -1, 9, 10, -1], np.int32)
+    w = rng.standard_normal((spec.T, spec.K)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.combine_fp8(spec, w, rr, codes, scales),
+                                  oracle.combine(spec, w, rr, y))
+
+
+def test_quant_rows_f32_against_brute_force_nearest_code():
+    """Random float32 rows (magnitudes spread over many binades, zero and -0
+    blocks): per block the exponent puts amax / 2^E in [256, 512), and every
+    code is the brute-force nearest e4m3 value of y / 2^E (ties to even,
+    saturating at 448), also torch's cast of the clipped value."""
+    rng = np.random.default_rng(22)
+    n, H = 6, 160
+    y = (rng.standard_normal((n, H)) * np.exp2(rng.integers(-30, 30, size=(n, H // 32)).repeat(32, 1))
+         * np.exp2(rng.uniform(-4, 0, size=(n, H)))).astype(np.float32)
+    y[0, 32:64] = 0.0
+    y[1, 64:96] = -0.0
+    y[2, 5] = 0.0
+    y[3, 96:128] = np.float32(448.0 * 2.0 ** -10)       # exactly representable
+    codes, scales = oracle.quant_rows_f32(y)
+    ecodes, evals = _e4m3_finite_table()
+    for r in range(n):
+        for b in range(H // 32):
+            blk = y[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert scales[r, b] == 127 and not codes[r, 32 * b:32 * b + 32].any()
+                continue
+            E = int(scales[r, b]) - 127
+            assert 256.0 <= amax / 2.0 ** E < 512.0
+            want = _brute_force_e4m3(blk / 2.0 ** E, ecodes, evals)
+            np.testing.assert_array_equal(codes[r, 32 * b:32 * b + 32].astype(np.int64), want)
+            t = torch.from_numpy(np.clip(blk / 2.0 ** E, -448, 448).astype(np.float32))
+            np.testing.assert_array_equal(codes[r, 32 * b:32 * b + 32],
+                                          t.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_combine_fp8_matches_a_numpy_float32_loop(seed):
+    """The FP8 combine against torch's e4m3 decode, numpy's ldexp and a
+    numpy float32 loop over ascending k, with -1, invalid and foreign slots
+    skipped and cancelling terms (s, then w*Y and w*(-Y) with |Y| near 2^22)
+    that expose another k order, a fused multiply-add, a product taken
+    before the exponent, or an extra rounding."""
+    rng = np.random.default_rng(30 + seed)
+    spec = synth.CaseSpec("comb8", T=37, H=256, I=256, E_total=9, E_local=7, expert_begin=1,
+                          K=8, dispatch_mode=seed, capacity=40)
+    ids = rng.integers(-1, spec.E_total + 2, size=(spec.T, spec.K)).astype(np.int32)
+    ids[0] = -1
+    w = (rng.standard_normal((spec.T, spec.K)) * 3).astype(np.float32)
+    d = oracle.dispatch(spec, ids)
+    R = oracle.row_capacity(spec)
+    codes, scales = _mx8_rows_top_binade(rng, R, spec.H, lo=60, hi=180)
+    rr = d["route_row"].reshape(spec.T, spec.K)
+    for t in range(spec.T):
+        kept = np.nonzero(rr[t] >= 0)[0]
+        if kept.size < 3:
+            continue
+        ka, kb, kc = kept[:3]
+        scales[rr[t, ka]] = 127 - 8
+        scales[rr[t, kb]] = 127 + 14             # values up to 448 * 2^14 ~ 2^22.8
+        scales[rr[t, kc]] = 127 + 14
+        codes[rr[t, kc]] = codes[rr[t, kb]] ^ 0x80
+        w[t, kc] = w[t, kb]
+    got = oracle.combine_fp8(spec, w, d["route_row"], codes, scales)
+    want = _combine_numpy(spec, w, d["route_row"], _mx8_rows_decoded(codes, scales))
+    np.testing.assert_array_equal(got, want)
+    none = (rr < 0).all(axis=1)
+    assert none.any() and not got[none].any()
+
+
+def test_layer_y8_is_quant_then_fp8_combine():
+    """The FP8-y layer is each route's float32 y quantised per 32 columns,
+    placed by the dispatch's route_row and combined from FP8, bit for bit."""
+    case = _case(seed=1013)
+    spec = case["spec"]
+    d = oracle.dispatch(spec, case["topk_ids"])
+    rr = d["route_row"]
+    routes = np.nonzero(rr >= 0)[0]
+    ffn = oracle.routes_ffn(case, routes)
+    R = oracle.row_capacity(spec)
+    yc = np.full((R, spec.H), 0x7F, np.uint8)     # NaN codes in rows nobody owns
+    ys = np.full((R, spec.H // 32), 255, np.uint8)
+    yc[rr[routes]], ys[rr[routes]] = oracle.quant_rows_f32(ffn["y"])
+    got = oracle.moe_layer(case, y_fp8=True)
+    np.testing.assert_array_equal(got, oracle.combine_fp8(spec, case["topk_w"], rr, yc, ys))
+    # and it is not the float32-y layer (the quantisation is there)
+    assert (got != oracle.moe_layer(case)).any()
+
+
+@pytest.mark.parametrize("seed", [1014, 1015])
+def test_layer_y8_against_float64_dense_evaluation(seed):
+    """The FP8-y layer against the float64 dense evaluation: besides the
+    float32-y layer's own error, each kept route adds at most |w| / 8 of its
+    block's largest |y|: the block exponent leaves amax / 2^E in [256, 512),
+    so a value rounds by at most half an e4m3 step (2^-4 of amax) or, past
+    448 * 2^E, saturates there (losing less than 64 * 2^E = amax / 8)."""
+    case = _case(seed=seed)
+    spec = case["spec"]
+    out = _f(oracle.moe_layer(case, y_fp8=True))
+    dense, parts = dense_layer(case, return_parts=True)
+    rms = np.sqrt((dense ** 2).mean())
+    allow = np.zeros_like(dense)
+    ids = case["topk_ids"]
+    for t in range(spec.T):
+        for k in range(spec.K):
+            e = int(ids[t, k]) - spec.expert_begin
+            if ids[t, k] < 0 or not 0 <= e < spec.E_local:
+                continue
+            Y = np.abs(parts[e]["Y"][t]).reshape(-1, 32).max(axis=1).repeat(32)
+            allow[t] += abs(float(case["topk_w"][t, k])) * 2.0 ** -3 * Y * (1 + 2.0 ** -6)
+    err = np.abs(out - dense)
+    bound = 2.0 ** -8 * np.abs(dense).max() + 2e-3 * rms + allow
+    assert (err <= bound).all(), float((err - bound).max())
+    # the quantisation shows: the FP8-y layer differs from the float32-y one
+    assert (out != _f(oracle.moe_layer(case))).any()
+
+
+def test_layer_y8_zero_w2_and_exponent_plus_one():
+    """Zero W2 gives +0 rows; a W2 exponent + 1 doubles every y exactly,
+    which keeps its codes and raises each block exponent by one, so the
+    FP8-y output doubles exactly."""
+    case = _case(seed=1016)
+    base = _f(oracle.moe_layer(case, y_fp8=True))
+    c2 = dict(case)
+    c2["w2_scale"] = case["w2_scale"] + 1
+    np.testing.assert_array_equal(_f(oracle.moe_layer(c2, y_fp8=True)), 2 * base)
+    c3 = dict(case)
+    c3["w2"] = np.zeros_like(case["w2"])
+    assert not oracle.moe_layer(c3, y_fp8=True).any()
