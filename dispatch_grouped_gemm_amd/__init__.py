@@ -25,21 +25,27 @@ __all__ = [
     "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
     "moe_dispatch_workspace_size", "moe_workspace_size", "moe_workspace_status_offset",
     "workspace_status", "moe_dispatch", "moe_gemm1_swiglu",
-    "moe_gemm2", "moe_combine", "moe_forward", "moe_forward_persistent", "moe_forward_static",
+    "moe_gemm2", "moe_combine", "moe_gemm2_fp8", "moe_combine_fp8", "moe_resolve_y_format",
+    "moe_forward", "moe_forward_persistent", "moe_forward_static",
     "moe_static_scratch_bytes", "moe_forward_static_need", "moe_strerror",
     "DispatchBuffers",
-    "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT",
+    "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT", "Y_BF16", "Y_FP8", "Y_AUTO",
 ]
 
 COMPACT = 0
 FIXED_SLOT = 1
+# format of the expert output rows between GEMM2 and the combine
+Y_BF16 = 0
+Y_FP8 = 1
+Y_AUTO = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
             "moe_workspace_size", "moe_workspace_status_offset", "moe_dispatch",
-            "moe_gemm1_swiglu", "moe_gemm2",
+            "moe_gemm1_swiglu", "moe_gemm2", "moe_gemm2_fp8", "moe_combine_fp8",
+            "moe_resolve_y_format",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
             "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_forward_static",
             "moe_static_scratch_bytes", "moe_forward_static_need", "moe_set_tile_table",
@@ -66,7 +72,8 @@ class _CForwardArgs(ctypes.Structure):
                 ("topk_w", ctypes.c_void_p), ("w13", ctypes.c_void_p),
                 ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("out_bf16", ctypes.c_void_p),
-                ("num_valid_tokens", ctypes.c_void_p), ("persistent", ctypes.c_int32)]
+                ("num_valid_tokens", ctypes.c_void_p), ("persistent", ctypes.c_int32),
+                ("y_format", ctypes.c_int32)]
 
 
 class TileEntry(ctypes.Structure):
@@ -137,6 +144,12 @@ def lib() -> ctypes.CDLL:
         h.moe_gemm2.restype = ctypes.c_int
         h.moe_combine.argtypes = [S, P, P, P, P, P]
         h.moe_combine.restype = ctypes.c_int
+        h.moe_gemm2_fp8.argtypes = [S, P, P, P, P, P, P, P, P, P]
+        h.moe_gemm2_fp8.restype = ctypes.c_int
+        h.moe_combine_fp8.argtypes = [S, P, P, P, P, P, P]
+        h.moe_combine_fp8.restype = ctypes.c_int
+        h.moe_resolve_y_format.argtypes = [S, ctypes.c_int32]
+        h.moe_resolve_y_format.restype = ctypes.c_int
         h.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         h.moe_forward.restype = ctypes.c_int
         h.moe_forward_persistent.argtypes = h.moe_forward.argtypes
@@ -393,6 +406,50 @@ def moe_combine(shape: MoeShape, topk_w, route_row, y_bf16, out_bf16, stream=Non
     _check(lib().moe_combine(ctypes.byref(c), *args, _stream(stream, dev)), "moe_combine")
 
 
+def moe_gemm2_fp8(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_scale, y_fp8,
+                  y_scale, stream=None):
+    """GEMM2 writing MX FP8 rows: e4m3 codes y_fp8 [R, H] and exponent bytes
+    y_scale [R, H/32]."""
+    dev = h_fp8.device
+    H, I, E = shape.H, shape.I, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(h_fp8, "h_fp8", (R, I), _fp8(), dev),
+            _ptr(h_scale, "h_scale", (R, I // 32), _e8m0("h_scale"), dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            _ptr(w2, "w2", (E, H, I // 2), _fp4(), dev),
+            _ptr(w2_scale, "w2_scale", (E, H, I // 32), _e8m0("w2_scale"), dev),
+            _ptr(y_fp8, "y_fp8", (R, H), _fp8(), dev),
+            _ptr(y_scale, "y_scale", (R, H // 32), _e8m0("y_scale"), dev)]
+    c = shape.c()
+    _check(lib().moe_gemm2_fp8(ctypes.byref(c), *args, _stream(stream, dev)), "moe_gemm2_fp8")
+
+
+def moe_combine_fp8(shape: MoeShape, topk_w, route_row, y_fp8, y_scale, out_bf16, stream=None):
+    """The combine of MX FP8 rows (codes [R, H], exponent bytes [R, H/32])."""
+    dev = topk_w.device
+    T, K, H = shape.T, shape.K, shape.H
+    R = max(moe_row_capacity(shape), 1)
+    bf = {torch.bfloat16, torch.uint16, torch.int16}
+    args = [_ptr(topk_w, "topk_w", (T, K), {torch.float32}, dev),
+            _ptr(route_row, "route_row", (max(T * K, 1),), {torch.int32}, dev),
+            _ptr(y_fp8, "y_fp8", (R, H), _fp8(), dev),
+            _ptr(y_scale, "y_scale", (R, H // 32), _e8m0("y_scale"), dev),
+            _ptr(out_bf16, "out_bf16", (T, H), bf, dev)]
+    c = shape.c()
+    _check(lib().moe_combine_fp8(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_combine_fp8")
+
+
+def moe_resolve_y_format(shape: MoeShape, y_format: int) -> int:
+    """The y format (Y_BF16 or Y_FP8) a layer call takes for y_format."""
+    c = shape.c()
+    rc = lib().moe_resolve_y_format(ctypes.byref(c), ctypes.c_int32(y_format))
+    _check(rc if rc < 0 else 0, "moe_resolve_y_format")
+    return rc
+
+
 def moe_quant_mxfp8(shape: MoeShape, x_bf16, x_fp8, x_scale, stream=None):
     """bf16 activation rows [T, H] -> e4m3 codes [T, H] + E8M0 exponents [T, H/32]."""
     dev = x_bf16.device
@@ -480,9 +537,10 @@ def moe_forward_static_need(shape: MoeShape) -> int:
 
 def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out_bf16,
                    workspace, x_fp8=None, x_scale=None, x_bf16=None, num_valid_tokens=None,
-                   persistent=False, stream=None):
+                   persistent=False, stream=None, y_format=Y_BF16):
     """The layer with every option (one of x_fp8 + x_scale or x_bf16;
-    num_valid_tokens an int32 tensor [1] on the device)."""
+    num_valid_tokens an int32 tensor [1] on the device; y_format one of
+    Y_BF16, Y_FP8, Y_AUTO)."""
     dev = topk_ids.device
     T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
     bf = {torch.bfloat16, torch.uint16, torch.int16}
@@ -503,6 +561,7 @@ def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_sca
         a.num_valid_tokens = _ptr(num_valid_tokens, "num_valid_tokens", (1,), {torch.int32},
                                   dev)
     a.persistent = 1 if persistent else 0
+    a.y_format = int(y_format)
     ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
     c = shape.c()
     _check(lib().moe_forward_ex(ctypes.byref(c), ctypes.byref(a), ws, workspace.numel(),

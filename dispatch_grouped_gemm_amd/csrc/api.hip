@@ -25,7 +25,8 @@ bool all_aligned16(const P *...p)
 
 // Byte layout of the moe_forward workspace.
 struct Layout {
-    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, xq, xqs, total;
+    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, ys, xq, xqs,
+        total;
 };
 
 Layout layout_of(const moe_shape &s)
@@ -52,8 +53,14 @@ Layout layout_of(const moe_shape &s)
     p = align_up(p + R * (size_t)s.I);
     L.hs = p;
     p = align_up(p + R * (size_t)(s.I / 32));
+    // y: bf16 rows, or MX FP8 rows (codes, then exponent bytes at ys)
     L.y = p;
-    p = align_up(p + R * (size_t)s.H * sizeof(uint16_t));
+    L.ys = align_up(p + R * (size_t)s.H);
+    {
+        const size_t bf16_end = p + R * (size_t)s.H * sizeof(uint16_t);
+        const size_t fp8_end = L.ys + R * (size_t)(s.H / 32);
+        p = align_up(bf16_end > fp8_end ? bf16_end : fp8_end);
+    }
     // MX FP8 activations of moe_forward_bf16
     L.xq = p;
     p = align_up(p + (size_t)s.T * (size_t)s.H);
@@ -233,8 +240,25 @@ int moe_gemm2(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int
         return MOE_EINVAL;
     if (!all_aligned16(h, hs, w2, w2s, y))
         return MOE_EINVAL;
-    return hip_status(
-        moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, as_stream(stream)));
+    return hip_status(moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s,
+                                        moe::YRows{y, nullptr, nullptr}, as_stream(stream)));
+}
+
+int moe_gemm2_fp8(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const int32_t *counts,
+                  const int32_t *offsets, const uint8_t *w2, const uint8_t *w2s, uint8_t *y_fp8,
+                  uint8_t *y_scale, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!h || !hs || !counts || !offsets || !w2 || !w2s || !y_fp8 || !y_scale)
+        return MOE_EINVAL;
+    if (!all_aligned16(h, hs, w2, w2s, y_fp8))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s,
+                                        moe::YRows{nullptr, y_fp8, y_scale}, as_stream(stream)));
 }
 
 int moe_quant_mxfp8(const moe_shape *s, const uint16_t *x, uint8_t *xq, uint8_t *xqs,
@@ -268,6 +292,37 @@ int moe_combine(const moe_shape *s, const float *tw, const int32_t *route_row, c
     return hip_status(moe::launch_combine(*s, tw, route_row, y, out, as_stream(stream)));
 }
 
+int moe_combine_fp8(const moe_shape *s, const float *tw, const int32_t *route_row,
+                    const uint8_t *y_fp8, const uint8_t *y_scale, uint16_t *out, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!tw || !route_row || !y_fp8 || !y_scale || !out)
+        return MOE_EINVAL;
+    if (!all_aligned16(y_fp8, out))
+        return MOE_EINVAL;
+    return hip_status(
+        moe::launch_combine_fp8(*s, tw, route_row, y_fp8, y_scale, out, as_stream(stream)));
+}
+
+int moe_resolve_y_format(const moe_shape *s, int32_t y_format)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (y_format == MOE_Y_BF16 || y_format == MOE_Y_FP8)
+        return y_format;
+    if (y_format != MOE_Y_AUTO)
+        return MOE_EINVAL;
+    // many rows per expert: where the tile rule reads weights through the
+    // cache (tiles of 128 rows or more, from 96 expected rows per local
+    // expert under uniform routing), from host-known sizes only
+    return (double)s->T * s->K / (double)s->E_total > 96.0 ? MOE_Y_FP8 : MOE_Y_BF16;
+}
+
 } // extern "C"
 
 namespace {
@@ -279,11 +334,15 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
                  const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                  const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
                  bool persistent, const uint16_t *x_bf16 = nullptr,
-                 const int32_t *valid = nullptr, size_t need_bytes = 0)
+                 const int32_t *valid = nullptr, size_t need_bytes = 0,
+                 int32_t y_format = MOE_Y_BF16)
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
         return rc;
+    const int yf = moe_resolve_y_format(s, y_format);
+    if (yf < 0)
+        return yf;
     if (persistent && !moe::persistent_supported(*s))
         return MOE_ENOTSUP;
     if (s->T == 0)
@@ -315,7 +374,10 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
     void *scratch = base + L.scratch;
     uint8_t *h = base + L.h;
     uint8_t *hs = base + L.hs;
-    uint16_t *y = reinterpret_cast<uint16_t *>(base + L.y);
+    const moe::YRows y = yf == MOE_Y_FP8
+                             ? moe::YRows{nullptr, base + L.y, base + L.ys}
+                             : moe::YRows{reinterpret_cast<uint16_t *>(base + L.y), nullptr,
+                                          nullptr};
     hipStream_t st = as_stream(stream);
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st, nullptr, 0, qj, valid);
@@ -331,7 +393,8 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
             e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
     }
     if (e == hipSuccess)
-        e = moe::launch_combine(*s, tw, route_row, y, out, st);
+        e = y.bf16 ? moe::launch_combine(*s, tw, route_row, y.bf16, out, st)
+                   : moe::launch_combine_fp8(*s, tw, route_row, y.codes, y.scales, out, st);
     return hip_status(e);
 }
 
@@ -408,7 +471,7 @@ int moe_forward_ex(const moe_shape *s, const moe_forward_args *a, void *ws, size
         return s->T == 0 ? MOE_OK : MOE_EINVAL;
     return forward_impl(s, a->x_fp8, a->x_scale, a->topk_ids, a->topk_w, a->w13, a->w13_scale,
                         a->w2, a->w2_scale, a->out_bf16, ws, ws_bytes, stream, a->persistent != 0,
-                        a->x_bf16, a->num_valid_tokens);
+                        a->x_bf16, a->num_valid_tokens, 0, a->y_format);
 }
 
 int moe_set_tile_table(const moe_tile_entry *entries, int32_t n)

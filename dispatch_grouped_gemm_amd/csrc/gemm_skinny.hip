@@ -204,7 +204,8 @@ struct LayerPtrs {
     const int32_t *counts, *offsets, *row_route;
     const uint8_t *w13, *w13s, *w2, *w2s;
     uint8_t *h, *hs;
-    uint16_t *y;
+    uint16_t *y;           // bf16 rows, or
+    uint8_t *y8, *y8s;     // MX FP8 rows (y null)
 };
 
 // Where an item's rows are: expert e, rows [row0, row0 + nrows).
@@ -357,7 +358,39 @@ __device__ __forceinline__ void gemm2_item(const Shape &s, const LayerPtrs &p, c
     k_loop<false, NMB>(acc, kp, KS, wave, nmb_act);
     reduce_waves<NMB>(acc, red, nmb_act);
 
-    if (wave < nmb_act) {
+    if (wave < nmb_act && p.y8) {
+        // MX FP8 rows: lane (i16, kq) holds columns n0 + 16 g + 4 kq + v;
+        // the 32-column block b is groups 2b and 2b + 1 of the four lanes kq
+        // of a route (every lane takes part in the exchanges; rows past
+        // nrows repeat the last row and are not stored)
+        const int mb = wave;
+        const int rloc = mb * 16 + i16;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float v[2][4];
+            float amax = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[g][q] = red[(mb * 4 + 2 * blk + g) * 4 * 64 + lane + 64 * q];
+                    amax = fmaxf(amax, fabsf(v[g][q]));
+                }
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int E = mx8_block_exponent(amax);
+            if (rloc < nrows) {
+                uint8_t *yr = p.y8 + (size_t)(row0 + rloc) * (size_t)H + n0 + 32 * blk + 4 * kq;
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    *reinterpret_cast<uint32_t *>(yr + 16 * g) =
+                        mx8_pack4(v[g][0], v[g][1], v[g][2], v[g][3], E, amax);
+                if (kq == 0)
+                    p.y8s[(size_t)(row0 + rloc) * (size_t)(H / 32) + (n0 + 32 * blk) / 32] =
+                        (uint8_t)(E + 127);
+            }
+        }
+    } else if (wave < nmb_act) {
         const int mb = wave;
         const int rloc = mb * 16 + i16;
         if (rloc < nrows) {
@@ -520,7 +553,7 @@ hipError_t launch_gemm1(const moe_shape &sh, const uint8_t *x, const uint8_t *xs
 
 hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                        const uint8_t *w2s, uint16_t *y, hipStream_t st)
+                        const uint8_t *w2s, const YRows &y, hipStream_t st)
 {
     if (use_tiled_gemm2(sh))
         return launch_gemm2_tiled(sh, h, hs, counts, offsets, w2, w2s, y, st);
@@ -532,7 +565,9 @@ hipError_t launch_gemm2(const moe_shape &sh, const uint8_t *h, const uint8_t *hs
     p.offsets = offsets;
     p.w2 = w2;
     p.w2s = w2s;
-    p.y = y;
+    p.y = y.bf16;
+    p.y8 = y.codes;
+    p.y8s = y.scales;
     const int nmb = pick_nmb(sh);
     const long nt = sh.H / 64;
 #define MOE_LAUNCH_G2(N)                                                                          \

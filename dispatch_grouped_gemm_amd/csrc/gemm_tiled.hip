@@ -134,7 +134,8 @@ struct TiledArgs {
     const int32_t *counts, *offsets, *row_route;
     const uint8_t *w, *ws;                  // W13 or W2 codes and exponents
     uint8_t *h_out, *hs_out;                // GEMM1 output
-    uint16_t *y_out;                        // GEMM2 output
+    uint16_t *y_out;                        // GEMM2 output, bf16 rows, or
+    uint8_t *y8_out, *y8s_out;              // MX FP8 rows (y_out null)
 };
 
 // One work item: N tile nt of row chunk q.  prefix holds the chunk plan,
@@ -506,6 +507,53 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                                                (size_t)nt * (BN / 2) + 16 * c) =
                         lds_read16(lds + r * HP + 16 * c);
             }
+        } else if (g.y8_out) {
+            // MX FP8 rows: one exponent per 32 consecutive output columns
+            // (weight groups 2b and 2b + 1 of a wavefront, met across the
+            // four lanes kq of a route), by the requant's rule; the codes go
+            // through LDS (rows of BN + 16 bytes, so the 4-byte writes of a
+            // wavefront hit distinct banks), then out as whole 16-byte pieces
+            // of rows
+            constexpr int YP = BN + 16;
+            static_assert(BM * YP <= L::kRing, "y code tile fits the stage ring");
+            static_assert(GW % 2 == 0, "32-column blocks");
+            __syncthreads();   // every wavefront is done with the stage ring
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int m = wm * (BM / NWM) + 16 * j + i16;
+#pragma unroll
+                for (int blk = 0; blk < GW / 2; ++blk) {
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int i = 2 * blk; i < 2 * blk + 2; ++i)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            amax = fmaxf(amax, fabsf(acc[i][j][v]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 16));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    const int E = mx8_block_exponent(amax);
+                    const int tcol = (BN / 2) * wn + 32 * blk;   // column in the tile
+#pragma unroll
+                    for (int i = 2 * blk; i < 2 * blk + 2; ++i)
+                        *reinterpret_cast<uint32_t *>(lds + m * YP + tcol + 16 * (i - 2 * blk) +
+                                                      4 * kq) =
+                            mx8_pack4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3], E,
+                                      amax);
+                    if (m < nrows && kq == 0)
+                        g.y8s_out[(size_t)(row0 + m) * (size_t)(H / 32) + (nt * BN + tcol) / 32] =
+                            (uint8_t)(E + 127);
+                }
+            }
+            __syncthreads();
+            constexpr int PR = BN / 16;                // 16-byte pieces per row
+#pragma unroll
+            for (int p = 0; p < (BM * PR + NTH - 1) / NTH; ++p) {
+                const int piece = p * NTH + tid, r = piece / PR, c = piece % PR;
+                if (piece < BM * PR && r < nrows)
+                    *reinterpret_cast<u32x4 *>(g.y8_out + (size_t)(row0 + r) * (size_t)H +
+                                               (size_t)nt * BN + 16 * c) =
+                        lds_read16(lds + r * YP + 16 * c);
+            }
         } else {
             // the bf16 tile goes through LDS (rows of BN*2 + 16 bytes: the
             // fragment writes of a half-wavefront hit distinct banks), then
@@ -813,7 +861,7 @@ TiledConfig tiled_config(const moe_shape &s, bool gemm1)
 template <bool kGemm1, int BM, int BN, int KU>
 hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
-                        const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, uint16_t *y,
+                        const uint8_t *w, const uint8_t *ws, uint8_t *h, uint8_t *hs, const YRows &y,
                         hipStream_t st)
 {
     // eight wavefronts for the 256-row tile, four otherwise
@@ -830,7 +878,8 @@ hipError_t launch_tiled(const moe_shape &sh, const uint8_t *act, const uint8_t *
         bq = grid / 8 / bnt > 1 ? grid / 8 / bnt : 1;
     }
     k<<<grid, NW * 64, 0, st>>>(to_dev(sh),
-                                 TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs, y},
+                                 TiledArgs{act, act_s, counts, offsets, row_route, w, ws, h, hs,
+                                           y.bf16, y.codes, y.scales},
                                  bq, bnt);
     return hipGetLastError();
 }
@@ -839,7 +888,7 @@ template <bool kGemm1>
 hipError_t launch_tiled_any(const moe_shape &sh, const uint8_t *act, const uint8_t *act_s,
                             const int32_t *counts, const int32_t *offsets,
                             const int32_t *row_route, const uint8_t *w, const uint8_t *ws,
-                            uint8_t *h, uint8_t *hs, uint16_t *y, hipStream_t st)
+                            uint8_t *h, uint8_t *hs, const YRows &y, hipStream_t st)
 {
     const TiledConfig c = tiled_config(sh, kGemm1);
 #define MOE_TILED_CASE(BM, BN, KU)                                                                \
@@ -864,7 +913,7 @@ hipError_t launch_gemm1_tiled(const moe_shape &sh, const uint8_t *x, const uint8
                               uint8_t *h, uint8_t *hs, hipStream_t st)
 {
     return launch_tiled_any<true>(sh, x, xs, counts, offsets, row_route, w13, w13s, h, hs,
-                                  nullptr, st);
+                                  YRows{nullptr, nullptr, nullptr}, st);
 }
 
 // XCDs of the device: the MI355X has 32 CUs per XCD, and its partition modes
@@ -952,13 +1001,15 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
                                    const int32_t *counts, const int32_t *offsets,
                                    const int32_t *row_route, const uint8_t *w13,
                                    const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
-                                   uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
+                                   uint8_t *h, uint8_t *hs, const YRows &y, int32_t *sync,
                                    int32_t *status, hipStream_t st)
 {
     const int nsync = persistent_sync_words(sh);
     fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
-    const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr};
-    const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y};
+    const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr, nullptr,
+                       nullptr};
+    const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y.bf16,
+                       y.codes, y.scales};
     const TiledConfig c1 = persistent_config(sh, true);
     const int bn1 = c1.bn, bn2 = persistent_config(sh, false).bn;
     const int nq = xcd_count();
@@ -987,7 +1038,7 @@ hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const 
 
 hipError_t launch_gemm2_tiled(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                              const uint8_t *w2s, uint16_t *y, hipStream_t st)
+                              const uint8_t *w2s, const YRows &y, hipStream_t st)
 {
     return launch_tiled_any<false>(sh, h, hs, counts, offsets, nullptr, w2, w2s, nullptr,
                                    nullptr, y, st);

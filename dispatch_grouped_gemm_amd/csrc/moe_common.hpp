@@ -331,9 +331,16 @@ hipError_t launch_gemm1(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                         const int32_t *counts, const int32_t *offsets, const int32_t *row_route,
                         const uint8_t *w13, const uint8_t *w13s, uint8_t *h, uint8_t *hs,
                         hipStream_t st);
+// GEMM2 output rows: bf16 [R, H] (codes and scales null), or MX FP8 rows,
+// e4m3 codes [R, H] and E8M0 bytes [R, H/32] by the requant's 1x32 rule
+// (bf16 null).
+struct YRows {
+    uint16_t *bf16;
+    uint8_t *codes, *scales;
+};
 hipError_t launch_gemm2(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                         const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                        const uint8_t *w2s, uint16_t *y, hipStream_t st);
+                        const uint8_t *w2s, const YRows &y, hipStream_t st);
 int tiled_bm(const moe_shape &s);
 bool use_tiled_gemm1(const moe_shape &s);
 bool use_tiled_gemm2(const moe_shape &s);
@@ -348,7 +355,7 @@ hipError_t launch_gemm1_tiled(const moe_shape &s, const uint8_t *x, const uint8_
                               uint8_t *h, uint8_t *hs, hipStream_t st);
 hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_t *hs,
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
-                              const uint8_t *w2s, uint16_t *y, hipStream_t st);
+                              const uint8_t *w2s, const YRows &y, hipStream_t st);
 bool persistent_supported(const moe_shape &s);
 int persistent_sync_words(const moe_shape &s);
 // GEMM1 + SwiGLU + requant and GEMM2 in one persistent launch (after a
@@ -358,11 +365,14 @@ hipError_t launch_layer_persistent(const moe_shape &s, const uint8_t *x, const u
                                    const int32_t *counts, const int32_t *offsets,
                                    const int32_t *row_route, const uint8_t *w13,
                                    const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
-                                   uint8_t *h, uint8_t *hs, uint16_t *y, int32_t *sync,
+                                   uint8_t *h, uint8_t *hs, const YRows &y, int32_t *sync,
                                    int32_t *status,
                                    hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
                           const uint16_t *y, uint16_t *out, hipStream_t st);
+hipError_t launch_combine_fp8(const moe_shape &s, const float *tw, const int32_t *route_row,
+                              const uint8_t *y_codes, const uint8_t *y_scales, uint16_t *out,
+                              hipStream_t st);
 
 int device_cu_count();
 

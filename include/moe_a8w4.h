@@ -43,7 +43,8 @@
  *                               layer's output is then not valid),
  *                           [3] zero; the dispatch writes all four
  * Intermediates, indexed by row:
- *   h_fp8 [R, I], h_scale [R, I/32], y_bf16 [R, H] (bf16 bit patterns)
+ *   h_fp8 [R, I], h_scale [R, I/32], y_bf16 [R, H] (bf16 bit patterns),
+ *   or y_fp8 [R, H] + y_scale [R, H/32] (MX FP8 rows, along H)
  *
  * Rows inside a compact segment are in ascending r (a stable scatter);
  * inside a fixed-slot segment their order is unspecified.
@@ -83,6 +84,11 @@ extern "C" {
 
 #define MOE_DISPATCH_COMPACT 0    /* histogram, scan, stable scatter */
 #define MOE_DISPATCH_FIXED_SLOT 1 /* atomic claim into per-expert capacity */
+
+/* Format of the expert output rows y between GEMM2 and the combine. */
+#define MOE_Y_BF16 0 /* bf16 rows (default) */
+#define MOE_Y_FP8 1  /* MX FP8 rows: e4m3 codes + one E8M0 byte per 32 columns */
+#define MOE_Y_AUTO 2 /* FP8 where the rows per local expert are many, else bf16 */
 
 typedef struct moe_shape {
     int32_t T;             /* source tokens (0 is a valid no-op); T*H < 2^32 */
@@ -170,6 +176,23 @@ int moe_gemm2(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_sca
               const uint8_t *w2_scale, uint16_t *y_bf16, void *stream);
 
 /*
+ * GEMM2 with MX FP8 output rows ("MegaMoEV2 ...", Technical Details,
+ * skewed routing, small input: a rank with many rows or a large expert
+ * sends its GEMM2 rows to the combine in the main path's 1x32 FP8 format
+ * instead of BF16).  The same float32 sums as moe_gemm2, then per 32
+ * consecutive columns of a row the requant's rule (exponent
+ * floor(log2(amax)) - 8 clamped to [-127, 127], byte 127 for an all-zero
+ * block, e4m3 codes rounded to nearest even, saturating at 448), with no
+ * bf16 rounding in between.  y_fp8 is [row capacity, H] e4m3 (16-byte
+ * aligned), y_scale [row capacity, H/32] exponent bytes; rows of used rows
+ * only are written.  Lossy against moe_gemm2: a value moves by up to 1/8 of
+ * its block's largest magnitude.
+ */
+int moe_gemm2_fp8(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_scale,
+                  const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
+                  const uint8_t *w2_scale, uint8_t *y_fp8, uint8_t *y_scale, void *stream);
+
+/*
  * Activation quant in front of the layer ("MegaMoEV2: fuse dispatch, GEMM1,
  * GEMM2 and combine into one kernel", Summary: the large-input path runs it
  * as its own kernel on the caller's stream): bf16 rows x_bf16[T, H] to e4m3
@@ -195,6 +218,27 @@ int moe_quant_mxfp8(const moe_shape *shape, const uint16_t *x_bf16, uint8_t *x_f
  */
 int moe_combine(const moe_shape *shape, const float *topk_w, const int32_t *route_row,
                 const uint16_t *y_bf16, uint16_t *out_bf16, void *stream);
+
+/*
+ * Combine of MX FP8 rows (as moe_gemm2_fp8 writes them; "MegaMoEV2 ...",
+ * Technical Details: the combine reads both formats): moe_combine with
+ * every y value decoded exactly, e4m3 value times 2^(y_scale byte - 127).
+ * y_fp8 and out_bf16 16-byte aligned; y rows read only through route_row.
+ */
+int moe_combine_fp8(const moe_shape *shape, const float *topk_w, const int32_t *route_row,
+                    const uint8_t *y_fp8, const uint8_t *y_scale, uint16_t *out_bf16,
+                    void *stream);
+
+/*
+ * The y format a layer call takes for y_format (MOE_Y_BF16, MOE_Y_FP8 or
+ * MOE_Y_AUTO): MOE_Y_AUTO becomes MOE_Y_FP8 when the expected rows per
+ * local expert under uniform routing, T*K/E_total, exceed 96 (where the
+ * tile rule takes tiles of 128 rows or more, whose weights are read through
+ * the cache: the pages pair FP8 rows with cached weights), else MOE_Y_BF16.
+ * Host-known sizes only, never device data.  Returns the format, or
+ * MOE_EINVAL for another value (or moe_check_shape's error).
+ */
+int moe_resolve_y_format(const moe_shape *shape, int32_t y_format);
 
 /*
  * The whole layer ("MegaMoEV2: fuse Dispatch, GEMM1, GEMM2 and Combine into
@@ -288,7 +332,10 @@ int moe_forward_bf16(const moe_shape *shape, const uint16_t *x_bf16, const int32
  * of the two; num_valid_tokens (device int32, or NULL for all T rows) as in
  * moe_dispatch_valid, so padding rows cost no expert work and get +0 output
  * rows; persistent != 0 takes moe_forward_persistent's launch (same
- * refusals).  Same workspace and result as moe_forward.
+ * refusals); y_format (see moe_resolve_y_format) sends the expert output
+ * rows to the combine as bf16 (MOE_Y_BF16, the result of moe_forward) or as
+ * MX FP8 (moe_gemm2_fp8 then moe_combine_fp8 in the workspace's y area; a
+ * lossy mode).  Same workspace as moe_forward.
  */
 typedef struct {
     const uint8_t *x_fp8;             /* [T, H] e4m3, or NULL */
@@ -303,6 +350,7 @@ typedef struct {
     uint16_t *out_bf16;               /* [T, H] */
     const int32_t *num_valid_tokens;  /* device int32, or NULL */
     int32_t persistent;
+    int32_t y_format;                 /* MOE_Y_BF16 (0), MOE_Y_FP8 or MOE_Y_AUTO */
 } moe_forward_args;
 
 int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *workspace,

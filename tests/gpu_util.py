@@ -164,6 +164,22 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return e4m3_values()[codes] * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=1))
 
 
+def e4m3_step(v: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """Spacing of the e4m3 values (scaled by 2^E) at |v|: 2^(E - 9) in the
+    subnormal range below 2^(E - 6), else 2^(E + b - 3) for the binade
+    2^b <= |v| / 2^E (b at most 8, where values saturate at 448)."""
+    a = np.abs(v) * np.exp2(-E)
+    b = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.exp2(E + np.minimum(b, 8) - 3)
+
+
+def y8_moves_allowed(bound: np.ndarray, y: np.ndarray, E: np.ndarray) -> float:
+    """How many FP8 y codes may move when each float32 sum may be off by
+    its MFMA bound: a code moves only if its sum lies within that error of a
+    rounding midpoint, at most min(1, 2 b / s) per code (s the e4m3 step)."""
+    return float(np.minimum(1.0, 2.0 * bound / e4m3_step(y, E)).sum())
+
+
 def gemm1_mfma_bound(case: dict, routes: np.ndarray) -> np.ndarray:
     """How far the GPU's pre-quantisation value of h may lie from the
     oracle's, per route slot and column [n, I]: inside one 32-value K block
@@ -197,6 +213,24 @@ def gemm1_mfma_bound(case: dict, routes: np.ndarray) -> np.ndarray:
     return 1.1 * np.abs(uc) * 2.0 ** -9 * ag + np.abs(silu) * 2.0 ** -9 * au
 
 
+def run_steps_y8(case: dict, g: dict | None = None) -> dict:
+    """The four steps with MX FP8 y rows (moe_gemm2_fp8, moe_combine_fp8)."""
+    spec = case["spec"]
+    shape = shape_of(spec)
+    g = g or upload(case)
+    d = run_dispatch(spec, g["topk_ids"])
+    R = max(moe.moe_row_capacity(shape), 1)
+    h = torch.zeros((R, spec.I), dtype=torch.uint8, device=DEV)
+    hs = torch.zeros((R, spec.I // 32), dtype=torch.uint8, device=DEV)
+    yc = torch.zeros((R, spec.H), dtype=torch.uint8, device=DEV)
+    ys = torch.zeros((R, spec.H // 32), dtype=torch.uint8, device=DEV)
+    out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+    moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"], h, hs)
+    moe.moe_gemm2_fp8(shape, h, hs, d, g["w2"], g["w2_scale"], yc, ys)
+    moe.moe_combine_fp8(shape, g["topk_w"], d.route_row, yc, ys, out)
+    return dict(d=d, h=h, hs=hs, yc=yc, ys=ys, out=out)
+
+
 def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dict,
                 what: str = "", max_flip_rate: float = 1e-3):
     """The layer output of `tokens` against the oracle.
@@ -213,17 +247,29 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
     The GPU keeps y in bf16 (the pages' expert output rows) where the oracle
     keeps float32: each kept route adds |w| * half a bf16 step of its y value
     to the allowance of its token.  Every other difference must be within
-    max(2e-2 * RMS(ref), one bf16 step)."""
-    from dense_ref import dec_fp4_rows
+    max(2e-2 * RMS(ref), one bf16 step).
+
+    With MX FP8 y rows (steps holding "yc" and "ys") the reference is the
+    oracle's FP8-y layer; each y code that moved adds |w| * |its value
+    change| to the token's allowance instead of the half bf16 step, and
+    must lie within one e4m3 step (larger block scale) of the oracle's
+    float32 y, widened by the MFMA bound of its sum and the effect of the
+    route's requant flips; moved y codes are held to max_flip_rate in the
+    routes without a requant flip."""
+    from dense_ref import dec_fp4_rows, dec_fp8_rows
     import oracle
     spec = case["spec"]
     K = spec.K
+    y8 = "yc" in steps
     tokens = np.asarray(tokens, dtype=np.int64)
-    ref_bits = oracle.moe_layer(case, tokens)
+    ref_bits = oracle.moe_layer(case, tokens, y_fp8=y8)
     rr = host(steps["d"].route_row).reshape(spec.T, K)
     slots = [(i, t * K + k) for i, t in enumerate(tokens) for k in range(K) if rr[t, k] >= 0]
     allowance = np.zeros((tokens.size, spec.H))
     n_codes = n_flips = 0
+    y8_codes = y8_moved = y8_moved_all = 0
+    y8_allowed = 0.0
+    w2abs = {}
     if slots:
         routes = np.array([r for _, r in slots], np.int64)
         orc = oracle.routes_ffn(case, routes)
@@ -246,14 +292,54 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
             assert ok[far[sel]].all(), what + ": invalid code"
         ids = case["topk_ids"].reshape(-1)
         w = case["topk_w"].reshape(-1)
+        if y8:
+            yg = dequant_rows(host(steps["yc"])[rows], host(steps["ys"])[rows])
+            rc, rs = oracle.quant_rows_f32(orc["y"])
+            yr = dequant_rows(rc, rs)
+            ymoved = yg != yr
+            Eg = np.repeat(host(steps["ys"])[rows].astype(np.float64) - 127, 32, axis=1)
+            Er = np.repeat(rs.astype(np.float64) - 127, 32, axis=1)
         for j, (i, r) in enumerate(slots):
-            allowance[i] += abs(float(w[r])) * bf16_ulp(yabs[j] * (1 + 2.0 ** -7)) / 2
-            cols = np.nonzero(flips[j])[0]
-            if cols.size == 0:
-                continue
             e = int(ids[r]) - spec.expert_begin
-            W2c = dec_fp4_rows(case["w2"][e], case["w2_scale"][e])[:, cols]
-            allowance[i] += abs(float(w[r])) * (np.abs(W2c) @ np.abs(hq_gpu[j, cols] - hq_ref[j, cols]))
+            cols = np.nonzero(flips[j])[0]
+            dy = np.zeros(spec.H)
+            if cols.size:
+                W2c = dec_fp4_rows(case["w2"][e], case["w2_scale"][e])[:, cols]
+                dy = np.abs(W2c) @ np.abs(hq_gpu[j, cols] - hq_ref[j, cols])
+                allowance[i] += abs(float(w[r])) * dy
+            if not y8:
+                allowance[i] += abs(float(w[r])) * bf16_ulp(yabs[j] * (1 + 2.0 ** -7)) / 2
+                continue
+            mc = np.nonzero(ymoved[j])[0]
+            y8_moved_all += mc.size
+            if cols.size == 0:
+                # no requant flip in this route: its moved y codes count
+                # against what the MFMA bound of its sums allows
+                y8_codes += spec.H
+                y8_moved += mc.size
+                if e in w2abs:
+                    W2e = w2abs[e]
+                else:
+                    W2e = np.abs(dec_fp4_rows(case["w2"][e], case["w2_scale"][e]))
+                    if spec.H * spec.I <= 1 << 22:
+                        w2abs[e] = W2e
+                y8_allowed += y8_moves_allowed(2.0 ** -12 * (W2e @ np.abs(hq_gpu[j])),
+                                               orc["y"][j].astype(np.float64), Er[j])
+            if mc.size == 0:
+                continue
+            allowance[i, mc] += abs(float(w[r])) * np.abs(yg[j, mc] - yr[j, mc])
+            # each moved code: one e4m3 step of the oracle's value at the
+            # larger block scale, widened by the MFMA bound of its sum and
+            # the requant flips' effect
+            W2m = np.abs(dec_fp4_rows(case["w2"][e][mc], case["w2_scale"][e][mc]))
+            mfma = 2.0 ** -12 * (W2m @ np.abs(hq_gpu[j]))
+            yo = orc["y"][j, mc].astype(np.float64)
+            E = np.maximum(Eg[j, mc], Er[j, mc])
+            slack = mfma + dy[mc]
+            step = (np.maximum(np.abs(yg[j, mc]), np.abs(yo) + slack) / 8 + np.exp2(E - 9)
+                    + np.maximum(np.abs(yo) + slack - 448.0 * np.exp2(Eg[j, mc]), 0))
+            assert (np.abs(yg[j, mc] - yo) <= (step + slack) * 1.0001).all(), \
+                what + ": a y code is not a rounding of the oracle's y"
     got = bf16_f64(out_bits)
     ref = bf16_f64(ref_bits)
     rms = float(np.sqrt((ref ** 2).mean())) if ref.size else 0.0
@@ -269,12 +355,20 @@ def check_layer(case: dict, tokens: np.ndarray, out_bits: np.ndarray, steps: dic
         "beyond 2e-2*RMS %d; requant flips %d of %d codes; beyond the bar without a flip to "
         "explain it: %d" % (what, tokens.size, len(slots), int((got != ref).sum()), got.size, lit,
                             rms, over, n_flips, n_codes, int(beyond.sum())))
+    extra = {}
+    if y8:
+        say("  FP8 y rows: %d y codes moved; in the routes without a requant flip %d of %d "
+            "(the MFMA bound allows %.1f)" % (y8_moved_all, y8_moved, y8_codes, y8_allowed))
+        extra = dict(y_fp8=1, y8_codes_no_requant_flip=y8_codes, y8_moved=y8_moved_all,
+                     y8_moved_no_requant_flip=y8_moved, y8_moves_allowed=y8_allowed)
     log_parity(what, tokens=tokens.size, routes=len(slots), elements=got.size,
                differ=int((got != ref).sum()), max_err_over_rms=lit, beyond_2e2_rms=over,
-               requant_flips=n_flips, requant_codes=n_codes)
+               requant_flips=n_flips, requant_codes=n_codes, **extra)
     assert not beyond.any(), what + ": elements beyond the bar"
     if n_codes:
         assert n_flips <= max(4, max_flip_rate * n_codes), what + ": too many requant flips"
+    if y8_codes:
+        assert y8_moved <= y8_allowed, what + ": more moved y codes than the MFMA bound allows"
     return lit
 
 

@@ -219,3 +219,41 @@ def test_tile_table(lib):
     finally:
         moe.set_tile_table([])
     assert tuple(moe.get_tile_config(dec, 1)[k] for k in ("bm", "bn", "ku")) == (32, 128, 2)
+
+
+def test_y_format_resolution_and_fp8_step_refusals(lib):
+    """MOE_Y_AUTO resolves from the shape alone (FP8 rows past 96 expected
+    rows per local expert); an unknown format and bad buffers of the FP8
+    steps are refused before any launch; the workspace holds either y form."""
+    dec = moe.MoeShape(**V4)
+    pre = moe.MoeShape(**{**V4, "T": 65536})
+    assert moe.moe_resolve_y_format(dec, moe.Y_AUTO) == moe.Y_BF16
+    assert moe.moe_resolve_y_format(pre, moe.Y_AUTO) == moe.Y_FP8
+    edge = moe.MoeShape(**{**V4, "T": 6144})        # exactly 96 rows per expert
+    assert moe.moe_resolve_y_format(edge, moe.Y_AUTO) == moe.Y_BF16
+    assert moe.moe_resolve_y_format(moe.MoeShape(**{**V4, "T": 6145}), moe.Y_AUTO) == moe.Y_FP8
+    for f in (moe.Y_BF16, moe.Y_FP8):
+        assert moe.moe_resolve_y_format(dec, f) == f
+    c = dec.c()
+    assert lib.moe_resolve_y_format(ctypes.byref(c), 3) == -1
+    assert lib.moe_resolve_y_format(ctypes.byref(moe.MoeShape(**{**V4, "K": 0}).c()), 0) == -1
+    null = None
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 4)
+    assert lib.moe_gemm2_fp8(ctypes.byref(c), *([null] * 8), null) == -1
+    assert lib.moe_gemm2_fp8(ctypes.byref(c), *([fake] * 6), odd, fake, null) == -1
+    assert lib.moe_combine_fp8(ctypes.byref(c), *([null] * 5), null) == -1
+    assert lib.moe_combine_fp8(ctypes.byref(c), fake, fake, odd, fake, fake, null) == -1
+    z = moe.MoeShape(**{**V4, "T": 0}).c()
+    assert lib.moe_combine_fp8(ctypes.byref(z), *([null] * 5), null) == 0
+    # a bad y_format is refused by moe_forward_ex before the workspace check
+    a = moe._CForwardArgs()
+    a.x_fp8 = a.x_scale = a.topk_ids = a.topk_w = a.w13 = a.w13_scale = 256
+    a.w2 = a.w2_scale = a.out_bf16 = 256
+    a.y_format = 5
+    assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(a), fake, 16, null) == -1
+    # FP8 rows and their exponent bytes fit where bf16 rows do, for any R
+    for T in (1, 3, 128, 65536):
+        s = moe.MoeShape(**{**V4, "T": T, "H": 128})
+        R = moe.moe_row_capacity(s)
+        assert moe.moe_workspace_size(s) >= R * (2 * 128) and moe.moe_workspace_size(s) > 0
