@@ -24,6 +24,7 @@ import torch
 __all__ = [
     "MoeShape", "MoeError", "lib", "library_path", "moe_check_shape", "moe_row_capacity",
     "moe_dispatch_workspace_size", "moe_workspace_size", "moe_workspace_status_offset",
+    "moe_workspace_init",
     "workspace_status", "moe_dispatch", "moe_gemm1_swiglu",
     "moe_gemm2", "moe_combine", "moe_gemm2_fp8", "moe_combine_fp8", "moe_resolve_y_format",
     "moe_forward", "moe_forward_persistent", "moe_forward_static",
@@ -43,7 +44,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_a8w4.so")
 
 EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size",
-            "moe_workspace_size", "moe_workspace_status_offset", "moe_dispatch",
+            "moe_workspace_size", "moe_workspace_status_offset", "moe_workspace_init",
+            "moe_dispatch",
             "moe_gemm1_swiglu", "moe_gemm2", "moe_gemm2_fp8", "moe_combine_fp8",
             "moe_resolve_y_format",
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
@@ -136,6 +138,8 @@ def lib() -> ctypes.CDLL:
         h.moe_workspace_size.restype = ctypes.c_size_t
         h.moe_workspace_status_offset.argtypes = [S]
         h.moe_workspace_status_offset.restype = ctypes.c_int64
+        h.moe_workspace_init.argtypes = [P, ctypes.c_size_t, P]
+        h.moe_workspace_init.restype = ctypes.c_int
         h.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         h.moe_dispatch.restype = ctypes.c_int
         h.moe_gemm1_swiglu.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
@@ -325,7 +329,19 @@ def alloc_dispatch(shape: MoeShape, device) -> DispatchBuffers:
 
 
 def alloc_workspace(shape: MoeShape, device) -> torch.Tensor:
-    return torch.empty(max(moe_workspace_size(shape), 1), dtype=torch.uint8, device=device)
+    """A moe_forward workspace for `shape`, its persistent-layer counters
+    zeroed (moe_workspace_init on the current stream)."""
+    ws = torch.empty(max(moe_workspace_size(shape), 4096), dtype=torch.uint8, device=device)
+    moe_workspace_init(ws)
+    return ws
+
+
+def moe_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero the persistent layer's counters at the start of a workspace."""
+    dev = workspace.device
+    ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
+    _check(lib().moe_workspace_init(ws, workspace.numel(), _stream(stream, dev)),
+           "moe_workspace_init")
 
 
 def moe_dispatch(shape: MoeShape, topk_ids, d: DispatchBuffers, stream=None,

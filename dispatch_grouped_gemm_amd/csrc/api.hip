@@ -25,8 +25,8 @@ bool all_aligned16(const P *...p)
 
 // Byte layout of the moe_forward workspace.
 struct Layout {
-    size_t counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, ys, xq, xqs,
-        total;
+    size_t hdr, counts, offsets, row_route, route_row, status, sync, scratch, h, hs, y, ys, xq,
+        xqs, total;
 };
 
 Layout layout_of(const moe_shape &s)
@@ -35,6 +35,10 @@ Layout layout_of(const moe_shape &s)
     const size_t TK = (size_t)s.T * (size_t)s.K;
     Layout L{};
     size_t p = 0;
+    // the persistent layer's counters: first, at a fixed place, so they stay
+    // where they were when a workspace serves other shapes
+    L.hdr = p;
+    p = align_up(p + sizeof(int32_t) * (size_t)moe::kPersistentHeaderWords);
     L.counts = p;
     p = align_up(p + sizeof(int32_t) * (size_t)s.E_local);
     L.offsets = p;
@@ -46,9 +50,12 @@ Layout layout_of(const moe_shape &s)
     L.status = p;
     p = align_up(p + sizeof(int32_t) * 4);
     L.sync = p;
-    p = align_up(p + sizeof(int32_t) * (size_t)moe::persistent_sync_words(s));
+    p = align_up(p + sizeof(int32_t) * (size_t)moe::persistent_ready_words(s));
     L.scratch = p;
-    p = align_up(p + moe::dispatch_scratch_bytes(s));
+    {
+        const size_t a = moe::dispatch_scratch_bytes(s), b = moe::persistent_table_bytes(s);
+        p = align_up(p + (a > b ? a : b));
+    }
     L.h = p;
     p = align_up(p + R * (size_t)s.I);
     L.hs = p;
@@ -163,6 +170,15 @@ size_t moe_workspace_size(const moe_shape *s)
     if (moe_check_shape(s) != MOE_OK)
         return 0;
     return layout_of(*s).total;
+}
+
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
+{
+    const size_t need = sizeof(int32_t) * (size_t)moe::kPersistentHeaderWords;
+    if (!ws || ws_bytes < need || ((uintptr_t)ws % kAlign) != 0)
+        return MOE_EWORKSPACE;
+    return hip_status(moe::launch_zero_words(static_cast<int32_t *>(ws),
+                                             moe::kPersistentHeaderWords, as_stream(stream)));
 }
 
 int64_t moe_workspace_status_offset(const moe_shape *s)
@@ -379,19 +395,30 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
                              : moe::YRows{reinterpret_cast<uint16_t *>(base + L.y), nullptr,
                                           nullptr};
     hipStream_t st = as_stream(stream);
+    if (persistent) {
+        // one launch (after the activation quant, when the rows come as bf16)
+        hipError_t e = qj ? moe::launch_quant_mxfp8(*qj, st) : hipSuccess;
+        const moe::PersistentBufs pb{counts,
+                                     offsets,
+                                     row_route,
+                                     route_row,
+                                     status,
+                                     reinterpret_cast<int32_t *>(base + L.hdr),
+                                     reinterpret_cast<int32_t *>(scratch),
+                                     reinterpret_cast<int32_t *>(base + L.sync),
+                                     h,
+                                     hs};
+        if (e == hipSuccess)
+            e = moe::launch_layer_persistent(*s, ids, valid, tw, x, xs, w13, w13s, w2, w2s, pb,
+                                             y, out, st);
+        return hip_status(e);
+    }
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st, nullptr, 0, qj, valid);
-    if (persistent) {
-        int32_t *sync = reinterpret_cast<int32_t *>(base + L.sync);
-        if (e == hipSuccess)
-            e = moe::launch_layer_persistent(*s, x, xs, counts, offsets, row_route, w13, w13s, w2,
-                                             w2s, h, hs, y, sync, status, st);
-    } else {
-        if (e == hipSuccess)
-            e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
-        if (e == hipSuccess)
-            e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
-    }
+    if (e == hipSuccess)
+        e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
+    if (e == hipSuccess)
+        e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
     if (e == hipSuccess)
         e = y.bf16 ? moe::launch_combine(*s, tw, route_row, y.bf16, out, st)
                    : moe::launch_combine_fp8(*s, tw, route_row, y.codes, y.scales, out, st);

@@ -32,73 +32,18 @@ combine_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict_
         combine_cols(s, tw, route_row, y, out, t, col);
 }
 
-// The combine of MX FP8 rows (e4m3 codes [R, H], E8M0 bytes [R, H/32]): a
-// thread owns 16 columns of one token (one 16-byte piece of each kept row
-// and its block's exponent byte); every value is decoded exactly (the
-// hardware e4m3 conversion, then ldexp by byte - 127), then summed as in
-// combine_cols: float32, k ascending, a product then an add per term, one
-// bf16 rounding.
-constexpr int kCombine8Vec = 16;
-
 __global__ void __launch_bounds__(kThreads)
 combine_fp8_kernel(Shape s, const float *__restrict__ tw, const int32_t *__restrict__ route_row,
                    const uint8_t *__restrict__ yc, const uint8_t *__restrict__ ys,
                    uint16_t *__restrict__ out)
 {
-#pragma clang fp contract(off)
     const int pieces = s.H / kCombine8Vec;
     const long i = (long)blockIdx.x * kThreads + threadIdx.x;
     if (i >= (long)s.T * pieces)
         return;
     const int t = (int)(i / pieces);
     const int col = (int)(i - (long)t * pieces) * kCombine8Vec;
-    constexpr int kMaxK = 8;
-    const size_t slot0 = (size_t)t * s.K;
-    int rows[kMaxK];
-    float w[kMaxK];
-#pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
-        rows[k] = k < s.K ? route_row[slot0 + k] : -1;
-        w[k] = k < s.K ? tw[slot0 + k] : 0.0f;
-    }
-    uint4 q[kMaxK];
-    int e[kMaxK];
-#pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-        if (rows[k] >= 0) {
-            q[k] = *reinterpret_cast<const uint4 *>(yc + (size_t)rows[k] * s.H + col);
-            e[k] = (int)ys[(size_t)rows[k] * (s.H / 32) + col / 32] - 127;
-        }
-    float acc[kCombine8Vec];
-#pragma unroll
-    for (int j = 0; j < kCombine8Vec; ++j)
-        acc[j] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
-        if (rows[k] < 0)
-            continue;
-        const int wd[4] = {(int)q[k].x, (int)q[k].y, (int)q[k].z, (int)q[k].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const float v[4] = {__builtin_amdgcn_cvt_f32_fp8(wd[d], 0),
-                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 1),
-                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 2),
-                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 3)};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float p = w[k] * ldexpf(v[b], e[k]);
-                acc[4 * d + b] = acc[4 * d + b] + p;
-            }
-        }
-    }
-    uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        o[j] = f32_to_bf16(acc[2 * j]) | (f32_to_bf16(acc[2 * j + 1]) << 16);
-    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-    u4v *dst = reinterpret_cast<u4v *>(out + (size_t)t * s.H + col);
-    __builtin_nontemporal_store(u4v{o[0], o[1], o[2], o[3]}, dst);
-    __builtin_nontemporal_store(u4v{o[4], o[5], o[6], o[7]}, dst + 1);
+    combine8_cols(s, tw, route_row, yc, ys, out, t, col);
 }
 
 } // namespace

@@ -37,7 +37,7 @@
 #include <mutex>
 #include <type_traits>
 
-#include "moe_common.hpp"
+#include "dispatch_dev.hpp"
 
 namespace moe {
 
@@ -89,11 +89,26 @@ __device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
 // kL2 reads data that another CU of the same XCD wrote earlier in the same
 // launch: sc0 makes the load miss the CU's own L1, which may hold the line
 // from before the write, and take it from the XCD's L2, where the write is.
+// A pointer every lane holds the same value of, in scalar registers (the
+// LDS DMA loads take their base from an SGPR pair).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+
 template <int SIZE, bool kStream = false, bool kL2 = false>
 __device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
 {
     static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
     static_assert(!(kStream && kL2), "one cache policy");
+    // both are wavefront-uniform by construction; readfirstlane tells the
+    // compiler so where its analysis cannot see it (it costs nothing when
+    // the values already sit in scalar registers)
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    base = uniform_ptr(base);
     if (SIZE == 16 && kL2)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc0" ::"s"(m0),
                      "v"(voff), "s"(base)
@@ -185,11 +200,12 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
         // one expert's weights or one row tile (GEMM1's gathered x rows are
         // addressed from x itself: T * H < 2^32 is checked on the host)
         const size_t wrows = kGemm1 ? 2 * (size_t)I : (size_t)H;
-        const uint8_t *__restrict__ w = g.w + (size_t)e * wrows * (size_t)(KT / 2);
-        const uint8_t *__restrict__ ws = g.ws + (size_t)e * wrows * (size_t)(KT / 32);
-        const uint8_t *__restrict__ act = kGemm1 ? g.act : g.act + (size_t)row0 * (size_t)KT;
+        const uint8_t *__restrict__ w = uniform_ptr(g.w + (size_t)e * wrows * (size_t)(KT / 2));
+        const uint8_t *__restrict__ ws = uniform_ptr(g.ws + (size_t)e * wrows * (size_t)(KT / 32));
+        const uint8_t *__restrict__ act =
+            uniform_ptr(kGemm1 ? g.act : g.act + (size_t)row0 * (size_t)KT);
         const uint8_t *__restrict__ act_s =
-            kGemm1 ? g.act_s : g.act_s + (size_t)row0 * (size_t)(KT / 32);
+            uniform_ptr(kGemm1 ? g.act_s : g.act_s + (size_t)row0 * (size_t)(KT / 32));
         if (tid < BM) {
             const int r = min(tid, nrows - 1);
             arow[tid] = kGemm1 ? row_route[row0 + r] / s.K : r;
@@ -595,92 +611,461 @@ struct TileShared {
 };
 
 // ---------------------------------------------------------------------------
-// The persistent layer for 128-row tiles: GEMM1 + SwiGLU + requant and GEMM2
-// in one launch, one work queue per XCD.  Row chunk q belongs to queue
-// q mod nq; a workgroup serves the queue of the XCD it runs on (hardware
-// XCC id mod nq, nq = the device's XCD count), so the h rows of a chunk are
-// written and read through one L2.  A queue hands out tickets for first
-// every GEMM1 item of its chunks, then every GEMM2 item; a GEMM2 item of
-// chunk q waits until ready[q] counts all NT1 GEMM1 items of q, so GEMM2
-// starts on the first chunks while GEMM1 finishes the last ones.  A
-// workgroup takes its next ticket when it starts an item (the atomic's
-// round trip hides behind the item); tickets go out in dependency order
-// and a workgroup's tickets rise, so every wait is on items that running
-// workgroups hold and reach first.  A GEMM1 item counts in ready[q] once
-// its h stores are in the L2; GEMM2 reads h past the CU's L1.
-// sync[32 x] is queue x's ticket counter (one 128-byte line each),
-// sync[256 + q] = ready[q], all zero at launch.  Every wait is bounded by
-// max_polls: past the bound the workgroup counts the timeout in status[2]
-// and goes on (its GEMM2 item may then read h before it is written), so
-// the caller sees a failed layer instead of a GPU that never finishes.
-template <int BM, int BN1, int BN2, int KU>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-layer_persistent_kernel(Shape s, TiledArgs g1, TiledArgs g2, int32_t *sync, int32_t *status,
-                        int nq, int max_polls)
+// The persistent layer: dispatch, GEMM1 + SwiGLU + requant, GEMM2 and the
+// combine in one launch ("MegaMoEV2: fuse Dispatch, GEMM1, GEMM2 and Combine
+// into one kernel", Technical Details, large input: one persistent kernel
+// overlaps the stages).  Every workgroup of the grid (all resident: the grid
+// is the device's CUs times the kernel's occupancy) runs the phases in turn:
+//
+//  1. Dispatch.  Slice b of the route slots (b below min(grid, kMaxSlices)):
+//     compact: per-wavefront histograms, the slice's totals into row b of a
+//     table; after a grid barrier every workgroup sums the table (segment
+//     sizes, and for its own slice the rows before it), scans the experts
+//     and scatters its slots stably; a second barrier publishes row_route
+//     and route_row.  Fixed-slot: wave-aggregated claims on per-expert
+//     counters in the header, then one barrier.
+//  2. GEMM1 and GEMM2 from one work queue per XCD (chunk q on queue q mod
+//     nq, served by the workgroups running on that XCD, so h is written and
+//     read through one L2): all GEMM1 tickets of a queue before its GEMM2
+//     tickets; a GEMM2 item of chunk q waits until ready[q] counts all NT1
+//     GEMM1 items of q.  Tickets map to (chunk, N tile) in blocks of bq
+//     chunks x bnt N tiles, so each round of an XCD's workgroups shares
+//     weight tiles and activation rows in its L2 (the pages' n-major claims
+//     when an expert is large: a weight tile serves bq row chunks in turn).
+//  3. After a grid barrier (every workgroup done with its tickets, y made
+//     visible device-wide), the combine of every token.
+//
+// Barriers: each workgroup makes its stores visible at device scope (a
+// release fence, once per barrier and workgroup), adds itself to a counter
+// and polls it (relaxed), then takes an acquire fence.  Every wait is
+// bounded by max_polls: a barrier that gives up is counted and sends its
+// workgroup straight to the end, so no phase ever reads data that was not
+// written (a GEMM2 wait that gives up goes on with h that may be stale but
+// is in bounds); the caller sees the count in status[2].
+//
+// The header (the first kHdrWords words of the workspace) must be zero at
+// launch; the last workgroup to finish copies the status words out and
+// zeroes it again, so a workspace stays ready for the next call.
+constexpr int kHdrTicket = 0;      // + 32 x: ticket counter of XCD queue x < 8
+constexpr int kHdrBarrier = 256;   // barrier arrivals, cumulative
+constexpr int kHdrDepart = 288;    // workgroups finished
+constexpr int kHdrInvalid = 320;   // ids outside [-1, E_total)
+constexpr int kHdrDropped = 352;   // fixed-slot routes past capacity
+constexpr int kHdrTimeouts = 384;  // waits that gave up
+constexpr int kHdrClaims = 512;    // fixed-slot claim counter of each local expert
+constexpr int kMaxSlices = 256;    // compact histogram table rows
+static_assert(kHdrClaims + kMaxLocalExperts <= kPersistentHeaderWords, "header size");
+
+struct FusedArgs {
+    const int32_t *ids, *valid;
+    const float *tw;
+    const uint8_t *x, *xs, *w13, *w13s, *w2, *w2s;
+    int32_t *counts, *offsets, *row_route, *route_row, *status;
+    int32_t *hdr;      // kPersistentHeaderWords, zero at launch and at exit
+    int32_t *table;    // [kMaxSlices][E_local + 1] slice histograms (compact)
+    int32_t *ready;    // nready words: finished GEMM1 items per row chunk
+    int nready;
+    uint8_t *h, *hs;
+    uint16_t *y;       // bf16 rows, or
+    uint8_t *y8, *y8s; // MX FP8 rows
+    uint16_t *out;
+};
+
+// Wavefront 0 polls *p (relaxed, device scope) until it reaches target, at
+// most max_polls times; returns whether it did (in every lane).
+__device__ __forceinline__ bool poll_at_least(const int32_t *p, int target, int max_polls)
 {
-    // one stage ring, sized for the wider of the two weight tiles
-    __shared__ TileShared<BM, (BN1 > BN2 ? BN1 : BN2), KU> sh;
-    __shared__ int ticket_sh;
+    for (int it = 0; it < max_polls; ++it) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (v >= target)
+            return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+// Grid barrier number n (1, 2, ...): true when every workgroup of the grid
+// arrived.  ok_sh is the workgroup's LDS word for the result.
+__device__ __forceinline__ bool grid_barrier(int32_t *hdr, int n, int max_polls, int *ok_sh)
+{
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int NT1 = s.I / (BN1 / 2), NT2 = s.H / BN2;
-    const int nchunks = plan_chunks(s, g1.counts, BM, sh.prefix);
-    unsigned xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    const int x = (int)(xcc & 7u) % nq;
-    const int mine = nchunks > x ? (nchunks - x + nq - 1) / nq : 0;
-    const int n1 = mine * NT1, n2 = mine * NT2;
-    int32_t *ticket = sync + 32 * x, *ready = sync + 256;
-    // wavefront 0 takes tickets (whole-wavefront atomic, value 1 in lane 0:
-    // control flow stays uniform) and hands them to the others through LDS
+    wait_vmcnt<0>();   // this thread's stores are done
+    __syncthreads();   // ... and every thread's
     if (wave == 0) {
-        const int t0 = atomicAdd(ticket, lane == 0 ? 1 : 0);
-        ticket_sh = __builtin_amdgcn_readfirstlane(t0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        atomicAdd(&hdr[kHdrBarrier], lane == 0 ? 1 : 0);
+        const bool ok = poll_at_least(&hdr[kHdrBarrier], n * (int)gridDim.x, max_polls);
+        if (!ok)
+            atomicAdd(&hdr[kHdrTimeouts], lane == 0 ? 1 : 0);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0)
+            *ok_sh = ok;
     }
     __syncthreads();
-    for (;;) {
-        const int t = ticket_sh;
-        __syncthreads();
-        if (t >= n1 + n2)
-            break;
-        int next = 0;
-        if (wave == 0)
-            next = atomicAdd(ticket, lane == 0 ? 1 : 0);
-        if (t < n1) {
-            const int q = x + nq * (t / NT1), nt = t % NT1;
-            tiled_item<true, BM, BN1, KU, false>(s, g1, sh.prefix, sh.arow, sh.ring, q, nt);
-            wait_vmcnt<0>();   // this thread's h stores are in the L2
-            __syncthreads();   // ... and every thread's
-            if (wave == 0)
-                atomicAdd(&ready[q], lane == 0 ? 1 : 0);
-        } else {
-            const int q = x + nq * ((t - n1) / NT2), nt = (t - n1) % NT2;
-            if (wave == 0) {
-                bool done = false;
-                for (int it = 0; it < max_polls; ++it) {
-                    const int v = __builtin_amdgcn_readfirstlane(
-                        __hip_atomic_load(&ready[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    if (v >= NT1) {
-                        done = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
+    return __builtin_amdgcn_readfirstlane(*ok_sh) != 0;
+}
+
+// Ticket t of a queue with `mine` row chunks and NT N tiles -> (local chunk
+// index, N tile): blocks of bq chunks x bnt N tiles, clipped at the edges,
+// chunk blocks outer, N blocks inner, chunk-major inside a block.
+__device__ __forceinline__ void queue_item(int t, int mine, int NT, int bq, int bnt, int &qi,
+                                           int &nt)
+{
+    const int full = bq * NT;
+    const int qb = t / full, r = t - qb * full;
+    const int cb = min(bq, mine - qb * bq);
+    const int nb = r / (cb * bnt), r2 = r - nb * cb * bnt;
+    const int nbw = min(bnt, NT - nb * bnt);
+    qi = qb * bq + r2 / nbw;
+    nt = nb * bnt + r2 % nbw;
+}
+
+// The combine of token t over chunks c0 .. c0 + nc - 1 of 64 pieces of its
+// row (lane l takes piece 64 c + l of each): the kept routes in ascending k,
+// each route's pieces loaded together, the same float32 arithmetic as
+// combine_cols / combine8_cols (so the same bits).  kFP8: pieces of 16
+// columns of MX FP8 rows, else 8 columns of bf16 rows.
+template <bool kFP8, int U>
+__device__ __forceinline__ void combine_row_part(const Shape &s, const FusedArgs &a, int t, int c0,
+                                                 int nc)
+{
+#pragma clang fp contract(off)
+    constexpr int V = kFP8 ? 16 : 8;
+    const int lane = threadIdx.x & 63;
+    float acc[U][V];
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            acc[j][v] = 0.0f;
+    for (int k = 0; k < s.K; ++k) {
+        const int row = __builtin_amdgcn_readfirstlane(a.route_row[(size_t)t * s.K + k]);
+        if (row < 0)
+            continue;
+        const float w = a.tw[(size_t)t * s.K + k];
+        uint4 q[U];
+        int e[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            if (j < nc) {
+                const int col = ((c0 + j) * 64 + lane) * V;
+                if (kFP8) {
+                    q[j] = *reinterpret_cast<const uint4 *>(a.y8 + (size_t)row * s.H + col);
+                    e[j] = (int)a.y8s[(size_t)row * (s.H / 32) + col / 32] - 127;
+                } else {
+                    q[j] = *reinterpret_cast<const uint4 *>(a.y + (size_t)row * s.H + col);
                 }
-                if (!done)
-                    atomicAdd(&status[2], lane == 0 ? 1 : 0);
             }
-            __syncthreads();
-            tiled_item<false, BM, BN2, KU, true>(s, g2, sh.prefix, sh.arow, sh.ring, q, nt);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (j >= nc)
+                break;
+            const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                if (kFP8) {
+                    const float v[4] = {__builtin_amdgcn_cvt_f32_fp8((int)wd[d], 0),
+                                        __builtin_amdgcn_cvt_f32_fp8((int)wd[d], 1),
+                                        __builtin_amdgcn_cvt_f32_fp8((int)wd[d], 2),
+                                        __builtin_amdgcn_cvt_f32_fp8((int)wd[d], 3)};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float p = w * ldexpf(v[b], e[j]);
+                        acc[j][4 * d + b] = acc[j][4 * d + b] + p;
+                    }
+                } else {
+                    const float p0 = w * __uint_as_float(wd[d] << 16);
+                    const float p1 = w * __uint_as_float(wd[d] & 0xffff0000u);
+                    acc[j][2 * d] = acc[j][2 * d] + p0;
+                    acc[j][2 * d + 1] = acc[j][2 * d + 1] + p1;
+                }
+            }
         }
-        if (wave == 0)
-            ticket_sh = __builtin_amdgcn_readfirstlane(next);
-        __syncthreads();
+    }
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        if (j >= nc)
+            break;
+        const int col = ((c0 + j) * 64 + lane) * V;
+        u4v *dst = reinterpret_cast<u4v *>(a.out + (size_t)t * s.H + col);
+#pragma unroll
+        for (int g = 0; g < V / 8; ++g) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = f32_to_bf16(acc[j][8 * g + 2 * i]) |
+                       (f32_to_bf16(acc[j][8 * g + 2 * i + 1]) << 16);
+            __builtin_nontemporal_store(u4v{o[0], o[1], o[2], o[3]}, dst + g);
+        }
     }
 }
 
-__global__ void __launch_bounds__(256) fill_zero_kernel(int32_t *p, int n)
+// The combine phase: wavefront tasks of up to U 64-piece chunks of one
+// token's row where a row is a whole number of such chunks (H a multiple of
+// 512 for bf16 rows, 1024 for FP8 rows), else one piece per thread.
+template <bool kFP8>
+__device__ __forceinline__ void combine_phase(const Shape &s, const FusedArgs &a)
 {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
-        p[i] = 0;
+    constexpr int U = 4;
+    const int V = kFP8 ? kCombine8Vec : kCombineVec;
+    const int NTH = blockDim.x, NW = NTH / 64;
+    const int pieces = s.H / V;
+    if (pieces % 64 == 0) {
+        const int C = pieces / 64, TPR = (C + U - 1) / U;
+        const long tasks = (long)s.T * TPR;
+        for (long task = (long)blockIdx.x * NW + (threadIdx.x >> 6); task < tasks;
+             task += (long)gridDim.x * NW) {
+            const int t = __builtin_amdgcn_readfirstlane((int)(task / TPR));
+            const int c0 = __builtin_amdgcn_readfirstlane((int)(task - (long)t * TPR) * U);
+            combine_row_part<kFP8, U>(s, a, t, c0, min(U, C - c0));
+        }
+        return;
+    }
+    const long n = (long)s.T * pieces;
+    for (long i = (long)blockIdx.x * NTH + threadIdx.x; i < n; i += (long)gridDim.x * NTH) {
+        const int t = (int)(i / pieces);
+        const int col = (int)(i - (long)t * pieces) * V;
+        if (kFP8)
+            combine8_cols(s, a.tw, a.route_row, a.y8, a.y8s, a.out, t, col);
+        else
+            combine_cols(s, a.tw, a.route_row, a.y, a.out, t, col);
+    }
+}
+
+template <int BM, int BN1, int BN2, int KU, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+layer_persistent_kernel(Shape s, FusedArgs a, int nq, int max_polls)
+{
+    constexpr int NTH = NW * 64;
+    constexpr int BN = BN1 > BN2 ? BN1 : BN2;
+    // (within 80 KB for the 128-row tiles: two workgroups per CU)
+    __shared__ TileShared<BM, BN, KU> sh;
+    __shared__ int ticket_sh, ok_sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = gridDim.x, blk = blockIdx.x;
+    const int E = s.E_local, E1 = E + 1;
+    const bool fixed = s.mode == MOE_DISPATCH_FIXED_SLOT;
+    int32_t *hdr = a.hdr;
+    int barriers = 0;
+    bool ok = true;
+
+    // ---- 1. dispatch -------------------------------------------------------
+    // LDS (the stage ring, free until the GEMMs): per-wavefront histograms
+    // [NW][E], partial table sums [2 NW][E + 1], segment sizes [E] and
+    // offsets [E + 1]
+    int *wh = reinterpret_cast<int *>(sh.ring);
+    int *part = wh + NW * E;
+    int *cnt = part + 2 * NW * E1;
+    int *offs = cnt + E;
+    static_assert(sizeof(sh.ring) >= sizeof(int) * (NW * kMaxLocalExperts +
+                                                    2 * NW * (kMaxLocalExperts + 1) +
+                                                    2 * kMaxLocalExperts + 1),
+                  "dispatch tables fit the stage ring");
+    const long n = (long)s.T * s.K;
+    const long nv = valid_slots(s, a.valid);
+    const int nsl = G < kMaxSlices ? G : kMaxSlices;
+    const long per = (n + nsl - 1) / nsl;
+    const long sb = blk < nsl ? min(n, per * blk) : n, se = blk < nsl ? min(n, sb + per) : n;
+    const long pw = (se - sb + NW - 1) / NW;
+    const long wb = min(se, sb + pw * wave), we = min(se, wb + pw);
+    for (int i = blk * NTH + tid; i < a.nready; i += G * NTH)
+        a.ready[i] = 0;
+    if (fixed) {
+        int inv = 0, drop = 0;
+        if (blk < nsl)
+            claim_slots<kBatch, false>(s, a.ids, wb, we, nv, hdr + kHdrClaims, a.row_route,
+                                       a.route_row, inv, drop);
+        inv = wave_sum(inv);
+        drop = wave_sum(drop);
+        if (inv)
+            atomicAdd(&hdr[kHdrInvalid], lane == 0 ? inv : 0);
+        if (drop)
+            atomicAdd(&hdr[kHdrDropped], lane == 0 ? drop : 0);
+        ok = grid_barrier(hdr, ++barriers, max_polls, &ok_sh);
+        if (ok && blk == 0) {
+            for (int e = tid; e < E; e += NTH) {
+                a.counts[e] = __hip_atomic_load(&hdr[kHdrClaims + e], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                a.offsets[e] = e * s.capacity;
+            }
+            if (tid == 0)
+                a.offsets[E] = E * s.capacity;
+        }
+    } else {
+        if (blk < nsl) {
+            for (int i = tid; i < NW * E; i += NTH)
+                wh[i] = 0;
+            __syncthreads();
+            const int inv = wave_histogram<kBatch>(s, a.ids, wb, we, nv, wh + wave * E);
+            if (inv)
+                atomicAdd(&hdr[kHdrInvalid], lane == 0 ? inv : 0);
+            __syncthreads();
+            for (int e = tid; e < E; e += NTH) {
+                int c = 0;
+                for (int w = 0; w < NW; ++w)
+                    c += wh[w * E + e];
+                a.table[(size_t)blk * E1 + e] = c;
+            }
+        }
+        ok = grid_barrier(hdr, ++barriers, max_polls, &ok_sh);
+        if (ok && (blk < nsl || blk == 0)) {
+            // wavefront w sums table rows w, w + NW, ...: over all slices
+            // (segment sizes) and over the slices before this one
+            for (int c = lane; c < E; c += 64) {
+                int before = 0, all = 0;
+                for (int b = wave; b < nsl; b += NW) {
+                    const int v = a.table[(size_t)b * E1 + c];
+                    all += v;
+                    before += b < blk ? v : 0;
+                }
+                part[wave * E1 + c] = all;
+                part[(NW + wave) * E1 + c] = before;
+            }
+            __syncthreads();
+            for (int e = tid; e < E; e += NTH) {
+                int all = 0;
+                for (int w = 0; w < NW; ++w)
+                    all += part[w * E1 + e];
+                cnt[e] = all;
+            }
+            __syncthreads();
+            scan_experts<NTH>(E, [&](int e) { return cnt[e]; }, offs);
+            if (blk == 0) {
+                for (int e = tid; e < E; e += NTH) {
+                    a.counts[e] = cnt[e];
+                    a.offsets[e] = offs[e];
+                }
+                if (tid == 0)
+                    a.offsets[E] = offs[E];
+            }
+            if (blk < nsl) {
+                // this slice's first row in each segment, then per wavefront
+                for (int e = tid; e < E; e += NTH) {
+                    int run = offs[e];
+                    for (int w = 0; w < NW; ++w)
+                        run += part[(NW + w) * E1 + e];
+                    for (int w = 0; w < NW; ++w) {
+                        const int c = wh[w * E + e];
+                        wh[w * E + e] = run;
+                        run += c;
+                    }
+                }
+                __syncthreads();
+                for (long base = wb; base < we; base += 64 * kBatch) {
+                    int ex[kBatch];
+                    load_keys<kBatch>(s, a.ids, base, we, nv, ex);
+                    scatter_keys<kBatch>(ex, base, we, wh + wave * E, a.row_route, a.route_row);
+                }
+            }
+        }
+    }
+    // counts, offsets, row_route and route_row published to every workgroup
+    if (ok)
+        ok = grid_barrier(hdr, ++barriers, max_polls, &ok_sh);
+
+    // ---- 2. GEMM1 and GEMM2 from the XCD's queue -------------------------------
+    if (ok) {
+        const int NT1 = s.I / (BN1 / 2), NT2 = s.H / BN2;
+        const int nchunks =
+            __builtin_amdgcn_readfirstlane(plan_chunks<NTH>(s, a.counts, BM, sh.prefix));
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        const int x = (int)(xcc & 7u) % nq;
+        const int mine = nchunks > x ? (nchunks - x + nq - 1) / nq : 0;
+        const int n1 = mine * NT1, n2 = mine * NT2;
+        // blocks of bq chunks x bnt N tiles per round of the XCD's workgroups
+        const int per_xcd = G / nq > 0 ? G / nq : 1;
+        const int bnt1 = min(NT1, 8), bnt2 = min(NT2, 8);
+        const int bq1 = max(1, per_xcd / bnt1), bq2 = max(1, per_xcd / bnt2);
+        const TiledArgs g1{a.x, a.xs, a.counts, a.offsets, a.row_route, a.w13, a.w13s, a.h, a.hs,
+                           nullptr, nullptr, nullptr};
+        const TiledArgs g2{a.h, a.hs, a.counts, a.offsets, nullptr, a.w2, a.w2s, nullptr, nullptr,
+                           a.y, a.y8, a.y8s};
+        int32_t *ticket = hdr + kHdrTicket + 32 * x;
+        if (wave == 0) {
+            const int t0 = atomicAdd(ticket, lane == 0 ? 1 : 0);
+            ticket_sh = __builtin_amdgcn_readfirstlane(t0);
+        }
+        __syncthreads();
+        for (;;) {
+            const int t = __builtin_amdgcn_readfirstlane(ticket_sh);
+            __syncthreads();
+            if (t >= n1 + n2)
+                break;
+            int next = 0;
+            if (wave == 0)
+                next = atomicAdd(ticket, lane == 0 ? 1 : 0);
+            int qi, nt;
+            if (t < n1) {
+                queue_item(t, mine, NT1, bq1, bnt1, qi, nt);
+                const int q = x + nq * qi;
+                tiled_item<true, BM, BN1, KU, false, NW>(s, g1, sh.prefix, sh.arow, sh.ring, q,
+                                                         nt);
+                wait_vmcnt<0>();   // this thread's h stores are in the L2
+                __syncthreads();   // ... and every thread's
+                if (wave == 0)
+                    atomicAdd(&a.ready[q], lane == 0 ? 1 : 0);
+            } else {
+                queue_item(t - n1, mine, NT2, bq2, bnt2, qi, nt);
+                const int q = x + nq * qi;
+                if (wave == 0) {
+                    const bool done = poll_at_least(&a.ready[q], NT1, max_polls);
+                    if (!done)
+                        atomicAdd(&hdr[kHdrTimeouts], lane == 0 ? 1 : 0);
+                    if (lane == 0)
+                        ok_sh = done;
+                }
+                __syncthreads();
+                // a wait that gave up: this workgroup takes no more tickets
+                // (the layer is reported failed), so a lost GEMM1 item costs
+                // one bounded wait per workgroup, not one per GEMM2 item
+                if (!__builtin_amdgcn_readfirstlane(ok_sh)) {
+                    ok = false;
+                    break;
+                }
+                tiled_item<false, BM, BN2, KU, true, NW>(s, g2, sh.prefix, sh.arow, sh.ring, q,
+                                                         nt);
+            }
+            if (wave == 0)
+                ticket_sh = __builtin_amdgcn_readfirstlane(next);
+            __syncthreads();
+        }
+        // every workgroup that reached the GEMMs meets here (also one whose
+        // wait gave up, so the others are not held up by it)
+        const bool met = grid_barrier(hdr, ++barriers, max_polls, &ok_sh);
+        ok = ok && met;
+    }
+
+    // ---- 3. combine ---------------------------------------------------------------
+    if (ok) {
+        if (a.y8)
+            combine_phase<true>(s, a);
+        else
+            combine_phase<false>(s, a);
+    }
+
+    // ---- the end: the last workgroup reports and clears the header -------------
+    __syncthreads();
+    if (wave == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const int old = __builtin_amdgcn_readfirstlane(atomicAdd(&hdr[kHdrDepart], lane == 0 ? 1 : 0));
+        if (old == G - 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (lane == 0) {
+                a.status[0] = __hip_atomic_load(&hdr[kHdrInvalid], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                a.status[1] = __hip_atomic_load(&hdr[kHdrDropped], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                a.status[2] = __hip_atomic_load(&hdr[kHdrTimeouts], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                a.status[3] = 0;
+            }
+            for (int i = lane; i < kPersistentHeaderWords; i += 64)
+                __hip_atomic_store(&hdr[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Row chunk q and N tile nt of grid-stride item `item` (workgroup blockIdx.x
@@ -954,33 +1339,41 @@ bool tile_config_of(const moe_shape &s, bool gemm1, int *bm, int *bn, int *ku)
     return true;
 }
 
-// The tile config of the persistent layer: that of the launches, with
-// 256-row tiles run as 128 rows (the persistent kernels are built for four
-// wavefronts and two workgroups per CU).
+// The tile config of the persistent layer: that of the launches.  The
+// 256-row tile (eight wavefronts, one workgroup per CU) runs when both GEMMs
+// take it; a 256-row tile next to another row tile runs as 128 rows.
 static TiledConfig persistent_config(const moe_shape &sh, bool gemm1)
 {
-    TiledConfig c = tiled_config(sh, gemm1);
-    if (c.bm == 256)
-        c.bm = 128;
+    const TiledConfig a = tiled_config(sh, true), b = tiled_config(sh, false);
+    TiledConfig c = gemm1 ? a : b;
+    if (c.bm == 256 && !(a.bm == 256 && b.bm == 256))
+        c = TiledConfig{128, 256, 1};
     return c;
 }
 
 // The persistent layer takes the tiled GEMMs when both use the same row
-// tile: 128 rows with one K step per stage (any weight tile widths) or 32 or
-// 64 rows with two K steps and 128 weight rows; on a device whose XCDs it
-// can tell apart.
+// tile: 256 rows (256 weight rows, one K step), 128 rows with one K step per
+// stage (any weight tile widths), or 32 or 64 rows with two K steps and 128
+// weight rows; on a device whose XCDs it can tell apart.
 bool persistent_supported(const moe_shape &sh)
 {
-    if (sh.H < 512 || sh.I < 512 || xcd_count() == 0)
+    if (sh.H < 512 || sh.I < 512 || xcd_count() == 0 || sh.E_local > kMaxLocalExperts)
         return false;
     const TiledConfig a = persistent_config(sh, true), b = persistent_config(sh, false);
+    if (a.bm == 256 && b.bm == 256)
+        return a.bn == 256 && b.bn == 256 && a.ku == 1 && b.ku == 1;
     if (a.bm == 128 && b.bm == 128 && a.ku == 1 && b.ku == 1)
         return true;
     return (a.bm == 32 || a.bm == 64) && b.bm == a.bm && a.ku == 2 && b.ku == 2 && a.bn == 128 &&
            b.bn == 128;
 }
 
-int persistent_sync_words(const moe_shape &sh) { return 256 + (int)tile_upper_bound(sh, 32); }
+int persistent_ready_words(const moe_shape &sh) { return (int)tile_upper_bound(sh, 32); }
+
+size_t persistent_table_bytes(const moe_shape &sh)
+{
+    return sizeof(int32_t) * (size_t)kMaxSlices * (size_t)(sh.E_local + 1);
+}
 
 // Polls of a persistent wait before it gives up (2^22 polls of s_sleep 2,
 // about a second); MOE_PERSISTENT_MAX_POLLS in the environment, read at
@@ -997,42 +1390,56 @@ static int persistent_max_polls()
     return *end == 0 && n >= 0 && n < kDefault ? (int)n : kDefault;
 }
 
-hipError_t launch_layer_persistent(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
-                                   const int32_t *counts, const int32_t *offsets,
-                                   const int32_t *row_route, const uint8_t *w13,
-                                   const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
-                                   uint8_t *h, uint8_t *hs, const YRows &y, int32_t *sync,
-                                   int32_t *status, hipStream_t st)
+hipError_t launch_layer_persistent(const moe_shape &sh, const int32_t *ids, const int32_t *valid,
+                                   const float *tw, const uint8_t *x, const uint8_t *xs,
+                                   const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                                   const uint8_t *w2s, const PersistentBufs &b, const YRows &y,
+                                   uint16_t *out, hipStream_t st)
 {
-    const int nsync = persistent_sync_words(sh);
-    fill_zero_kernel<<<(nsync + 255) / 256, 256, 0, st>>>(sync, nsync);
-    const TiledArgs g1{x, xs, counts, offsets, row_route, w13, w13s, h, hs, nullptr, nullptr,
-                       nullptr};
-    const TiledArgs g2{h, hs, counts, offsets, nullptr, w2, w2s, nullptr, nullptr, y.bf16,
-                       y.codes, y.scales};
-    const TiledConfig c1 = persistent_config(sh, true);
-    const int bn1 = c1.bn, bn2 = persistent_config(sh, false).bn;
+    const FusedArgs a{ids,       valid,      tw,      x,         xs,       w13,
+                      w13s,      w2,         w2s,     b.counts,  b.offsets, b.row_route,
+                      b.route_row, b.status, b.hdr,   b.table,   b.ready,  persistent_ready_words(sh),
+                      b.h,       b.hs,       y.bf16,  y.codes,   y.scales, out};
+    const TiledConfig c1 = persistent_config(sh, true), c2 = persistent_config(sh, false);
     const int nq = xcd_count();
-    // workgroup b runs on XCD b mod nq: a grid of nq or more workgroups puts
-    // at least one on every XCD, so every queue is served
-    auto go = [&](auto k, int bm, int b1, int b2) {
-        const long items = tile_upper_bound(sh, bm) * (long)(sh.I / (b1 / 2) + sh.H / b2);
-        const int grid = tiled_grid(k, items);
-        k<<<grid > nq ? grid : nq, kThreads, 0, st>>>(to_dev(sh), g1, g2, sync, status, nq,
-                                                        persistent_max_polls());
+    // every workgroup resident at once (the grid barriers wait for all of
+    // them): the device's CUs times the kernel's occupancy
+    auto go = [&](auto k, int nw) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, nw * 64, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        const int grid = device_cu_count() * per_cu;
+        k<<<grid, nw * 64, 0, st>>>(to_dev(sh), a, nq, persistent_max_polls());
     };
-    if (c1.bm == 32)
-        go(layer_persistent_kernel<32, 128, 128, 2>, 32, 128, 128);
+    if (c1.bm == 256)
+        go(layer_persistent_kernel<256, 256, 256, 1, 8>, 8);
+    else if (c1.bm == 32)
+        go(layer_persistent_kernel<32, 128, 128, 2, 4>, 4);
     else if (c1.bm == 64)
-        go(layer_persistent_kernel<64, 128, 128, 2>, 64, 128, 128);
-    else if (bn1 == 256 && bn2 == 256)
-        go(layer_persistent_kernel<128, 256, 256, 1>, 128, 256, 256);
-    else if (bn1 == 256)
-        go(layer_persistent_kernel<128, 256, 128, 1>, 128, 256, 128);
-    else if (bn2 == 256)
-        go(layer_persistent_kernel<128, 128, 256, 1>, 128, 128, 256);
+        go(layer_persistent_kernel<64, 128, 128, 2, 4>, 4);
+    else if (c1.bn == 256 && c2.bn == 256)
+        go(layer_persistent_kernel<128, 256, 256, 1, 4>, 4);
+    else if (c1.bn == 256)
+        go(layer_persistent_kernel<128, 256, 128, 1, 4>, 4);
+    else if (c2.bn == 256)
+        go(layer_persistent_kernel<128, 128, 256, 1, 4>, 4);
     else
-        go(layer_persistent_kernel<128, 128, 128, 1>, 128, 128, 128);
+        go(layer_persistent_kernel<128, 128, 128, 1, 4>, 4);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ void __launch_bounds__(256) zero_words_kernel(int32_t *p, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+        p[i] = 0;
+}
+} // namespace
+
+hipError_t launch_zero_words(int32_t *p, int words, hipStream_t st)
+{
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, st>>>(p, words);
     return hipGetLastError();
 }
 

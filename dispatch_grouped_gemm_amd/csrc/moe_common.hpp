@@ -9,6 +9,9 @@
 namespace moe {
 
 constexpr int kMaxLocalExperts = 512;
+// int32 words at the start of the moe_forward workspace that the persistent
+// layer keeps its counters in (zero before its first call, zero after each)
+constexpr int kPersistentHeaderWords = 1024;
 
 // Kernel-side copy of moe_shape, passed by value.
 struct Shape {
@@ -309,6 +312,70 @@ __device__ __forceinline__ void combine_cols(const Shape &s, const float *__rest
                                 reinterpret_cast<u4v *>(out + (size_t)t * s.H + col));
 }
 
+// The combine of MX FP8 rows (e4m3 codes [R, H], E8M0 bytes [R, H/32]) for
+// output columns [col, col + 16) of token t: one 16-byte piece of each kept
+// row and its block's exponent byte; every value is decoded exactly (the
+// hardware e4m3 conversion, then ldexp by byte - 127), then summed as in
+// combine_cols: float32, k ascending, a product then an add per term, one
+// bf16 rounding.
+constexpr int kCombine8Vec = 16;
+
+__device__ __forceinline__ void combine8_cols(const Shape &s, const float *__restrict__ tw,
+                                              const int32_t *__restrict__ route_row,
+                                              const uint8_t *__restrict__ yc,
+                                              const uint8_t *__restrict__ ys,
+                                              uint16_t *__restrict__ out, int t, int col)
+{
+#pragma clang fp contract(off)
+    constexpr int kMaxK = 8;
+    const size_t slot0 = (size_t)t * s.K;
+    int rows[kMaxK];
+    float w[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        rows[k] = k < s.K ? route_row[slot0 + k] : -1;
+        w[k] = k < s.K ? tw[slot0 + k] : 0.0f;
+    }
+    uint4 q[kMaxK];
+    int e[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+        if (rows[k] >= 0) {
+            q[k] = *reinterpret_cast<const uint4 *>(yc + (size_t)rows[k] * s.H + col);
+            e[k] = (int)ys[(size_t)rows[k] * (s.H / 32) + col / 32] - 127;
+        }
+    float acc[kCombine8Vec];
+#pragma unroll
+    for (int j = 0; j < kCombine8Vec; ++j)
+        acc[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (rows[k] < 0)
+            continue;
+        const int wd[4] = {(int)q[k].x, (int)q[k].y, (int)q[k].z, (int)q[k].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float v[4] = {__builtin_amdgcn_cvt_f32_fp8(wd[d], 0),
+                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 1),
+                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 2),
+                                __builtin_amdgcn_cvt_f32_fp8(wd[d], 3)};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float p = w[k] * ldexpf(v[b], e[k]);
+                acc[4 * d + b] = acc[4 * d + b] + p;
+            }
+        }
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        o[j] = f32_to_bf16(acc[2 * j]) | (f32_to_bf16(acc[2 * j + 1]) << 16);
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    u4v *dst = reinterpret_cast<u4v *>(out + (size_t)t * s.H + col);
+    __builtin_nontemporal_store(u4v{o[0], o[1], o[2], o[3]}, dst);
+    __builtin_nontemporal_store(u4v{o[4], o[5], o[6], o[7]}, dst + 1);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (defined in the kernel sources).
 // ---------------------------------------------------------------------------
@@ -357,17 +424,26 @@ hipError_t launch_gemm2_tiled(const moe_shape &s, const uint8_t *h, const uint8_
                               const int32_t *counts, const int32_t *offsets, const uint8_t *w2,
                               const uint8_t *w2s, const YRows &y, hipStream_t st);
 bool persistent_supported(const moe_shape &s);
-int persistent_sync_words(const moe_shape &s);
-// GEMM1 + SwiGLU + requant and GEMM2 in one persistent launch (after a
-// zero-fill of sync[0 .. persistent_sync_words)); a wait that gives up
+// words of the persistent layer's per-chunk ready counters
+int persistent_ready_words(const moe_shape &s);
+// bytes of its dispatch table
+size_t persistent_table_bytes(const moe_shape &s);
+// The whole layer in one persistent launch: dispatch, GEMM1 + SwiGLU +
+// requant, GEMM2 and the combine.  hdr (kPersistentHeaderWords) must be zero
+// at launch and is zero again when the kernel ends; a wait that gives up
 // counts in status[2].
-hipError_t launch_layer_persistent(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
-                                   const int32_t *counts, const int32_t *offsets,
-                                   const int32_t *row_route, const uint8_t *w13,
-                                   const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s,
-                                   uint8_t *h, uint8_t *hs, const YRows &y, int32_t *sync,
-                                   int32_t *status,
-                                   hipStream_t st);
+struct PersistentBufs {
+    int32_t *counts, *offsets, *row_route, *route_row, *status;
+    int32_t *hdr, *table, *ready;
+    uint8_t *h, *hs;
+};
+hipError_t launch_layer_persistent(const moe_shape &s, const int32_t *ids, const int32_t *valid,
+                                   const float *tw, const uint8_t *x, const uint8_t *xs,
+                                   const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
+                                   const uint8_t *w2s, const PersistentBufs &b, const YRows &y,
+                                   uint16_t *out, hipStream_t st);
+// zero the first `words` words of p (the persistent header of a workspace)
+hipError_t launch_zero_words(int32_t *p, int words, hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, const float *tw, const int32_t *route_row,
                           const uint16_t *y, uint16_t *out, hipStream_t st);
 hipError_t launch_combine_fp8(const moe_shape &s, const float *tw, const int32_t *route_row,

@@ -118,6 +118,13 @@ size_t moe_dispatch_workspace_size(const moe_shape *shape);
  * MX FP8 activations of moe_forward_bf16). */
 size_t moe_workspace_size(const moe_shape *shape);
 
+/* Zero the persistent layer's counters at the start of a moe_forward
+ * workspace (its first 4096 bytes; one small launch on `stream`): needed
+ * once before the first moe_forward_persistent call on a workspace whose
+ * memory was not zero-filled.  MOE_EWORKSPACE for a null, short or
+ * misaligned workspace. */
+int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
 /* Byte offset inside the moe_forward workspace of the dispatch's int32[4]
  * status array (see "status" above), which the forward entry points leave
  * there for the caller to read; -1 for a refused shape. */
@@ -261,22 +268,34 @@ int moe_forward(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_s
                 uint16_t *out_bf16, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The same layer with GEMM1 + SwiGLU + requant and GEMM2 in one persistent
- * launch ("MegaMoEV2 ...", Technical Details: the large-M path is a
- * persistent kernel that overlaps the stages): the row chunks are split over
- * one work queue per XCD, whose workgroups take tickets for every GEMM1 item
- * of the queue's chunks first, then every GEMM2 item; a GEMM2 item of a row
- * chunk waits until all GEMM1 items of that chunk are done, and h passes
- * between them through that XCD's L2.  Same arguments, workspace and result
- * as moe_forward (the output bits are identical); MOE_ENOTSUP for shapes it
+ * The same layer in one persistent launch ("MegaMoEV2 ...", Technical
+ * Details, large input: dispatch, GEMM1, GEMM2 and combine fused into one
+ * persistent kernel that overlaps the stages; skewed routing handled inside
+ * the kernel, with no host sync).  Every workgroup of the grid (the device's
+ * CUs times the kernel's occupancy, all resident at once) dispatches a slice
+ * of the route slots, meets the others at a grid barrier, takes GEMM1 and
+ * GEMM2 tickets from the work queue of the XCD it runs on (a GEMM2 item of a
+ * row chunk waits until every GEMM1 item of that chunk is done; h passes
+ * between them through that XCD's L2; tickets cover blocks of row chunks x
+ * weight tiles, so a large expert's weight tile serves several chunks in
+ * turn), and after a last barrier combines tokens.  Same arguments and
+ * result as moe_forward (identical output bits).
+ *
+ * The first 1024 int32 words (4096 bytes) of `workspace` hold
+ * the kernel's counters: they must be zero before the first persistent call
+ * on a workspace (moe_workspace_init, or a zero-filled allocation), and
+ * every call leaves them zero when it ends, also after a wait gave up; the
+ * four-launch entry points never touch them.  MOE_ENOTSUP for shapes it
  * does not cover (H or I below 512, or a tuned table giving GEMM1 and GEMM2
  * different row tiles) and on a device whose CU count is not that of 1, 2,
- * 4 or 8 MI355X XCDs.  Calls that overlap on one workspace
- * race, as for moe_forward.  Every wait of a GEMM2 item is bounded; one that
- * gives up counts in the workspace's status[2] (the int32[4] status
- * array at byte moe_workspace_status_offset(shape) of the workspace), and
- * the output is then not valid.  MOE_PERSISTENT_MAX_POLLS in the environment (read at
- * every launch) lowers the bound, which tests use to force the timeout.
+ * 4 or 8 MI355X XCDs.  The grid barriers need the whole grid resident: with
+ * other work occupying the device some workgroups may start late.  Every
+ * wait is bounded; one that gives up counts in status[2] of the workspace
+ * (moe_workspace_status_offset) and sends its workgroup to the end without
+ * touching memory it has not been handed, and the output is then not valid.
+ * MOE_PERSISTENT_MAX_POLLS in the environment (read at every launch) lowers
+ * the bound, which tests use to force the timeouts.  Calls that overlap on
+ * one workspace race.
  */
 int moe_forward_persistent(const moe_shape *shape, const uint8_t *x_fp8, const uint8_t *x_scale,
                            const int32_t *topk_ids, const float *topk_w, const uint8_t *w13,

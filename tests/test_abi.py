@@ -257,3 +257,13 @@ def test_y_format_resolution_and_fp8_step_refusals(lib):
         s = moe.MoeShape(**{**V4, "T": T, "H": 128})
         R = moe.moe_row_capacity(s)
         assert moe.moe_workspace_size(s) >= R * (2 * 128) and moe.moe_workspace_size(s) > 0
+
+
+def test_workspace_init_refusals(lib):
+    """moe_workspace_init refuses a null, short or misaligned workspace
+    before any launch."""
+    assert lib.moe_workspace_init(None, 1 << 20, None) == -3
+    assert lib.moe_workspace_init(ctypes.c_void_p(256), 4095, None) == -3
+    assert lib.moe_workspace_init(ctypes.c_void_p(256 + 16), 1 << 20, None) == -3
+    # the persistent counters come first in every workspace layout
+    assert moe.moe_workspace_status_offset(moe.MoeShape(**V4)) >= 4096

@@ -260,10 +260,10 @@ def test_short_contraction_path(T, H, I):
 
 @pytest.mark.parametrize("T,H,I", [(1200, 512, 512), (600, 640, 512)])
 def test_persistent_layer_small(T, H, I):
-    """moe_forward_persistent (GEMM1 and GEMM2 in one persistent launch,
+    """moe_forward_persistent (the whole layer in one persistent launch,
     128-row tiles) gives the bits of moe_forward, twice in a row on one
-    workspace (each call clears its ticket and ready counters), and the
-    layer matches the oracle on every token."""
+    workspace (each call leaves its counters zero), and the layer matches the
+    oracle on every token."""
     case = synth.make_case("tiny", T=T, H=H, I=I, seed=1300 + T + H)
     shape = shape_of(case["spec"])
     say("persistent small T H I", T, H, I)
@@ -279,10 +279,11 @@ def test_persistent_layer_small(T, H, I):
 
 
 def test_persistent_wait_timeout_is_reported():
-    """With the poll bound forced to zero every GEMM2 item of the persistent
-    layer gives up its wait at once: the kernels still finish and status[2]
-    of the workspace counts the timeouts; with the bound restored the count
-    is zero again and the bits are moe_forward's."""
+    """With the poll bound forced to zero every wait of the persistent layer
+    (its first grid barrier) gives up at once: the kernel still finishes,
+    status[2] of the workspace counts the timeouts and the counters are zero
+    again; with the bound restored the count is zero and the bits are
+    moe_forward's."""
     case = synth.make_case("tiny", T=1200, H=512, I=512, seed=1310)
     shape = shape_of(case["spec"])
     g = upload(case)
@@ -304,10 +305,11 @@ def test_persistent_wait_timeout_is_reported():
                                   "flash_t4096_compact", "v4_prefill_t65536_uniform",
                                   "v4_prefill_t65536_zipf", "v4_prefill_t65536_hot30"])
 def test_persistent_layer_full_size(name):
-    """The persistent layer on the full-size workloads (64-row tiles with two
-    K steps up to T=4096, 128-row tiles at 65,536 tokens, skewed routing
-    included): every output element equals moe_forward's (which the sampled
-    oracle checks cover) and no wait gave up."""
+    """The persistent layer on the full-size workloads (32- and 64-row tiles
+    with two K steps up to T=4096, 256-row tiles on eight wavefronts at 65,536
+    tokens, skewed routing included): every output element equals
+    moe_forward's (which the sampled oracle checks cover) and no wait gave
+    up."""
     case = cached_case(name)
     shape = shape_of(case["spec"])
     say("persistent", name)
