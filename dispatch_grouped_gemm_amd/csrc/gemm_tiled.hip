@@ -654,6 +654,7 @@ constexpr int kHdrDropped = 352;   // fixed-slot routes past capacity
 constexpr int kHdrTimeouts = 384;  // waits that gave up
 constexpr int kHdrClaims = 512;    // fixed-slot claim counter of each local expert
 constexpr int kMaxSlices = 256;    // compact histogram table rows
+constexpr int kSliceSlots = 2048;  // fewest route slots per dispatch slice
 static_assert(kHdrClaims + kMaxLocalExperts <= kPersistentHeaderWords, "header size");
 
 struct FusedArgs {
@@ -808,7 +809,7 @@ __device__ __forceinline__ void combine_row_part(const Shape &s, const FusedArgs
 template <bool kFP8>
 __device__ __forceinline__ void combine_phase(const Shape &s, const FusedArgs &a)
 {
-    constexpr int U = 4;
+    constexpr int U = kFP8 ? 4 : 8;   // 64 float32 sums per lane either way
     const int V = kFP8 ? kCombine8Vec : kCombineVec;
     const int NTH = blockDim.x, NW = NTH / 64;
     const int pieces = s.H / V;
@@ -865,7 +866,10 @@ layer_persistent_kernel(Shape s, FusedArgs a, int nq, int max_polls)
                   "dispatch tables fit the stage ring");
     const long n = (long)s.T * s.K;
     const long nv = valid_slots(s, a.valid);
-    const int nsl = G < kMaxSlices ? G : kMaxSlices;
+    // slices of at least kSliceSlots slots (the table every workgroup sums
+    // then has few rows), at most one per workgroup and kMaxSlices
+    const long want = (n + kSliceSlots - 1) / kSliceSlots;
+    const int nsl = (int)min((long)min(G, kMaxSlices), want > 0 ? want : 1L);
     const long per = (n + nsl - 1) / nsl;
     const long sb = blk < nsl ? min(n, per * blk) : n, se = blk < nsl ? min(n, sb + per) : n;
     const long pw = (se - sb + NW - 1) / NW;
@@ -915,6 +919,7 @@ layer_persistent_kernel(Shape s, FusedArgs a, int nq, int max_polls)
             // (segment sizes) and over the slices before this one
             for (int c = lane; c < E; c += 64) {
                 int before = 0, all = 0;
+#pragma unroll 8
                 for (int b = wave; b < nsl; b += NW) {
                     const int v = a.table[(size_t)b * E1 + c];
                     all += v;
