@@ -67,8 +67,11 @@ def parse():
                    help="time moe_forward_bf16: the layer from bf16 activation rows, their "
                         "MX FP8 quant included in the step")
     p.add_argument("--persistent", action="store_true",
-                   help="time moe_forward_persistent (GEMM1 and GEMM2 in one persistent "
-                        "launch; 128-row tile sizes only)")
+                   help="time moe_forward_persistent (the whole layer in one persistent "
+                        "launch)")
+    p.add_argument("--y-format", choices=["bf16", "fp8", "auto"], default="bf16",
+                   help="expert output rows between GEMM2 and the combine: bf16 (the exact "
+                        "layer, default), MX FP8 (a lossy option), or the size rule")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the layer, time a plain device copy of this many MiB "
                         "(the reference size for the HBM byte counters)")
@@ -177,11 +180,17 @@ def main():
     ws = moe.alloc_workspace(shape, dev)
     out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=dev)
 
-    if args.bf16_input and args.persistent:
-        print("--bf16-input and --persistent are separate entry points", file=sys.stderr)
-        sys.exit(2)
+    y_format = {"bf16": moe.Y_BF16, "fp8": moe.Y_FP8, "auto": moe.Y_AUTO}[args.y_format]
+    y8 = moe.moe_resolve_y_format(shape, y_format) == moe.Y_FP8
 
     def forward(stream=None):
+        if y_format != moe.Y_BF16 or (args.bf16_input and args.persistent):
+            xa = (dict(x_bf16=g["x_bf16"]) if args.bf16_input
+                  else dict(x_fp8=g["x_fp8"], x_scale=g["x_scale"]))
+            moe.moe_forward_ex(shape, g["topk_ids"], g["topk_w"], g["w13"], g["w13_scale"],
+                               g["w2"], g["w2_scale"], out, ws, persistent=args.persistent,
+                               y_format=y_format, stream=stream, **xa)
+            return
         if args.bf16_input:
             moe.moe_forward_bf16(shape, g["x_bf16"], g["topk_ids"], g["topk_w"], g["w13"],
                                  g["w13_scale"], g["w2"], g["w2_scale"], out, ws, stream=stream)
@@ -232,6 +241,8 @@ def main():
     h = torch.empty((R, spec.I), dtype=torch.uint8, device=dev)
     hs = torch.empty((R, spec.I // 32), dtype=torch.uint8, device=dev)
     y = torch.empty((R, spec.H), dtype=torch.uint16, device=dev)
+    y8c = torch.empty((R, spec.H), dtype=torch.uint8, device=dev) if y8 else None
+    y8s = torch.empty((R, spec.H // 32), dtype=torch.uint8, device=dev) if y8 else None
     st = torch.cuda.current_stream()
     iters = args.kernel_iters or args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(iters)]
@@ -250,9 +261,15 @@ def main():
         moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"],
                              h, hs, stream=st)
         e[2].record(st)
-        moe.moe_gemm2(shape, h, hs, d, g["w2"], g["w2_scale"], y, stream=st)
+        if y8:
+            moe.moe_gemm2_fp8(shape, h, hs, d, g["w2"], g["w2_scale"], y8c, y8s, stream=st)
+        else:
+            moe.moe_gemm2(shape, h, hs, d, g["w2"], g["w2_scale"], y, stream=st)
         e[3].record(st)
-        moe.moe_combine(shape, g["topk_w"], d.route_row, y, out, stream=st)
+        if y8:
+            moe.moe_combine_fp8(shape, g["topk_w"], d.route_row, y8c, y8s, out, stream=st)
+        else:
+            moe.moe_combine(shape, g["topk_w"], d.route_row, y, out, stream=st)
         e[4].record(st)
     torch.cuda.synchronize()
     names = ["dispatch", "gemm1_swiglu", "gemm2", "combine"]
@@ -306,6 +323,7 @@ def main():
                    "capacity": spec.capacity, "routes": work["routes"],
                    "touched_experts": work["touched"],
                    "forward": "persistent" if args.persistent else "four launches",
+                   "y_rows": "MX FP8" if y8 else "bf16",
                    "input": "bf16 rows, quantised in the step" if args.bf16_input
                    else "MX FP8 rows"},
         "us_per_layer": round(us, 2),

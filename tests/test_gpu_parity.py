@@ -186,8 +186,10 @@ def test_gemm2_tiny_given_h():
     assert (np.abs(got - ref) <= sum_bound + half_step).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "v4_decode_t128_fixed"])
+@pytest.mark.parametrize("name", ["tiny", "v4_decode_t128_fixed", "flash_t4096_compact"])
 def test_combine_bit_exact_given_y(name):
+    """bf16 combine bit for bit against the oracle's on the same y rows: 512
+    columns (one piece per lane), 7168 and 5120 (two pieces per lane)."""
     spec, ids, w = synth.make_routing(name)
     shape = shape_of(spec)
     d = run_dispatch(spec, dev(ids))

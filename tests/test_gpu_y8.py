@@ -145,13 +145,15 @@ def _combine_rows(rng, spec, rr):
     return codes, scales
 
 
-@pytest.mark.parametrize("K,mode", [(6, 0), (8, 1)])
-def test_combine_fp8_bit_exact_given_rows(K, mode):
+@pytest.mark.parametrize("K,mode,H", [(6, 0, 512), (8, 1, 512), (6, 0, 1024), (7, 1, 7168)])
+def test_combine_fp8_bit_exact_given_rows(K, mode, H):
     """The FP8 combine against the oracle's on the same route_row (the
     oracle's dispatch) and the same MX FP8 rows: bit for bit, including
-    subnormal decodes (exponent byte 0) and large ones (246)."""
+    subnormal decodes (exponent byte 0) and large ones (246); rows of 512
+    columns take the one-piece kernel, rows of 1024 and 7168 the paired
+    one."""
     rng = np.random.default_rng(40 + K)
-    spec = synth.CaseSpec("comb8", T=300, H=512, I=256, E_total=12, E_local=9, expert_begin=2,
+    spec = synth.CaseSpec("comb8", T=300, H=H, I=256, E_total=12, E_local=9, expert_begin=2,
                           K=K, dispatch_mode=mode, capacity=200)
     ids = rng.integers(-1, spec.E_total + 2, size=(spec.T, K)).astype(np.int32)
     w = (rng.standard_normal((spec.T, K)) * 3).astype(np.float32)
@@ -168,7 +170,7 @@ def test_combine_fp8_bit_exact_given_rows(K, mode):
     ys = np.full((R, spec.H // 32), 127, np.uint8)
     yc[:codes.shape[0]], ys[:scales.shape[0]] = codes, scales
     out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
-    say("combine fp8 K", K, "mode", mode)
+    say("combine fp8 K", K, "mode", mode, "H", H)
     moe.moe_combine_fp8(shape_of(spec), dev(w), dev(rr.astype(np.int32)), dev(yc), dev(ys), out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(out), oracle.combine_fp8(spec, w, rr, yc, ys))
