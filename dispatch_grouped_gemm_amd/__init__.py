@@ -501,7 +501,10 @@ def moe_forward_bf16(shape: MoeShape, x_bf16, topk_ids, topk_w, w13, w13_scale, 
 
 def moe_forward(shape: MoeShape, x_fp8, x_scale, topk_ids, topk_w, w13, w13_scale, w2,
                 w2_scale, out_bf16, workspace, stream=None, persistent=False):
-    """The layer; persistent=True calls moe_forward_persistent."""
+    """The layer; persistent=True calls moe_forward_persistent (the layer in
+    one launch; its counters in the workspace's first 4 KiB must be zero
+    before the first such call on a workspace, as alloc_workspace leaves
+    them)."""
     dev = x_fp8.device
     T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
     bf = {torch.bfloat16, torch.uint16, torch.int16}

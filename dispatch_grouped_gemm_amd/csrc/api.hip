@@ -343,7 +343,8 @@ int moe_resolve_y_format(const moe_shape *s, int32_t y_format)
 
 namespace {
 
-// The layer; `persistent` runs GEMM1 and GEMM2 in one persistent launch.
+// The layer; `persistent` runs it as one persistent launch (dispatch, both
+// GEMMs and the combine).
 // With x_bf16 the activations arrive as bf16 rows and are quantised into the
 // workspace first (x and xs are then ignored).
 int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
