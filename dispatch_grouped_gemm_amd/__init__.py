@@ -6,9 +6,13 @@ streams.  There is no fallback: if the shared library is missing the import
 of any entry point raises.
 
 Entry points (same names as the C ABI):
-    moe_dispatch, moe_gemm1_swiglu, moe_gemm2, moe_combine, moe_forward,
-    moe_forward_persistent,
-    moe_workspace_size, moe_dispatch_workspace_size, moe_row_capacity,
+    moe_dispatch, moe_dispatch_valid, moe_gemm1_swiglu, moe_gemm2,
+    moe_gemm2_fp8, moe_combine, moe_combine_fp8, moe_quant_mxfp8,
+    moe_forward, moe_forward_persistent, moe_forward_bf16, moe_forward_ex,
+    moe_forward_static, moe_workspace_init, moe_workspace_size,
+    moe_workspace_status_offset, moe_dispatch_workspace_size,
+    moe_row_capacity, moe_resolve_y_format, moe_static_scratch_bytes,
+    moe_forward_static_need, moe_set_tile_table, moe_get_tile_config,
     moe_check_shape, moe_strerror
 """
 
