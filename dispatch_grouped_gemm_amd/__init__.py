@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     moe_workspace_status_offset, moe_dispatch_workspace_size,
     moe_row_capacity, moe_resolve_y_format, moe_static_scratch_bytes,
     moe_forward_static_need, moe_set_tile_table, moe_get_tile_config,
+    moe_pack_weights, moe_packed_codes_bytes, moe_packed_scales_bytes,
     moe_check_shape, moe_strerror
 """
 
@@ -33,7 +34,8 @@ __all__ = [
     "moe_gemm2", "moe_combine", "moe_gemm2_fp8", "moe_combine_fp8", "moe_resolve_y_format",
     "moe_forward", "moe_forward_persistent", "moe_forward_static",
     "moe_static_scratch_bytes", "moe_forward_static_need", "moe_strerror",
-    "DispatchBuffers",
+    "moe_pack_weights", "moe_packed_codes_bytes", "moe_packed_scales_bytes", "PackedWeights",
+    "pack_layer_weights", "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT", "Y_BF16", "Y_FP8", "Y_AUTO",
 ]
 
@@ -55,7 +57,8 @@ EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size"
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
             "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_forward_static",
             "moe_static_scratch_bytes", "moe_forward_static_need", "moe_set_tile_table",
-            "moe_get_tile_config", "moe_strerror"]
+            "moe_get_tile_config", "moe_pack_weights", "moe_packed_codes_bytes",
+            "moe_packed_scales_bytes", "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -79,7 +82,9 @@ class _CForwardArgs(ctypes.Structure):
                 ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w2_scale", ctypes.c_void_p), ("out_bf16", ctypes.c_void_p),
                 ("num_valid_tokens", ctypes.c_void_p), ("persistent", ctypes.c_int32),
-                ("y_format", ctypes.c_int32)]
+                ("y_format", ctypes.c_int32), ("w13_packed", ctypes.c_void_p),
+                ("w13_packed_scale", ctypes.c_void_p), ("w2_packed", ctypes.c_void_p),
+                ("w2_packed_scale", ctypes.c_void_p)]
 
 
 class TileEntry(ctypes.Structure):
@@ -180,6 +185,12 @@ def lib() -> ctypes.CDLL:
         h.moe_static_scratch_bytes.restype = ctypes.c_size_t
         h.moe_forward_static_need.argtypes = [S]
         h.moe_forward_static_need.restype = ctypes.c_size_t
+        h.moe_pack_weights.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                       P, P]
+        h.moe_pack_weights.restype = ctypes.c_int
+        for n in ("moe_packed_codes_bytes", "moe_packed_scales_bytes"):
+            getattr(h, n).argtypes = [ctypes.c_int32] * 3
+            getattr(h, n).restype = ctypes.c_size_t
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -558,12 +569,64 @@ def moe_forward_static_need(shape: MoeShape) -> int:
     return int(lib().moe_forward_static_need(ctypes.byref(c)))
 
 
+def moe_packed_codes_bytes(E: int, N: int, K: int) -> int:
+    """Bytes of moe_pack_weights' packed codes (0 for refused sizes)."""
+    return int(lib().moe_packed_codes_bytes(E, N, K))
+
+
+def moe_packed_scales_bytes(E: int, N: int, K: int) -> int:
+    """Bytes of moe_pack_weights' packed exponents (0 for refused sizes)."""
+    return int(lib().moe_packed_scales_bytes(E, N, K))
+
+
+def moe_pack_weights(w, w_scale, packed, packed_scale, stream=None) -> None:
+    """Pack w [E, N, K/2] (MXFP4 codes) and w_scale [E, N, K/32] into the
+    register-streaming GEMMs' order (packed and packed_scale: uint8 tensors
+    of moe_packed_codes_bytes / moe_packed_scales_bytes bytes)."""
+    dev = w.device
+    if w.dim() != 3 or w_scale.dim() != 3:
+        raise ValueError("w and w_scale must be [E, N, K/2] and [E, N, K/32]")
+    E, N, K = int(w.shape[0]), int(w.shape[1]), int(w.shape[2]) * 2
+    nc, ns = moe_packed_codes_bytes(E, N, K), moe_packed_scales_bytes(E, N, K)
+    if nc == 0:
+        raise ValueError("moe_pack_weights: unsupported sizes E=%d N=%d K=%d" % (E, N, K))
+    args = [_ptr(w, "w", (E, N, K // 2), _fp4(), dev),
+            _ptr(w_scale, "w_scale", (E, N, K // 32), _e8m0("w_scale"), dev)]
+    pc = _ptr(packed, "packed", (nc,), {torch.uint8}, dev)
+    ps = _ptr(packed_scale, "packed_scale", (ns,), {torch.uint8}, dev)
+    _check(lib().moe_pack_weights(args[0], args[1], E, N, K, pc, ps, _stream(stream, dev)),
+           "moe_pack_weights")
+
+
+@dataclass
+class PackedWeights:
+    """moe_pack_weights of a layer's W13 and W2 (codes and exponents)."""
+    w13: torch.Tensor
+    w13_scale: torch.Tensor
+    w2: torch.Tensor
+    w2_scale: torch.Tensor
+
+
+def pack_layer_weights(w13, w13_scale, w2, w2_scale, stream=None) -> PackedWeights:
+    """Allocate and fill the packed copies of both weight arrays."""
+    out = []
+    for w, ws in ((w13, w13_scale), (w2, w2_scale)):
+        E, N, K = int(w.shape[0]), int(w.shape[1]), int(w.shape[2]) * 2
+        pc = torch.empty(moe_packed_codes_bytes(E, N, K), dtype=torch.uint8, device=w.device)
+        ps = torch.empty(moe_packed_scales_bytes(E, N, K), dtype=torch.uint8, device=w.device)
+        moe_pack_weights(w, ws, pc, ps, stream=stream)
+        out += [pc, ps]
+    return PackedWeights(*out)
+
+
 def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out_bf16,
                    workspace, x_fp8=None, x_scale=None, x_bf16=None, num_valid_tokens=None,
-                   persistent=False, stream=None, y_format=Y_BF16):
+                   persistent=False, stream=None, y_format=Y_BF16,
+                   packed: Optional[PackedWeights] = None):
     """The layer with every option (one of x_fp8 + x_scale or x_bf16;
     num_valid_tokens an int32 tensor [1] on the device; y_format one of
-    Y_BF16, Y_FP8, Y_AUTO)."""
+    Y_BF16, Y_FP8, Y_AUTO; packed the layer's pack_layer_weights, which the
+    register-streaming GEMMs read where the shape takes them)."""
     dev = topk_ids.device
     T, H, I, K, E = shape.T, shape.H, shape.I, shape.K, shape.E_local
     bf = {torch.bfloat16, torch.uint16, torch.int16}
@@ -585,6 +648,14 @@ def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_sca
                                   dev)
     a.persistent = 1 if persistent else 0
     a.y_format = int(y_format)
+    if packed is not None:
+        for n, (N, KK) in (("w13", (2 * I, H)), ("w2", (H, I))):
+            nc, ns = moe_packed_codes_bytes(E, N, KK), moe_packed_scales_bytes(E, N, KK)
+            setattr(a, n + "_packed",
+                    _ptr(getattr(packed, n), n + "_packed", (nc,), {torch.uint8}, dev))
+            setattr(a, n + "_packed_scale",
+                    _ptr(getattr(packed, n + "_scale"), n + "_packed_scale", (ns,),
+                         {torch.uint8}, dev))
     ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
     c = shape.c()
     _check(lib().moe_forward_ex(ctypes.byref(c), ctypes.byref(a), ws, workspace.numel(),

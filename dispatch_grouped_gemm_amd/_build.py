@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_a8w4.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "dispatch.hip", "quant.hip", "gemm_skinny.hip", "gemm_tiled.hip",
-           "combine.hip"]
+           "gemm_stream.hip", "combine.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -347,12 +347,17 @@ namespace {
 // GEMMs and the combine).
 // With x_bf16 the activations arrive as bf16 rows and are quantised into the
 // workspace first (x and xs are then ignored).
+// Packed weights of the register-streaming GEMMs (either pair may be null).
+struct Packed {
+    const uint8_t *w13, *w13s, *w2, *w2s;
+};
+
 int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const int32_t *ids,
                  const float *tw, const uint8_t *w13, const uint8_t *w13s, const uint8_t *w2,
                  const uint8_t *w2s, uint16_t *out, void *ws, size_t ws_bytes, void *stream,
                  bool persistent, const uint16_t *x_bf16 = nullptr,
                  const int32_t *valid = nullptr, size_t need_bytes = 0,
-                 int32_t y_format = MOE_Y_BF16)
+                 int32_t y_format = MOE_Y_BF16, const Packed &pk = Packed{})
 {
     int rc = moe_check_shape(s);
     if (rc != MOE_OK)
@@ -381,6 +386,9 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
     if (!ws || ws_bytes < (need_bytes ? need_bytes : L.total) || ((uintptr_t)ws % kAlign) != 0)
         return MOE_EWORKSPACE;
     if (!all_aligned16(x, xs, w13, w13s, w2, w2s, out))
+        return MOE_EINVAL;
+    if ((!pk.w13 != !pk.w13s) || (!pk.w2 != !pk.w2s) ||
+        !all_aligned16(pk.w13, pk.w13s, pk.w2, pk.w2s))
         return MOE_EINVAL;
     const moe::QuantJob *qj = x_bf16 ? &quant : nullptr;
     int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
@@ -417,9 +425,14 @@ int forward_impl(const moe_shape *s, const uint8_t *x, const uint8_t *xs, const 
     hipError_t e = moe::launch_dispatch(*s, ids, counts, offsets, row_route, route_row, status,
                                         scratch, st, nullptr, 0, qj, valid);
     if (e == hipSuccess)
-        e = moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
+        e = pk.w13 && moe::use_stream_gemm(*s, true)
+                ? moe::launch_gemm1_stream(*s, x, xs, counts, offsets, row_route, pk.w13,
+                                           pk.w13s, h, hs, st)
+                : moe::launch_gemm1(*s, x, xs, counts, offsets, row_route, w13, w13s, h, hs, st);
     if (e == hipSuccess)
-        e = moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
+        e = pk.w2 && moe::use_stream_gemm(*s, false)
+                ? moe::launch_gemm2_stream(*s, h, hs, counts, offsets, pk.w2, pk.w2s, y, st)
+                : moe::launch_gemm2(*s, h, hs, counts, offsets, w2, w2s, y, st);
     if (e == hipSuccess)
         e = y.bf16 ? moe::launch_combine(*s, tw, route_row, y.bf16, out, st)
                    : moe::launch_combine_fp8(*s, tw, route_row, y.codes, y.scales, out, st);
@@ -499,7 +512,35 @@ int moe_forward_ex(const moe_shape *s, const moe_forward_args *a, void *ws, size
         return s->T == 0 ? MOE_OK : MOE_EINVAL;
     return forward_impl(s, a->x_fp8, a->x_scale, a->topk_ids, a->topk_w, a->w13, a->w13_scale,
                         a->w2, a->w2_scale, a->out_bf16, ws, ws_bytes, stream, a->persistent != 0,
-                        a->x_bf16, a->num_valid_tokens, 0, a->y_format);
+                        a->x_bf16, a->num_valid_tokens, 0, a->y_format,
+                        Packed{a->w13_packed, a->w13_packed_scale, a->w2_packed,
+                               a->w2_packed_scale});
+}
+
+static bool pack_dims_ok(int32_t E, int32_t N, int32_t K)
+{
+    return E >= 1 && N >= 64 && K >= 128 && N % 64 == 0 && K % 128 == 0 &&
+           (long double)E * N * (K / 2) < (long double)(1ll << 40);
+}
+
+size_t moe_packed_codes_bytes(int32_t E, int32_t N, int32_t K)
+{
+    return pack_dims_ok(E, N, K) ? moe::packed_codes_bytes(E, N, K) : 0;
+}
+
+size_t moe_packed_scales_bytes(int32_t E, int32_t N, int32_t K)
+{
+    return pack_dims_ok(E, N, K) ? moe::packed_scales_bytes(E, N, K) : 0;
+}
+
+int moe_pack_weights(const uint8_t *w, const uint8_t *w_scale, int32_t E, int32_t N, int32_t K,
+                     uint8_t *packed, uint8_t *packed_scale, void *stream)
+{
+    if (!pack_dims_ok(E, N, K) || !w || !w_scale || !packed || !packed_scale ||
+        !all_aligned16(w, w_scale, packed, packed_scale))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_pack(w, w_scale, packed, packed_scale, E, N, K,
+                                       as_stream(stream)));
 }
 
 int moe_set_tile_table(const moe_tile_entry *entries, int32_t n)

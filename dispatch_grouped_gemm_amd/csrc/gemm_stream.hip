@@ -1,0 +1,527 @@
+// Register-streaming expert GEMMs on packed weights, for the row tiles whose
+// GEMMs are bound by the weight stream (32 and 64 rows per chunk: decode and
+// the mid sizes).  ("full-expert DeepSeek V4.1 Flash MegaMoE tuning",
+// Changes and tuning: weight pipelining and the B cache policy are among the
+// searched knobs; the packed order is an internal layout, written once by
+// moe_pack_weights.)
+//
+// Packed layout of a weight matrix W [E, N, K/2] (FP4 codes) with exponents
+// Ws [E, N, K/32], N rows in groups of 16, K in steps of 128:
+//   codes  P[e][ks][g][lane][16 bytes] = W[e][16 g + (lane & 15)]
+//                                          [64 ks + 16 (lane >> 4) .. + 16]
+//   scales S[e][ks4][g][lane][j]       = Ws[e][16 g + (lane & 15)]
+//                                          [4 (4 ks4 + j) + (lane >> 4)]
+//          (j < 4; K steps past the last are zero bytes)
+// so one K step of a 16-row group is 1 KiB in the scaled MFMA's FP4 lane
+// order (lane l: row l mod 16, 32 K values 32 (l div 16) ..) and one dword
+// per lane holds its exponents of four K steps.  K-step major: the
+// wavefronts of a launch, which advance through K at about the same pace,
+// read one contiguous span of the weights at a time rather than thousands
+// of streams a fixed stride apart.
+//
+// A wavefront takes work items alone -- (row chunk, slice of the weight
+// rows): GEMM1 32 intermediate columns (the gate and up groups of them,
+// 64 W13 rows, so the requant's 32-column block stays in the wavefront),
+// GEMM2 64 output columns -- with no LDS and no barriers.  Its weight
+// fragments stream into registers four K steps ahead in 1 KiB contiguous
+// loads; its activation fragments (the gathered x rows, or h rows, read
+// through the L2) one K step ahead.  Every output element is the same
+// sequence of scaled MFMAs over ascending K steps as in the LDS-tiled
+// kernels, and the epilogues are theirs, so the bits are the same.
+#include <type_traits>
+
+#include "moe_common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+
+struct StreamArgs {
+    const uint8_t *act, *act_s;          // x (GEMM1, gathered) or h (GEMM2) rows
+    const int32_t *counts, *offsets, *row_route;
+    const uint8_t *wp, *wps;             // packed W13 or W2 codes and exponents
+    uint8_t *h_out, *hs_out;             // GEMM1 output
+    uint16_t *y_out;                     // GEMM2 output, bf16 rows, or
+    uint8_t *y8_out, *y8s_out;           // MX FP8 rows
+};
+
+// Buffer loads: a wavefront-uniform resource (base and byte range, in
+// SGPRs), a 32-bit lane offset and a uniform offset (an SGPR), so a lane
+// keeps one VGPR per address stream.  Bytes past the range read as zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRawBufferFlags = 0x00020000;   // raw bytes, 32-bit data format
+constexpr int kNonTemporal = 2;               // cache policy bit nt
+
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(uniform_ptr(base)), (short)0,
+                                             (int)bytes, kRawBufferFlags);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ u32x4s load16(Rsrc r, uint32_t voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, kAux);
+}
+
+// an activation fragment: bytes 0..15 and 64..79 of a K step
+__device__ __forceinline__ v8i load_frag(Rsrc r, uint32_t voff, int soff)
+{
+    const u32x4s lo = load16(r, voff, soff), hi = load16(r, voff + 64, soff);
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__device__ __forceinline__ uint32_t load4(Rsrc r, uint32_t voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, soff, 0);
+}
+
+// Scaled MFMA with the weight exponent taken from byte SEL of a dword that
+// holds four K steps' exponents (the instruction's scale byte select).
+template <int SEL>
+__device__ __forceinline__ v4f mfma_w4a8_sel(const v8i &a_fp4, const v8i &b_fp8, v4f c,
+                                             uint32_t sa4, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp8, c, 4, 0, SEL, (int)sa4,
+                                                            0, sb);
+}
+
+__device__ __forceinline__ u32x4s lds_read16(const uint8_t *p)
+{
+    return *reinterpret_cast<const u32x4s *>(p);
+}
+
+// LDS bytes of one activation stage: four K steps of NL 16-row blocks, each
+// block step two 1 KiB halves in the scaled MFMA's FP8 lane order
+// (lane (i16, kq): bytes 16 kq .. of the step (half 0) or 64 + 16 kq ..
+// (half 1) of block row i16).
+template <int NL>
+constexpr int kStageBytes = 4 * NL * 2 * 1024;
+
+// One work item of a workgroup: NL (1 .. TB) live 16-row blocks of the chunk
+// at rows row0 .. row0 + nrows - 1 of expert e; wavefront w takes slice
+// 4 sg + w (four weight groups).  Each K step's activation fragments are
+// fetched once per workgroup -- wavefront w loads step 4 q + w of stage q --
+// and shared through a two-stage LDS ring, one barrier per four K steps;
+// every wavefront streams its own weights into registers.
+template <bool kGemm1, int TB, int NL>
+__device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g, int e, int row0,
+                                            int nrows, int sg, uint8_t *lds)
+{
+    const int lane = threadIdx.x & 63, i16 = lane & 15, kq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = s.H, I = s.I;
+    const int KT = kGemm1 ? H : I;
+    const int KS = KT / 128, KS4 = (KS + 3) / 4;
+    const int N = kGemm1 ? 2 * I : H;
+    const int G = N / 16;
+    const int S = kGemm1 ? I / 32 : H / 64;
+    const int slice = 4 * sg + wave;
+    const bool live = slice < S;
+    const Rsrc null_r = make_rsrc(g.wp, 0);
+    // the wavefront's four 16-row weight groups: GEMM1 the gate groups of
+    // intermediate columns 32 slice .. + 31, then their up groups; GEMM2
+    // output columns 64 slice .. + 63.  Offsets within expert e's packed
+    // codes (K-step major: 1 KiB per group and K step, a K step's groups
+    // adjacent) and exponents (256 bytes per group and four K steps).  A
+    // slice past the last (the workgroup's last wavefronts where S is not a
+    // multiple of 4) reads zeros and stores nothing.
+    const Rsrc wr_r =
+        live ? make_rsrc(g.wp + (size_t)e * G * KS * 1024, (uint32_t)(G * KS * 1024)) : null_r;
+    const Rsrc ws_r =
+        live ? make_rsrc(g.wps + (size_t)e * G * KS4 * 256, (uint32_t)(G * KS4 * 256)) : null_r;
+    int wgo[4], sgo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int grp = kGemm1 ? (i < 2 ? 2 * slice + i : (I / 16) + 2 * slice + (i - 2))
+                               : 4 * slice + i;
+        wgo[i] = grp * 1024;
+        sgo[i] = grp * 256;
+    }
+    const uint32_t wl = 16 * lane, sl = 4 * lane;
+    // activation rows of the live blocks (rows past nrows repeat the last):
+    // GEMM1 gathered x rows (T H < 2^32), GEMM2 the chunk's h rows
+    const Rsrc act_r = kGemm1 ? make_rsrc(g.act, (uint32_t)s.T * (uint32_t)KT)
+                              : make_rsrc(g.act + (size_t)row0 * KT, (uint32_t)(nrows * KT));
+    const Rsrc acs_r = kGemm1 ? make_rsrc(g.act_s, (uint32_t)s.T * (uint32_t)(KT / 32))
+                              : make_rsrc(g.act_s + (size_t)row0 * (KT / 32),
+                                          (uint32_t)(nrows * (KT / 32)));
+    uint32_t ao[NL], aso[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int r = min(16 * j + i16, nrows - 1);
+        const uint32_t arow = kGemm1 ? (uint32_t)(g.row_route[row0 + r] / s.K) : (uint32_t)r;
+        ao[j] = arow * (uint32_t)KT + 16 * kq;
+        aso[j] = arow * (uint32_t)(KT / 32) + 4 * kq;
+    }
+
+    v4f acc[4][NL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // weight fragments of K steps ks .. ks + 3 (slot ks mod 4)
+    u32x4s wr[4][4];
+    uint32_t we[2][4];   // exponents of four K steps, double-buffered
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wr[d][i] = load16<kNonTemporal>(d < KS ? wr_r : null_r, wl, wgo[i] + d * G * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        we[0][i] = load4(ws_r, sl, sgo[i]);
+    // activation exponents four K steps to a dword: lane (i16, kq) holds the
+    // four block exponents of K step 4 q + kq of its row (stage q, buffer
+    // q mod 2), and a step takes its byte kq from lane i16 + 16 (ks mod 4)
+    uint32_t ax[2][NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+        ax[0][j] = load4(acs_r, aso[j], 0);
+
+    // this wavefront's share of stage q: K step 4 q + wave of every block,
+    // straight into the ring (LDS DMA: lane l's 16 bytes land at 16 l of a
+    // 1 KiB block).  A step past the last reloads the last (never read).
+    // These loads are inline assembly, out of the compiler's wait
+    // accounting: the waits for them are the explicit ones below, and the
+    // compiler's own waits for its loads, which do not count them, only
+    // wait longer than needed.
+    const uint8_t *act = kGemm1 ? g.act : g.act + (size_t)row0 * KT;
+    const uint32_t ring = lds_addr(lds) + wave * (NL * 2048);
+    auto stage_load = [&](int q) {
+        const uint8_t *base = act + (size_t)min(4 * q + wave, KS - 1) * 128;
+        const uint32_t m0 = ring + (q & 1) * kStageBytes<NL>;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            g2lds<16>(base, ao[j], m0 + j * 2048);
+            g2lds<16>(base + 64, ao[j], m0 + j * 2048 + 1024);
+        }
+    };
+    // vector memory operations a wavefront issues in a stage after its
+    // stage loads: the next exponents (4 weight dwords, NL activation
+    // dwords) and four K steps of weight fragments
+    constexpr int kAfterStage = 4 + NL + 16;
+    const int nq = (KS + 3) / 4;
+    // every wavefront is done with the previous item's ring (its reads are
+    // consumed; its own loads into the ring were waited for)
+    raw_barrier();
+    stage_load(0);
+
+    // K step ks = 4 q + D: its weight exponents are byte D of we[0].
+    // Prefetches past the last K step go to a null resource (no memory
+    // access, zeros), so every step issues the same loads and the buffers
+    // rotate without copies; steps past the last skip the MFMAs.
+    auto step = [&](int q, auto dc) {
+        constexpr int D = decltype(dc)::value;
+        const int ks = 4 * q + D;
+        if (ks < KS) {
+            const uint8_t *b = lds + (q & 1) * kStageBytes<NL> + D * (NL * 2048) + 16 * lane;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const u32x4s lo = lds_read16(b + j * 2048), hi = lds_read16(b + j * 2048 + 1024);
+                const v8i bj = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const int sb =
+                    (int)((uint32_t)__shfl((int)ax[0][j], i16 + 16 * D) >> (8 * kq)) & 0xff;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8i a = v8i{(int)wr[D][i][0], (int)wr[D][i][1], (int)wr[D][i][2],
+                                      (int)wr[D][i][3], 0, 0, 0, 0};
+                    acc[i][j] = mfma_w4a8_sel<D>(a, bj, acc[i][j], we[0][i], sb);
+                }
+            }
+        }
+        // the scheduler would hoist the next loads into this slot above the
+        // MFMAs that read it (two live copies, then register moves that wait
+        // on the loads) or sink them to the end of the unrolled body (the
+        // next step waits on them at once): keep every step's loads in place
+        __builtin_amdgcn_sched_barrier(0);
+        // this slot's next weight fragments: K step ks + 4
+        {
+            const Rsrc r = ks + 4 < KS ? wr_r : null_r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wr[D][i] = load16<kNonTemporal>(r, wl, wgo[i] + (ks + 4) * G * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int q = 0; q < nq; ++q) {
+        // stage q is in the ring: this wavefront's loads of it are done
+        // (issued one stage ago, or in the prologue), and after the barrier
+        // every wavefront's; every wavefront is also done reading stage
+        // q - 1, whose buffer now takes q + 1
+        // (the compiler moves no memory operation across the empty asm, so
+        // exactly kAfterStage operations follow the stage loads here)
+        asm volatile("" ::: "memory");
+        if (q == 0)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<kAfterStage>();
+        raw_barrier();
+        if (q + 1 < nq)
+            stage_load(q + 1);
+        // the next four K steps' weight and activation exponents
+        {
+            const Rsrc r = 4 * q + 4 < KS ? ws_r : null_r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                we[1][i] = load4(r, sl, sgo[i] + (q + 1) * G * 256);
+            const Rsrc rs = 4 * q + 4 < KS ? acs_r : null_r;
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                ax[1][j] = load4(rs, aso[j], (4 * q + 4) * 4);
+        }
+        step(q, std::integral_constant<int, 0>{});
+        step(q, std::integral_constant<int, 1>{});
+        step(q, std::integral_constant<int, 2>{});
+        step(q, std::integral_constant<int, 3>{});
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            we[0][i] = we[1][i];
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            ax[0][j] = ax[1][j];
+    }
+    if (!live)
+        return;
+
+    // epilogue: lane holds rows 16 j + i16, columns 4 kq .. 4 kq + 3 of each
+    // of its four groups
+    if (kGemm1) {
+        const int c0 = 32 * slice;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            float hv[2][4];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    hv[cb][v] = swiglu_clamped(acc[cb][j][v], acc[cb + 2][j][v], s.gate_limit,
+                                               s.up_limit);
+            float amax = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    amax = fmaxf(amax, fabsf(hv[cb][v]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int E = mx8_block_exponent(amax);
+            const int m = 16 * j + i16;
+            if (m < nrows) {
+                uint8_t *hr = g.h_out + (size_t)(row0 + m) * I + c0 + 4 * kq;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    *reinterpret_cast<uint32_t *>(hr + 16 * cb) =
+                        mx8_pack4(hv[cb][0], hv[cb][1], hv[cb][2], hv[cb][3], E, amax);
+                if (kq == 0)
+                    g.hs_out[(size_t)(row0 + m) * (I / 32) + c0 / 32] = (uint8_t)(E + 127);
+            }
+        }
+    } else if (g.y8_out) {
+        const int n0 = 64 * slice;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int m = 16 * j + i16;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 2 * blk; i < 2 * blk + 2; ++i)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        amax = fmaxf(amax, fabsf(acc[i][j][v]));
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int E = mx8_block_exponent(amax);
+                if (m < nrows) {
+                    uint8_t *yr = g.y8_out + (size_t)(row0 + m) * H + n0 + 32 * blk + 4 * kq;
+#pragma unroll
+                    for (int i = 2 * blk; i < 2 * blk + 2; ++i)
+                        *reinterpret_cast<uint32_t *>(yr + 16 * (i - 2 * blk)) =
+                            mx8_pack4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3],
+                                      E, amax);
+                    if (kq == 0)
+                        g.y8s_out[(size_t)(row0 + m) * (H / 32) + (n0 + 32 * blk) / 32] =
+                            (uint8_t)(E + 127);
+                }
+            }
+        }
+    } else {
+        const int n0 = 64 * slice;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int m = 16 * j + i16;
+            if (m >= nrows)
+                continue;
+            uint16_t *yr = g.y_out + (size_t)(row0 + m) * H + n0 + 4 * kq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint2 *>(yr + 16 * i) =
+                    uint2{f32_to_bf16(acc[i][j][0]) | (f32_to_bf16(acc[i][j][1]) << 16),
+                          f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16)};
+        }
+    }
+}
+
+// Workgroup items: (row chunk q of BM rows, group of four slices)
+// chunk-major, so the workgroups of a round share a chunk's activation rows
+// in the L2.
+template <bool kGemm1, int BM>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_stream_kernel(Shape s, StreamArgs g)
+{
+    constexpr int TB = BM / 16;
+    __shared__ int prefix[kMaxLocalExperts + 1];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes<TB>];
+    const int nchunks = plan_chunks<kThreads>(s, g.counts, BM, prefix);
+    const int S = kGemm1 ? s.I / 32 : s.H / 64;
+    const int SG = (S + 3) / 4;
+    const long items = (long)nchunks * SG;
+    for (long item = blockIdx.x; item < items; item += gridDim.x) {
+        const int q = __builtin_amdgcn_readfirstlane((int)(item / SG));
+        const int sg = __builtin_amdgcn_readfirstlane((int)(item - (long)q * SG));
+        const int e = __builtin_amdgcn_readfirstlane(chunk_expert(prefix, s.E_local, q));
+        const int c = q - prefix[e];
+        const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e] + c * BM);
+        const int nrows =
+            __builtin_amdgcn_readfirstlane(min(BM, used_rows(s, g.counts[e]) - c * BM));
+        const int nl = (nrows + 15) >> 4;
+        if (nl >= TB)
+            stream_item<kGemm1, TB, TB>(s, g, e, row0, nrows, sg, ring);
+        else if (nl == 1)
+            stream_item<kGemm1, TB, 1>(s, g, e, row0, nrows, sg, ring);
+        else if constexpr (TB >= 4) {
+            if (nl == 2)
+                stream_item<kGemm1, TB, (TB >= 4 ? 2 : 1)>(s, g, e, row0, nrows, sg, ring);
+            else
+                stream_item<kGemm1, TB, (TB >= 4 ? 3 : 1)>(s, g, e, row0, nrows, sg, ring);
+        }
+    }
+}
+
+// Packing, one thread per (expert, group, K step, lane): 16 code bytes; and
+// per (expert, group, four K steps, lane): 4 exponent bytes.
+__global__ void __launch_bounds__(256)
+pack_codes_kernel(const uint8_t *__restrict__ w, uint8_t *__restrict__ p, int E, int N, int K)
+{
+    const int KS = K / 128, G = N / 16;
+    const long n = (long)E * KS * G * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const int lane = (int)(i & 63);
+        const long blk = i >> 6;   // (e * KS + ks) * G + g
+        const int gi = (int)(blk % G);
+        const long eks = blk / G;
+        const int ks = (int)(eks % KS);
+        const long e = eks / KS;
+        const long row = e * N + 16 * gi + (lane & 15);
+        *reinterpret_cast<uint4 *>(p + i * 16) = *reinterpret_cast<const uint4 *>(
+            w + row * (K / 2) + 64 * ks + 16 * (lane >> 4));
+    }
+}
+
+__global__ void __launch_bounds__(256)
+pack_scales_kernel(const uint8_t *__restrict__ ws, uint8_t *__restrict__ ps, int E, int N, int K)
+{
+    const int KS = K / 128, KS4 = (KS + 3) / 4, G = N / 16;
+    const long n = (long)E * KS4 * G * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const int lane = (int)(i & 63);
+        const long blk = i >> 6;   // (e * KS4 + ks4) * G + g
+        const int gi = (int)(blk % G);
+        const long eks = blk / G;
+        const int ks4 = (int)(eks % KS4);
+        const long e = eks / KS4;
+        const long row = e * N + 16 * gi + (lane & 15);
+        uint32_t v = 0;
+        for (int j = 0; j < 4; ++j) {
+            const int ks = 4 * ks4 + j;
+            if (ks < KS)
+                v |= (uint32_t)ws[row * (K / 32) + 4 * ks + (lane >> 4)] << (8 * j);
+        }
+        *reinterpret_cast<uint32_t *>(ps + i * 4) = v;
+    }
+}
+
+int stream_grid(const void *kernel)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return device_cu_count() * per_cu;
+}
+
+template <bool kGemm1>
+hipError_t launch_stream(const moe_shape &sh, const StreamArgs &g, int bm, hipStream_t st)
+{
+    if (bm == 32) {
+        auto k = gemm_stream_kernel<kGemm1, 32>;
+        k<<<stream_grid(reinterpret_cast<const void *>(k)), kThreads, 0, st>>>(to_dev(sh), g);
+    } else {
+        auto k = gemm_stream_kernel<kGemm1, 64>;
+        k<<<stream_grid(reinterpret_cast<const void *>(k)), kThreads, 0, st>>>(to_dev(sh), g);
+    }
+    return hipGetLastError();
+}
+
+} // namespace
+
+size_t packed_codes_bytes(int E, int N, int K) { return (size_t)E * N * (size_t)(K / 2); }
+
+size_t packed_scales_bytes(int E, int N, int K)
+{
+    const int KS4 = (K / 128 + 3) / 4;
+    return (size_t)E * (size_t)(N / 16) * KS4 * 256;
+}
+
+hipError_t launch_pack(const uint8_t *w, const uint8_t *ws, uint8_t *p, uint8_t *ps, int E,
+                       int N, int K, hipStream_t st)
+{
+    const long nc = (long)E * (N / 16) * (K / 128) * 64;
+    const long nsc = (long)E * (N / 16) * ((K / 128 + 3) / 4) * 64;
+    auto grid = [](long n) { return (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536); };
+    pack_codes_kernel<<<grid(nc), 256, 0, st>>>(w, p, E, N, K);
+    pack_scales_kernel<<<grid(nsc), 256, 0, st>>>(ws, ps, E, N, K);
+    return hipGetLastError();
+}
+
+bool use_stream_gemm(const moe_shape &s, bool gemm1)
+{
+    int bm = 0, bn = 0, ku = 0;
+    return tile_config_of(s, gemm1, &bm, &bn, &ku) && bm <= 64;
+}
+
+hipError_t launch_gemm1_stream(const moe_shape &sh, const uint8_t *x, const uint8_t *xs,
+                               const int32_t *counts, const int32_t *offsets,
+                               const int32_t *row_route, const uint8_t *w13p,
+                               const uint8_t *w13ps, uint8_t *h, uint8_t *hs, hipStream_t st)
+{
+    const StreamArgs g{x, xs, counts, offsets, row_route, w13p, w13ps, h, hs, nullptr, nullptr,
+                       nullptr};
+    int bm = 0, bn = 0, ku = 0;
+    tile_config_of(sh, true, &bm, &bn, &ku);
+    return launch_stream<true>(sh, g, bm, st);
+}
+
+hipError_t launch_gemm2_stream(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
+                               const int32_t *counts, const int32_t *offsets,
+                               const uint8_t *w2p, const uint8_t *w2ps, const YRows &y,
+                               hipStream_t st)
+{
+    const StreamArgs g{h, hs, counts, offsets, nullptr, w2p, w2ps, nullptr, nullptr, y.bf16,
+                       y.codes, y.scales};
+    int bm = 0, bn = 0, ku = 0;
+    tile_config_of(sh, false, &bm, &bn, &ku);
+    return launch_stream<false>(sh, g, bm, st);
+}
+
+} // namespace moe

@@ -71,78 +71,6 @@ __device__ __forceinline__ u32x4 lds_read16(const uint8_t *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(uint8_t *p)
-{
-    return (uint32_t)(uintptr_t)(lds_u8 *)p;
-}
-
-// global -> LDS without registers: lane l's SIZE bytes from base + voff land
-// at LDS address m0 + SIZE * l (m0 is wavefront-uniform).  Issued as inline
-// assembly so that the waits are exactly the ones this file writes: the
-// loads count in vmcnt like any vector memory load.  An LDS DMA reads m0 one
-// wait state after an SALU write of m0 at the earliest, hence the s_nop.
-// kStream marks data read once (non-temporal: the L2 evicts it first, so it
-// does not push out the activation rows that other tiles read again).
-// kL2 reads data that another CU of the same XCD wrote earlier in the same
-// launch: sc0 makes the load miss the CU's own L1, which may hold the line
-// from before the write, and take it from the XCD's L2, where the write is.
-// A pointer every lane holds the same value of, in scalar registers (the
-// LDS DMA loads take their base from an SGPR pair).
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
-{
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
-}
-
-template <int SIZE, bool kStream = false, bool kL2 = false>
-__device__ __forceinline__ void g2lds(const uint8_t *base, uint32_t voff, uint32_t m0)
-{
-    static_assert(SIZE == 16 || SIZE == 4, "dword and dwordx4 LDS DMA only");
-    static_assert(!(kStream && kL2), "one cache policy");
-    // both are wavefront-uniform by construction; readfirstlane tells the
-    // compiler so where its analysis cannot see it (it costs nothing when
-    // the values already sit in scalar registers)
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    base = uniform_ptr(base);
-    if (SIZE == 16 && kL2)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 sc0" ::"s"(m0),
-                     "v"(voff), "s"(base)
-                     : "memory", "m0");
-    else if (SIZE == 16 && kStream)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0),
-                     "v"(voff), "s"(base)
-                     : "memory", "m0");
-    else if (SIZE == 16)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
-                     "v"(voff), "s"(base)
-                     : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0),
-                     "v"(voff), "s"(base)
-                     : "memory", "m0");
-}
-
-// The workgroup barrier without the memory fence __syncthreads() adds (that
-// fence would wait for every outstanding load, prefetches included).
-__device__ __forceinline__ void raw_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Operands of one GEMM launch.
 struct TiledArgs {
     const uint8_t *act, *act_s;             // FP8 activation rows (x or h) and exponents

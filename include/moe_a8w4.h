@@ -354,7 +354,13 @@ int moe_forward_bf16(const moe_shape *shape, const uint16_t *x_bf16, const int32
  * refusals); y_format (see moe_resolve_y_format) sends the expert output
  * rows to the combine as bf16 (MOE_Y_BF16, the result of moe_forward) or as
  * MX FP8 (moe_gemm2_fp8 then moe_combine_fp8 in the workspace's y area; a
- * lossy mode).  Same workspace as moe_forward.
+ * lossy mode).  Same workspace as moe_forward.  w13_packed / w2_packed
+ * (with their scale arrays; each pair may be given alone, or NULL) are
+ * moe_pack_weights of w13 / w2: where the shape's GEMM takes a tile of 32
+ * or 64 rows (moe_get_tile_config) it then runs the register-streaming
+ * kernel on them, which gives the same output bits; elsewhere, and in the
+ * persistent launch, they are not read.  The plain arrays are still
+ * required.
  */
 typedef struct {
     const uint8_t *x_fp8;             /* [T, H] e4m3, or NULL */
@@ -370,10 +376,38 @@ typedef struct {
     const int32_t *num_valid_tokens;  /* device int32, or NULL */
     int32_t persistent;
     int32_t y_format;                 /* MOE_Y_BF16 (0), MOE_Y_FP8 or MOE_Y_AUTO */
+    const uint8_t *w13_packed;        /* moe_pack_weights(w13, N 2I, K H), or NULL */
+    const uint8_t *w13_packed_scale;
+    const uint8_t *w2_packed;         /* moe_pack_weights(w2, N H, K I), or NULL */
+    const uint8_t *w2_packed_scale;
 } moe_forward_args;
 
 int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * Weights packed for the register-streaming GEMMs ("full-expert DeepSeek
+ * V4.1 Flash MegaMoE tuning", Changes and tuning: weight pipelining and the
+ * B-matrix cache policy are among the knobs the pages search; this layout
+ * is this library's own).  A weight array w [E, N, K/2] of MXFP4 codes with
+ * exponents w_scale [E, N, K/32] (W13: N = 2I, K = H; W2: N = H, K = I) is
+ * rewritten so that each 16-row group's 128-value K step is 1 KiB in the
+ * scaled MFMA's operand order (lane l: row l mod 16, 16 code bytes from byte
+ * 64 ks + 16 (l div 16) of the row) and its exponents four K steps to a
+ * dword per lane:
+ *   packed       [E][K/128][N/16][64 lanes][16 bytes]
+ *   packed_scale [E][ceil(K/512)][N/16][64 lanes][4 bytes], byte j = the
+ *                exponent of K step 4 q + j (zero past the last step).
+ * One pass on `stream`, reading the inputs once; the caller owns every
+ * buffer (moe_packed_codes_bytes / moe_packed_scales_bytes bytes, 16-byte
+ * aligned).  MOE_EINVAL for E < 1, N not a multiple of 64, K not a multiple
+ * of 128, E N K / 2 of 2^40 bytes or more, a NULL or misaligned pointer.
+ * The packed copy is a second copy of the weights: pack once at load time.
+ */
+size_t moe_packed_codes_bytes(int32_t E, int32_t N, int32_t K);
+size_t moe_packed_scales_bytes(int32_t E, int32_t N, int32_t K);
+int moe_pack_weights(const uint8_t *w, const uint8_t *w_scale, int32_t E, int32_t N, int32_t K,
+                     uint8_t *packed, uint8_t *packed_scale, void *stream);
 
 /*
  * Tuned tile table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE
