@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--persistent", action="store_true",
                    help="time moe_forward_persistent (the whole layer in one persistent "
                         "launch)")
+    p.add_argument("--packed", action="store_true",
+                   help="pack W13 and W2 once with moe_pack_weights (before timing) and time "
+                        "moe_forward_ex on the packed copies: the packed-weight GEMMs where "
+                        "the tile rule takes 32- or 64-row tiles, the same bits")
     p.add_argument("--y-format", choices=["bf16", "fp8", "auto"], default="bf16",
                    help="expert output rows between GEMM2 and the combine: bf16 (the exact "
                         "layer, default), MX FP8 (a lossy option), or the size rule")
@@ -110,11 +114,12 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, packed: bool = False):
     """HBM bytes per launch of the dominant kernel, from the rocprofv3 counter
-    summary of this workload under profiles/, or None when there is none or
-    the kernel sources have changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", workload + ".md")
+    summary of this workload (with packed weights: <workload>_packed) under
+    profiles/, or None when there is none or the kernel sources have changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", workload + ("_packed" if packed else "") + ".md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -183,13 +188,20 @@ def main():
     y_format = {"bf16": moe.Y_BF16, "fp8": moe.Y_FP8, "auto": moe.Y_AUTO}[args.y_format]
     y8 = moe.moe_resolve_y_format(shape, y_format) == moe.Y_FP8
 
+    pk = None
+    if args.packed:
+        pk = moe.pack_layer_weights(g["w13"], g["w13_scale"], g["w2"], g["w2_scale"])
+        torch.cuda.synchronize()
+    packed_gemm = [pk is not None and moe.get_tile_config(shape, k) is not None
+                   and moe.get_tile_config(shape, k)["bm"] in (32, 64) for k in (1, 2)]
+
     def forward(stream=None):
-        if y_format != moe.Y_BF16 or (args.bf16_input and args.persistent):
+        if y_format != moe.Y_BF16 or (args.bf16_input and args.persistent) or pk is not None:
             xa = (dict(x_bf16=g["x_bf16"]) if args.bf16_input
                   else dict(x_fp8=g["x_fp8"], x_scale=g["x_scale"]))
             moe.moe_forward_ex(shape, g["topk_ids"], g["topk_w"], g["w13"], g["w13_scale"],
                                g["w2"], g["w2_scale"], out, ws, persistent=args.persistent,
-                               y_format=y_format, stream=stream, **xa)
+                               y_format=y_format, stream=stream, packed=pk, **xa)
             return
         if args.bf16_input:
             moe.moe_forward_bf16(shape, g["x_bf16"], g["topk_ids"], g["topk_w"], g["w13"],
@@ -258,10 +270,18 @@ def main():
         e[0].record(st)
         moe.moe_dispatch(shape, g["topk_ids"], d, stream=st)
         e[1].record(st)
-        moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"],
-                             h, hs, stream=st)
+        if packed_gemm[0]:
+            moe.moe_gemm1_swiglu_packed(shape, g["x_fp8"], g["x_scale"], d, pk, h, hs, stream=st)
+        else:
+            moe.moe_gemm1_swiglu(shape, g["x_fp8"], g["x_scale"], d, g["w13"], g["w13_scale"],
+                                 h, hs, stream=st)
         e[2].record(st)
-        if y8:
+        if packed_gemm[1]:
+            if y8:
+                moe.moe_gemm2_packed(shape, h, hs, d, pk, y_fp8=y8c, y_scale=y8s, stream=st)
+            else:
+                moe.moe_gemm2_packed(shape, h, hs, d, pk, y_bf16=y, stream=st)
+        elif y8:
             moe.moe_gemm2_fp8(shape, h, hs, d, g["w2"], g["w2_scale"], y8c, y8s, stream=st)
         else:
             moe.moe_gemm2(shape, h, hs, d, g["w2"], g["w2_scale"], y, stream=st)
@@ -300,7 +320,7 @@ def main():
         roof = {"bound": "hbm", "kernel": "gemm1_swiglu",
                 "achieved": round(g1_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(g1_bytes / g1_s / 1e9 / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = recorded_traffic(spec_name)
+    roof["traffic"] = recorded_traffic(spec_name, packed_gemm[0])
     roof["bytes_per_launch"] = int(g1_bytes)
     mfma_bound = roof["bound"] == "mfma"
     result = {
@@ -324,6 +344,10 @@ def main():
                    "touched_experts": work["touched"],
                    "forward": "persistent" if args.persistent else "four launches",
                    "y_rows": "MX FP8" if y8 else "bf16",
+                   "weights": ("packed (moe_pack_weights, once before timing); GEMMs on "
+                               "them: %s" % ",".join(n for n, k in zip(("1", "2"), packed_gemm)
+                                                     if k) or "none") if pk is not None
+                   else "as given",
                    "input": "bf16 rows, quantised in the step" if args.bf16_input
                    else "MX FP8 rows"},
         "us_per_layer": round(us, 2),

@@ -14,7 +14,7 @@ Entry points (same names as the C ABI):
     moe_row_capacity, moe_resolve_y_format, moe_static_scratch_bytes,
     moe_forward_static_need, moe_set_tile_table, moe_get_tile_config,
     moe_pack_weights, moe_packed_codes_bytes, moe_packed_scales_bytes,
-    moe_check_shape, moe_strerror
+    moe_gemm1_swiglu_packed, moe_gemm2_packed, moe_check_shape, moe_strerror
 """
 
 from __future__ import annotations
@@ -35,6 +35,7 @@ __all__ = [
     "moe_forward", "moe_forward_persistent", "moe_forward_static",
     "moe_static_scratch_bytes", "moe_forward_static_need", "moe_strerror",
     "moe_pack_weights", "moe_packed_codes_bytes", "moe_packed_scales_bytes", "PackedWeights",
+    "moe_gemm1_swiglu_packed", "moe_gemm2_packed",
     "pack_layer_weights", "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT", "Y_BF16", "Y_FP8", "Y_AUTO",
 ]
@@ -58,7 +59,8 @@ EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size"
             "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_forward_static",
             "moe_static_scratch_bytes", "moe_forward_static_need", "moe_set_tile_table",
             "moe_get_tile_config", "moe_pack_weights", "moe_packed_codes_bytes",
-            "moe_packed_scales_bytes", "moe_strerror"]
+            "moe_packed_scales_bytes", "moe_gemm1_swiglu_packed", "moe_gemm2_packed",
+            "moe_strerror"]
 
 
 class MoeError(RuntimeError):
@@ -191,6 +193,10 @@ def lib() -> ctypes.CDLL:
         for n in ("moe_packed_codes_bytes", "moe_packed_scales_bytes"):
             getattr(h, n).argtypes = [ctypes.c_int32] * 3
             getattr(h, n).restype = ctypes.c_size_t
+        h.moe_gemm1_swiglu_packed.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        h.moe_gemm1_swiglu_packed.restype = ctypes.c_int
+        h.moe_gemm2_packed.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        h.moe_gemm2_packed.restype = ctypes.c_int
         h.moe_strerror.argtypes = [ctypes.c_int]
         h.moe_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -457,6 +463,62 @@ def moe_gemm2_fp8(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers, w2, w2_sc
     _check(lib().moe_gemm2_fp8(ctypes.byref(c), *args, _stream(stream, dev)), "moe_gemm2_fp8")
 
 
+def _packed_ptrs(shape: MoeShape, packed: "PackedWeights", which: str, dev):
+    H, I, E = shape.H, shape.I, shape.E_local
+    N, K = (2 * I, H) if which == "w13" else (H, I)
+    nc, ns = moe_packed_codes_bytes(E, N, K), moe_packed_scales_bytes(E, N, K)
+    return [_ptr(getattr(packed, which), which + "_packed", (nc,), {torch.uint8}, dev),
+            _ptr(getattr(packed, which + "_scale"), which + "_packed_scale", (ns,),
+                 {torch.uint8}, dev)]
+
+
+def moe_gemm1_swiglu_packed(shape: MoeShape, x_fp8, x_scale, d: DispatchBuffers,
+                            packed: "PackedWeights", h_fp8, h_scale, stream=None):
+    """moe_gemm1_swiglu on the packed W13 of pack_layer_weights."""
+    dev = x_fp8.device
+    T, H, I, E = shape.T, shape.H, shape.I, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(x_fp8, "x_fp8", (T, H), _fp8(), dev),
+            _ptr(x_scale, "x_scale", (T, H // 32), _e8m0("x_scale"), dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            _ptr(d.row_route, "row_route", (R,), i32, dev),
+            *_packed_ptrs(shape, packed, "w13", dev),
+            _ptr(h_fp8, "h_fp8", (R, I), _fp8(), dev),
+            _ptr(h_scale, "h_scale", (R, I // 32), _e8m0("h_scale"), dev)]
+    c = shape.c()
+    _check(lib().moe_gemm1_swiglu_packed(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_gemm1_swiglu_packed")
+
+
+def moe_gemm2_packed(shape: MoeShape, h_fp8, h_scale, d: DispatchBuffers,
+                     packed: "PackedWeights", y_bf16=None, y_fp8=None, y_scale=None,
+                     stream=None):
+    """moe_gemm2 (y_bf16) or moe_gemm2_fp8 (y_fp8 + y_scale) on the packed
+    W2 of pack_layer_weights."""
+    dev = h_fp8.device
+    H, I, E = shape.H, shape.I, shape.E_local
+    R = max(moe_row_capacity(shape), 1)
+    i32 = {torch.int32}
+    args = [_ptr(h_fp8, "h_fp8", (R, I), _fp8(), dev),
+            _ptr(h_scale, "h_scale", (R, I // 32), _e8m0("h_scale"), dev),
+            _ptr(d.counts, "counts", (E,), i32, dev),
+            _ptr(d.offsets, "offsets", (E + 1,), i32, dev),
+            *_packed_ptrs(shape, packed, "w2", dev)]
+    if (y_bf16 is None) == (y_fp8 is None and y_scale is None):
+        raise ValueError("moe_gemm2_packed: give y_bf16, or y_fp8 and y_scale")
+    if y_bf16 is not None:
+        args += [_ptr(y_bf16, "y_bf16", (R, H), {torch.bfloat16, torch.uint16, torch.int16}, dev),
+                 None, None]
+    else:
+        args += [None, _ptr(y_fp8, "y_fp8", (R, H), _fp8(), dev),
+                 _ptr(y_scale, "y_scale", (R, H // 32), _e8m0("y_scale"), dev)]
+    c = shape.c()
+    _check(lib().moe_gemm2_packed(ctypes.byref(c), *args, _stream(stream, dev)),
+           "moe_gemm2_packed")
+
+
 def moe_combine_fp8(shape: MoeShape, topk_w, route_row, y_fp8, y_scale, out_bf16, stream=None):
     """The combine of MX FP8 rows (codes [R, H], exponent bytes [R, H/32])."""
     dev = topk_w.device
@@ -649,13 +711,8 @@ def moe_forward_ex(shape: MoeShape, topk_ids, topk_w, w13, w13_scale, w2, w2_sca
     a.persistent = 1 if persistent else 0
     a.y_format = int(y_format)
     if packed is not None:
-        for n, (N, KK) in (("w13", (2 * I, H)), ("w2", (H, I))):
-            nc, ns = moe_packed_codes_bytes(E, N, KK), moe_packed_scales_bytes(E, N, KK)
-            setattr(a, n + "_packed",
-                    _ptr(getattr(packed, n), n + "_packed", (nc,), {torch.uint8}, dev))
-            setattr(a, n + "_packed_scale",
-                    _ptr(getattr(packed, n + "_scale"), n + "_packed_scale", (ns,),
-                         {torch.uint8}, dev))
+        a.w13_packed, a.w13_packed_scale = _packed_ptrs(shape, packed, "w13", dev)
+        a.w2_packed, a.w2_packed_scale = _packed_ptrs(shape, packed, "w2", dev)
     ws = _ptr(workspace, "workspace", None, {torch.uint8}, dev)
     c = shape.c()
     _check(lib().moe_forward_ex(ctypes.byref(c), ctypes.byref(a), ws, workspace.numel(),

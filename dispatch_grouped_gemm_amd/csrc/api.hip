@@ -277,6 +277,50 @@ int moe_gemm2_fp8(const moe_shape *s, const uint8_t *h, const uint8_t *hs, const
                                         moe::YRows{nullptr, y_fp8, y_scale}, as_stream(stream)));
 }
 
+int moe_gemm1_swiglu_packed(const moe_shape *s, const uint8_t *x, const uint8_t *xs,
+                            const int32_t *counts, const int32_t *offsets,
+                            const int32_t *row_route, const uint8_t *w13p, const uint8_t *w13ps,
+                            uint8_t *h, uint8_t *hs, void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (!moe::use_stream_gemm(*s, true))
+        return MOE_ENOTSUP;
+    if (s->T == 0)
+        return MOE_OK;
+    if (!x || !xs || !counts || !offsets || !row_route || !w13p || !w13ps || !h || !hs)
+        return MOE_EINVAL;
+    if (!all_aligned16(x, xs, w13p, w13ps, h, hs))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_gemm1_stream(*s, x, xs, counts, offsets, row_route, w13p,
+                                               w13ps, h, hs, as_stream(stream)));
+}
+
+int moe_gemm2_packed(const moe_shape *s, const uint8_t *h, const uint8_t *hs,
+                     const int32_t *counts, const int32_t *offsets, const uint8_t *w2p,
+                     const uint8_t *w2ps, uint16_t *y_bf16, uint8_t *y_fp8, uint8_t *y_scale,
+                     void *stream)
+{
+    int rc = moe_check_shape(s);
+    if (rc != MOE_OK)
+        return rc;
+    if (!moe::use_stream_gemm(*s, false))
+        return MOE_ENOTSUP;
+    if (s->T == 0)
+        return MOE_OK;
+    // exactly one output form: bf16 rows, or MX FP8 codes with exponents
+    const bool fp8 = y_fp8 || y_scale;
+    if (!h || !hs || !counts || !offsets || !w2p || !w2ps || fp8 == (y_bf16 != nullptr) ||
+        (fp8 && (!y_fp8 || !y_scale)))
+        return MOE_EINVAL;
+    if (!all_aligned16(h, hs, w2p, w2ps, y_bf16, y_fp8))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_gemm2_stream(*s, h, hs, counts, offsets, w2p, w2ps,
+                                               moe::YRows{y_bf16, y_fp8, y_scale},
+                                               as_stream(stream)));
+}
+
 int moe_quant_mxfp8(const moe_shape *s, const uint16_t *x, uint8_t *xq, uint8_t *xqs,
                     void *stream)
 {

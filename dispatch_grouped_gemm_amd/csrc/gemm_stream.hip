@@ -1,6 +1,6 @@
-// Register-streaming expert GEMMs on packed weights, for the row tiles whose
-// GEMMs are bound by the weight stream (32 and 64 rows per chunk: decode and
-// the mid sizes).  ("full-expert DeepSeek V4.1 Flash MegaMoE tuning",
+// Packed-weight expert GEMMs, for the row tiles whose GEMMs are bound by the
+// weight stream (the 32- and 64-row tile classes: decode and the mid
+// sizes).  ("full-expert DeepSeek V4.1 Flash MegaMoE tuning",
 // Changes and tuning: weight pipelining and the B cache policy are among the
 // searched knobs; the packed order is an internal layout, written once by
 // moe_pack_weights.)
@@ -16,18 +16,21 @@
 // order (lane l: row l mod 16, 32 K values 32 (l div 16) ..) and one dword
 // per lane holds its exponents of four K steps.  K-step major: the
 // wavefronts of a launch, which advance through K at about the same pace,
-// read one contiguous span of the weights at a time rather than thousands
-// of streams a fixed stride apart.
+// read one contiguous span of the weights at a time.
 //
-// A wavefront takes work items alone -- (row chunk, slice of the weight
-// rows): GEMM1 32 intermediate columns (the gate and up groups of them,
-// 64 W13 rows, so the requant's 32-column block stays in the wavefront),
-// GEMM2 64 output columns -- with no LDS and no barriers.  Its weight
-// fragments stream into registers four K steps ahead in 1 KiB contiguous
-// loads; its activation fragments (the gathered x rows, or h rows, read
-// through the L2) one K step ahead.  Every output element is the same
-// sequence of scaled MFMAs over ascending K steps as in the LDS-tiled
-// kernels, and the epilogues are theirs, so the bits are the same.
+// A workgroup of four wavefronts takes an item (row chunk, four slices of
+// the weight rows); a wavefront's slice is GEMM1 32 intermediate columns
+// (their gate and up groups, 64 W13 rows, so the requant's 32-column block
+// stays in the wavefront) or GEMM2 64 output columns.  Each wavefront
+// streams its four weight groups into registers four K steps ahead with
+// 1 KiB buffer loads (no LDS for weights).  The activation fragments (the
+// gathered x rows, or h rows) of four K steps at a time go through a
+// two-stage LDS ring by LDS DMA, each K step fetched once per workgroup,
+// one barrier per four K steps: read by every wavefront from registers
+// instead, the activation reads quadruple the L1 traffic and the L1, not
+// HBM, becomes the bound.  Every output element is the same sequence of
+// scaled MFMAs over ascending K steps as in the LDS-tiled kernels, and the
+// epilogues are theirs, so the bits are the same.
 #include <type_traits>
 
 #include "moe_common.hpp"
@@ -37,6 +40,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kStreamBigRows = 96;
 
 typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
 
@@ -96,12 +100,12 @@ __device__ __forceinline__ u32x4s lds_read16(const uint8_t *p)
     return *reinterpret_cast<const u32x4s *>(p);
 }
 
-// LDS bytes of one activation stage: four K steps of NL 16-row blocks, each
+// LDS bytes of one activation stage: two K steps of NL 16-row blocks, each
 // block step two 1 KiB halves in the scaled MFMA's FP8 lane order
 // (lane (i16, kq): bytes 16 kq .. of the step (half 0) or 64 + 16 kq ..
 // (half 1) of block row i16).
 template <int NL>
-constexpr int kStageBytes = 4 * NL * 2 * 1024;
+constexpr int kStageBytes = 2 * NL * 2 * 1024;
 
 // One work item of a workgroup: NL (1 .. TB) live 16-row blocks of the chunk
 // at rows row0 .. row0 + nrows - 1 of expert e; wavefront w takes slice
@@ -186,33 +190,47 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     for (int j = 0; j < NL; ++j)
         ax[0][j] = load4(acs_r, aso[j], 0);
 
-    // this wavefront's share of stage q: K step 4 q + wave of every block,
-    // straight into the ring (LDS DMA: lane l's 16 bytes land at 16 l of a
-    // 1 KiB block).  A step past the last reloads the last (never read).
-    // These loads are inline assembly, out of the compiler's wait
-    // accounting: the waits for them are the explicit ones below, and the
-    // compiler's own waits for its loads, which do not count them, only
-    // wait longer than needed.
-    const uint8_t *act = kGemm1 ? g.act : g.act + (size_t)row0 * KT;
-    const uint32_t ring = lds_addr(lds) + wave * (NL * 2048);
-    auto stage_load = [&](int q) {
-        const uint8_t *base = act + (size_t)min(4 * q + wave, KS - 1) * 128;
-        const uint32_t m0 = ring + (q & 1) * kStageBytes<NL>;
+    // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
+    // 2 p + (wave & 1), half wave >> 1, of every block, straight into the
+    // ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
+    // step past the last reloads the last (never read).  These loads are
+    // inline assembly, out of the compiler's wait accounting: the waits for
+    // them are the explicit ones below, and the compiler's own waits for its
+    // loads, which do not count them, only wait longer than needed.
+    const uint8_t *act = (kGemm1 ? g.act : g.act + (size_t)row0 * KT) + 64 * (wave >> 1);
+    const uint32_t ring = lds_addr(lds) + (wave & 1) * (NL * 2048) + (wave >> 1) * 1024;
+    auto stage_load = [&](int p) {
+        const uint8_t *base = act + (size_t)min(2 * p + (wave & 1), KS - 1) * 128;
+        const uint32_t m0 = ring + (p & 1) * kStageBytes<NL>;
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
+        for (int j = 0; j < NL; ++j)
             g2lds<16>(base, ao[j], m0 + j * 2048);
-            g2lds<16>(base + 64, ao[j], m0 + j * 2048 + 1024);
-        }
     };
-    // vector memory operations a wavefront issues in a stage after its
-    // stage loads: the next exponents (4 weight dwords, NL activation
-    // dwords) and four K steps of weight fragments
-    constexpr int kAfterStage = 4 + NL + 16;
-    const int nq = (KS + 3) / 4;
+    const int np = (KS + 1) / 2, nq = (KS + 3) / 4;
     // every wavefront is done with the previous item's ring (its reads are
     // consumed; its own loads into the ring were waited for)
     raw_barrier();
     stage_load(0);
+
+    // Stage p is in the ring once this wavefront's loads of it are done
+    // (issued at the start of stage p - 1, or in the prologue) and, after
+    // the barrier, every wavefront's; every wavefront is then also done
+    // reading stage p - 1, whose buffer takes p + 1.  kAfter: the vector
+    // memory operations issued after the stage loads by then -- the
+    // exponents of the next four K steps (4 weight dwords, NL activation
+    // dwords) where stage p - 1 began a group of four K steps, and two K
+    // steps of weight fragments (8).  The empty asm keeps every memory
+    // operation on its side of the count.
+    auto stage_begin = [&](int p, auto after) {
+        asm volatile("" ::: "memory");
+        if (p == 0)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<decltype(after)::value>();
+        raw_barrier();
+        if (p + 1 < np)
+            stage_load(p + 1);
+    };
 
     // K step ks = 4 q + D: its weight exponents are byte D of we[0].
     // Prefetches past the last K step go to a null resource (no memory
@@ -222,7 +240,8 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         constexpr int D = decltype(dc)::value;
         const int ks = 4 * q + D;
         if (ks < KS) {
-            const uint8_t *b = lds + (q & 1) * kStageBytes<NL> + D * (NL * 2048) + 16 * lane;
+            const uint8_t *b =
+                lds + ((2 * q + D / 2) & 1) * kStageBytes<NL> + (D & 1) * (NL * 2048) + 16 * lane;
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
                 const u32x4s lo = lds_read16(b + j * 2048), hi = lds_read16(b + j * 2048 + 1024);
@@ -253,20 +272,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         __builtin_amdgcn_sched_barrier(0);
     };
     for (int q = 0; q < nq; ++q) {
-        // stage q is in the ring: this wavefront's loads of it are done
-        // (issued one stage ago, or in the prologue), and after the barrier
-        // every wavefront's; every wavefront is also done reading stage
-        // q - 1, whose buffer now takes q + 1
-        // (the compiler moves no memory operation across the empty asm, so
-        // exactly kAfterStage operations follow the stage loads here)
-        asm volatile("" ::: "memory");
-        if (q == 0)
-            wait_vmcnt<0>();
-        else
-            wait_vmcnt<kAfterStage>();
-        raw_barrier();
-        if (q + 1 < nq)
-            stage_load(q + 1);
+        stage_begin(2 * q, std::integral_constant<int, 8>{});
         // the next four K steps' weight and activation exponents
         {
             const Rsrc r = 4 * q + 4 < KS ? ws_r : null_r;
@@ -280,6 +286,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         }
         step(q, std::integral_constant<int, 0>{});
         step(q, std::integral_constant<int, 1>{});
+        stage_begin(2 * q + 1, std::integral_constant<int, 4 + NL + 8>{});
         step(q, std::integral_constant<int, 2>{});
         step(q, std::integral_constant<int, 3>{});
 #pragma unroll
@@ -371,12 +378,26 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     }
 }
 
+// The item code for NL live blocks, NL = nl (1 .. TB), each count its own
+// straight-line instance.
+template <bool kGemm1, int TB, int NL = 1>
+__device__ __forceinline__ void dispatch_nl(int nl, const Shape &s, const StreamArgs &g, int e,
+                                            int row0, int nrows, int sg, uint8_t *lds)
+{
+    if (nl == NL)
+        stream_item<kGemm1, TB, NL>(s, g, e, row0, nrows, sg, lds);
+    else if constexpr (NL < TB)
+        dispatch_nl<kGemm1, TB, NL + 1>(nl, s, g, e, row0, nrows, sg, lds);
+}
+
 // Workgroup items: (row chunk q of BM rows, group of four slices)
-// chunk-major, so the workgroups of a round share a chunk's activation rows
-// in the L2.
+// chunk-major.  Workgroup b runs on XCD b mod X (X XCDs, the grid a
+// multiple of X); XCD x takes the contiguous block x of the item list, so
+// the items of a chunk, which read the same activation rows, mostly share
+// one XCD's L2.
 template <bool kGemm1, int BM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_stream_kernel(Shape s, StreamArgs g)
+gemm_stream_kernel(Shape s, StreamArgs g, int X)
 {
     constexpr int TB = BM / 16;
     __shared__ int prefix[kMaxLocalExperts + 1];
@@ -385,7 +406,12 @@ gemm_stream_kernel(Shape s, StreamArgs g)
     const int S = kGemm1 ? s.I / 32 : s.H / 64;
     const int SG = (S + 3) / 4;
     const long items = (long)nchunks * SG;
-    for (long item = blockIdx.x; item < items; item += gridDim.x) {
+    const long per = (items + X - 1) / X;
+    const int xcd = blockIdx.x % X, nb = gridDim.x / X;
+    for (long t = blockIdx.x / X; t < per; t += nb) {
+        const long item = xcd * per + t;
+        if (item >= items)
+            break;
         const int q = __builtin_amdgcn_readfirstlane((int)(item / SG));
         const int sg = __builtin_amdgcn_readfirstlane((int)(item - (long)q * SG));
         const int e = __builtin_amdgcn_readfirstlane(chunk_expert(prefix, s.E_local, q));
@@ -393,17 +419,8 @@ gemm_stream_kernel(Shape s, StreamArgs g)
         const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e] + c * BM);
         const int nrows =
             __builtin_amdgcn_readfirstlane(min(BM, used_rows(s, g.counts[e]) - c * BM));
-        const int nl = (nrows + 15) >> 4;
-        if (nl >= TB)
-            stream_item<kGemm1, TB, TB>(s, g, e, row0, nrows, sg, ring);
-        else if (nl == 1)
-            stream_item<kGemm1, TB, 1>(s, g, e, row0, nrows, sg, ring);
-        else if constexpr (TB >= 4) {
-            if (nl == 2)
-                stream_item<kGemm1, TB, (TB >= 4 ? 2 : 1)>(s, g, e, row0, nrows, sg, ring);
-            else
-                stream_item<kGemm1, TB, (TB >= 4 ? 3 : 1)>(s, g, e, row0, nrows, sg, ring);
-        }
+        const int nl = min((nrows + 15) >> 4, TB);
+        dispatch_nl<kGemm1, TB>(nl, s, g, e, row0, nrows, sg, ring);
     }
 }
 
@@ -460,17 +477,40 @@ int stream_grid(const void *kernel)
     return device_cu_count() * per_cu;
 }
 
+// XCDs the grid spreads over round-robin: the MI355X has 32 CUs per XCD
+// (1 where the CU count says otherwise, or the grid is not a multiple).
+int stream_xcds(int grid)
+{
+    const int cus = device_cu_count();
+    const int x = cus % 32 == 0 ? cus / 32 : 1;
+    return x > 0 && grid % x == 0 ? x : 1;
+}
+
 template <bool kGemm1>
 hipError_t launch_stream(const moe_shape &sh, const StreamArgs &g, int bm, hipStream_t st)
 {
     if (bm == 32) {
         auto k = gemm_stream_kernel<kGemm1, 32>;
-        k<<<stream_grid(reinterpret_cast<const void *>(k)), kThreads, 0, st>>>(to_dev(sh), g);
+        const int grid = stream_grid(reinterpret_cast<const void *>(k));
+        k<<<grid, kThreads, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
     } else {
-        auto k = gemm_stream_kernel<kGemm1, 64>;
-        k<<<stream_grid(reinterpret_cast<const void *>(k)), kThreads, 0, st>>>(to_dev(sh), g);
+        auto k = gemm_stream_kernel<kGemm1, kStreamBigRows>;
+        const int grid = stream_grid(reinterpret_cast<const void *>(k));
+        k<<<grid, kThreads, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
     }
     return hipGetLastError();
+}
+
+// Chunk rows of the packed kernels: 32 where the tile rule takes 32-row
+// tiles, else kStreamBigRows.  A chunk costs MFMAs for its live 16-row
+// blocks only, so the taller chunk loses nothing where experts hold fewer
+// rows, and where they hold more than 64 (Flash: 64 expected) it keeps an
+// expert in one chunk, its weights read once.
+int stream_bm(const moe_shape &s, bool gemm1)
+{
+    int bm = 0, bn = 0, ku = 0;
+    tile_config_of(s, gemm1, &bm, &bn, &ku);
+    return bm == 32 ? 32 : kStreamBigRows;
 }
 
 } // namespace
@@ -507,9 +547,7 @@ hipError_t launch_gemm1_stream(const moe_shape &sh, const uint8_t *x, const uint
 {
     const StreamArgs g{x, xs, counts, offsets, row_route, w13p, w13ps, h, hs, nullptr, nullptr,
                        nullptr};
-    int bm = 0, bn = 0, ku = 0;
-    tile_config_of(sh, true, &bm, &bn, &ku);
-    return launch_stream<true>(sh, g, bm, st);
+    return launch_stream<true>(sh, g, stream_bm(sh, true), st);
 }
 
 hipError_t launch_gemm2_stream(const moe_shape &sh, const uint8_t *h, const uint8_t *hs,
@@ -519,9 +557,7 @@ hipError_t launch_gemm2_stream(const moe_shape &sh, const uint8_t *h, const uint
 {
     const StreamArgs g{h, hs, counts, offsets, nullptr, w2p, w2ps, nullptr, nullptr, y.bf16,
                        y.codes, y.scales};
-    int bm = 0, bn = 0, ku = 0;
-    tile_config_of(sh, false, &bm, &bn, &ku);
-    return launch_stream<false>(sh, g, bm, st);
+    return launch_stream<false>(sh, g, stream_bm(sh, false), st);
 }
 
 } // namespace moe

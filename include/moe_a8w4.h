@@ -357,8 +357,8 @@ int moe_forward_bf16(const moe_shape *shape, const uint16_t *x_bf16, const int32
  * lossy mode).  Same workspace as moe_forward.  w13_packed / w2_packed
  * (with their scale arrays; each pair may be given alone, or NULL) are
  * moe_pack_weights of w13 / w2: where the shape's GEMM takes a tile of 32
- * or 64 rows (moe_get_tile_config) it then runs the register-streaming
- * kernel on them, which gives the same output bits; elsewhere, and in the
+ * or 64 rows (moe_get_tile_config) it then runs the packed-weight kernel
+ * on them, which gives the same output bits; elsewhere, and in the
  * persistent launch, they are not read.  The plain arrays are still
  * required.
  */
@@ -386,7 +386,7 @@ int moe_forward_ex(const moe_shape *shape, const moe_forward_args *args, void *w
                    size_t workspace_bytes, void *stream);
 
 /*
- * Weights packed for the register-streaming GEMMs ("full-expert DeepSeek
+ * Weights packed for the packed-weight GEMMs ("full-expert DeepSeek
  * V4.1 Flash MegaMoE tuning", Changes and tuning: weight pipelining and the
  * B-matrix cache policy are among the knobs the pages search; this layout
  * is this library's own).  A weight array w [E, N, K/2] of MXFP4 codes with
@@ -408,6 +408,25 @@ size_t moe_packed_codes_bytes(int32_t E, int32_t N, int32_t K);
 size_t moe_packed_scales_bytes(int32_t E, int32_t N, int32_t K);
 int moe_pack_weights(const uint8_t *w, const uint8_t *w_scale, int32_t E, int32_t N, int32_t K,
                      uint8_t *packed, uint8_t *packed_scale, void *stream);
+
+/*
+ * moe_gemm1_swiglu and moe_gemm2 / moe_gemm2_fp8 on packed weights (the
+ * packed-weight kernels moe_forward_ex runs when given them): the same
+ * arguments and output bits, the weights replaced by moe_pack_weights of
+ * w13 (N 2I, K H) or w2 (N H, K I).  moe_gemm2_packed writes bf16 rows
+ * (y_bf16, with y_fp8 and y_scale NULL) or MX FP8 rows (y_fp8 and y_scale,
+ * with y_bf16 NULL).  MOE_ENOTSUP where the shape's GEMM takes no packed
+ * kernel (moe_get_tile_config gives other than 32 or 64 rows, or no tile).
+ */
+int moe_gemm1_swiglu_packed(const moe_shape *shape, const uint8_t *x_fp8,
+                            const uint8_t *x_scale, const int32_t *counts,
+                            const int32_t *offsets, const int32_t *row_route,
+                            const uint8_t *w13_packed, const uint8_t *w13_packed_scale,
+                            uint8_t *h_fp8, uint8_t *h_scale, void *stream);
+int moe_gemm2_packed(const moe_shape *shape, const uint8_t *h_fp8, const uint8_t *h_scale,
+                     const int32_t *counts, const int32_t *offsets, const uint8_t *w2_packed,
+                     const uint8_t *w2_packed_scale, uint16_t *y_bf16, uint8_t *y_fp8,
+                     uint8_t *y_scale, void *stream);
 
 /*
  * Tuned tile table ("[FlyDSL] Add full-expert DeepSeek V4.1 Flash MegaMoE

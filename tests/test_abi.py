@@ -267,3 +267,59 @@ def test_workspace_init_refusals(lib):
     assert lib.moe_workspace_init(ctypes.c_void_p(256 + 16), 1 << 20, None) == -3
     # the persistent counters come first in every workspace layout
     assert moe.moe_workspace_status_offset(moe.MoeShape(**V4)) >= 4096
+
+
+def test_pack_sizes_and_refusals(lib):
+    """Packed sizes follow the header's layout; moe_pack_weights and the
+    packed fields of moe_forward_ex refuse bad arguments before any launch."""
+    E, N, K = 48, 6144, 7168
+    assert moe.moe_packed_codes_bytes(E, N, K) == E * N * K // 2
+    assert moe.moe_packed_scales_bytes(E, N, K) == E * (N // 16) * 14 * 256   # 56 K steps
+    assert moe.moe_packed_scales_bytes(2, 64, 640) == 2 * 4 * 2 * 256        # 5 K steps
+    assert moe.moe_packed_scales_bytes(1, 64, 128) == 4 * 256
+    for dims in [(0, 64, 128), (-1, 64, 128), (1, 48, 128), (1, 64, 192), (1, 64, 64),
+                 (1, 0, 128), (1 << 20, 1 << 16, 1 << 16)]:
+        assert moe.moe_packed_codes_bytes(*dims) == 0, dims
+        assert moe.moe_packed_scales_bytes(*dims) == 0, dims
+    null = None
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 4)
+    assert lib.moe_pack_weights(fake, fake, 1, 48, 128, fake, fake, null) == -1
+    assert lib.moe_pack_weights(null, fake, 1, 64, 128, fake, fake, null) == -1
+    assert lib.moe_pack_weights(fake, fake, 1, 64, 128, fake, null, null) == -1
+    assert lib.moe_pack_weights(odd, fake, 1, 64, 128, fake, fake, null) == -1
+    assert lib.moe_pack_weights(fake, fake, 1, 64, 128, odd, fake, null) == -1
+    # a packed array without its exponents (or off a 16-byte boundary) is
+    # refused after the workspace check, before any launch
+    c = moe.MoeShape(**V4).c()
+    for w13p, w13ps, w2p, w2ps in [(256, None, None, None), (None, None, None, 256),
+                                   (256 + 4, 256, None, None), (256, 256, 256 + 8, 256)]:
+        a = moe._CForwardArgs()
+        a.x_fp8 = a.x_scale = a.topk_ids = a.topk_w = a.w13 = a.w13_scale = 256
+        a.w2 = a.w2_scale = a.out_bf16 = 256
+        a.w13_packed, a.w13_packed_scale, a.w2_packed, a.w2_packed_scale = w13p, w13ps, w2p, w2ps
+        assert lib.moe_forward_ex(ctypes.byref(c), ctypes.byref(a), fake, 1 << 40, null) == -1
+
+
+def test_packed_gemm_refusals(lib):
+    """The standalone packed GEMMs refuse shapes whose GEMM takes no packed
+    kernel, and bad buffers, before any launch."""
+    null = None
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 4)
+    dec = moe.MoeShape(**V4).c()                      # 32-row tiles: packed kernels
+    pre = moe.MoeShape(**{**V4, "T": 65536}).c()      # 256-row tiles
+    short = moe.MoeShape(**{**V4, "H": 256, "I": 256}).c()
+    for c in (pre, short):
+        assert lib.moe_gemm1_swiglu_packed(ctypes.byref(c), *([fake] * 9), null) == -2
+        assert lib.moe_gemm2_packed(ctypes.byref(c), *([fake] * 7), null, null, null) == -2
+    assert lib.moe_gemm1_swiglu_packed(ctypes.byref(dec), *([null] * 9), null) == -1
+    assert lib.moe_gemm1_swiglu_packed(ctypes.byref(dec), *([fake] * 5), odd, fake, fake, fake,
+                                       null) == -1
+    # exactly one output form
+    assert lib.moe_gemm2_packed(ctypes.byref(dec), *([fake] * 6), null, null, null, null) == -1
+    assert lib.moe_gemm2_packed(ctypes.byref(dec), *([fake] * 6), fake, fake, fake, null) == -1
+    assert lib.moe_gemm2_packed(ctypes.byref(dec), *([fake] * 6), null, fake, null, null) == -1
+    assert lib.moe_gemm2_packed(ctypes.byref(dec), *([fake] * 6), odd, null, null, null) == -1
+    z = moe.MoeShape(**{**V4, "T": 0}).c()
+    assert lib.moe_gemm1_swiglu_packed(ctypes.byref(z), *([null] * 9), null) == 0
