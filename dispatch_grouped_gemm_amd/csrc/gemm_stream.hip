@@ -152,16 +152,30 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     // GEMM1 gathered x rows (T H < 2^32), GEMM2 the chunk's h rows
     const Rsrc act_r = kGemm1 ? make_rsrc(g.act, (uint32_t)s.T * (uint32_t)KT)
                               : make_rsrc(g.act + (size_t)row0 * KT, (uint32_t)(nrows * KT));
-    const Rsrc acs_r = kGemm1 ? make_rsrc(g.act_s, (uint32_t)s.T * (uint32_t)(KT / 32))
-                              : make_rsrc(g.act_s + (size_t)row0 * (KT / 32),
-                                          (uint32_t)(nrows * (KT / 32)));
-    uint32_t ao[NL], aso[NL];
+    uint32_t ao[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
         const int r = min(16 * j + i16, nrows - 1);
         const uint32_t arow = kGemm1 ? (uint32_t)(g.row_route[row0 + r] / s.K) : (uint32_t)r;
         ao[j] = arow * (uint32_t)KT + 16 * kq;
-        aso[j] = arow * (uint32_t)(KT / 32) + 4 * kq;
+    }
+    // activation exponents, shared through LDS like the fragments: four K
+    // steps at a time, per block 64 dwords, lane (i16, kq)'s dword the four
+    // block exponents of K step 4 q + kq of its row; a step reads byte kq of
+    // lane i16 + 16 (ks mod 4)'s dword.  This wavefront loads blocks
+    // wave + 4 n (n < kAxLoads, clamped to the last block: a repeated block
+    // is the same bytes written twice).
+    constexpr int kAxLoads = (NL + 3) / 4;
+    uint32_t axrow[kAxLoads];
+    int axblk[kAxLoads];
+#pragma unroll
+    for (int n = 0; n < kAxLoads; ++n) {
+        axblk[n] = min(wave + 4 * n, NL - 1);
+        uint32_t v = ao[0];
+#pragma unroll
+        for (int j = 1; j < NL; ++j)
+            v = axblk[n] == j ? ao[j] : v;
+        axrow[n] = (v - 16 * kq) / 32;   // the row's first exponent byte
     }
 
     v4f acc[4][NL];
@@ -182,14 +196,6 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         we[0][i] = load4(ws_r, sl, sgo[i]);
-    // activation exponents four K steps to a dword: lane (i16, kq) holds the
-    // four block exponents of K step 4 q + kq of its row (stage q, buffer
-    // q mod 2), and a step takes its byte kq from lane i16 + 16 (ks mod 4)
-    uint32_t ax[2][NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-        ax[0][j] = load4(acs_r, aso[j], 0);
-
     // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
     // 2 p + (wave & 1), half wave >> 1, of every block, straight into the
     // ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
@@ -206,21 +212,39 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         for (int j = 0; j < NL; ++j)
             g2lds<16>(base, ao[j], m0 + j * 2048);
     };
+    // exponents of K steps 4 q .. 4 q + 3 into buffer q mod 2 (a step past
+    // the last reloads the last)
+    const uint8_t *act_s = kGemm1 ? g.act_s : g.act_s + (size_t)row0 * (KT / 32);
+    const uint8_t *ax_lds = lds + 2 * kStageBytes<TB>;
+    auto ax_load = [&](int q) {
+        const uint32_t voff = 4 * min(4 * q + kq, KS - 1);
+        const uint32_t m0 = lds_addr(const_cast<uint8_t *>(ax_lds)) + (q & 1) * (NL * 256);
+#pragma unroll
+        for (int n = 0; n < kAxLoads; ++n)
+            g2lds<4>(act_s, axrow[n] + voff, m0 + axblk[n] * 256);
+    };
     const int np = (KS + 1) / 2, nq = (KS + 3) / 4;
-    // every wavefront is done with the previous item's ring (its reads are
-    // consumed; its own loads into the ring were waited for)
+    // every wavefront is done with the previous item's ring: its reads are
+    // consumed, and its loads into the ring (the last group's exponent loads
+    // among them, which no wait of that item covers) are done before the
+    // barrier, so none lands in this item's ring
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
     raw_barrier();
     stage_load(0);
+    ax_load(0);
 
     // Stage p is in the ring once this wavefront's loads of it are done
     // (issued at the start of stage p - 1, or in the prologue) and, after
     // the barrier, every wavefront's; every wavefront is then also done
     // reading stage p - 1, whose buffer takes p + 1.  kAfter: the vector
     // memory operations issued after the stage loads by then -- the
-    // exponents of the next four K steps (4 weight dwords, NL activation
-    // dwords) where stage p - 1 began a group of four K steps, and two K
-    // steps of weight fragments (8).  The empty asm keeps every memory
-    // operation on its side of the count.
+    // exponents of the next four K steps (kAxLoads activation DMA dwords, 4
+    // weight dwords) where stage p - 1 began a group of four K steps, and
+    // two K steps of weight fragments (8).  The empty asm keeps every memory
+    // operation on its side of the count.  The activation exponents of a
+    // group, loaded at the start of the group before, are done by the wait
+    // of the group's first stage (loaded before that stage's fragments).
     auto stage_begin = [&](int p, auto after) {
         asm volatile("" ::: "memory");
         if (p == 0)
@@ -247,8 +271,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
                 const u32x4s lo = lds_read16(b + j * 2048), hi = lds_read16(b + j * 2048 + 1024);
                 const v8i bj = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                const int sb =
-                    (int)((uint32_t)__shfl((int)ax[0][j], i16 + 16 * D) >> (8 * kq)) & 0xff;
+                const int sb = ax_lds[(q & 1) * (NL * 256) + j * 256 + 4 * (i16 + 16 * D) + kq];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const v8i a = v8i{(int)wr[D][i][0], (int)wr[D][i][1], (int)wr[D][i][2],
@@ -273,28 +296,23 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     };
     for (int q = 0; q < nq; ++q) {
         stage_begin(2 * q, std::integral_constant<int, 8>{});
-        // the next four K steps' weight and activation exponents
+        // the next four K steps' activation and weight exponents (past the
+        // last group too: the wait counts assume these loads in every group)
+        ax_load(q + 1);
         {
             const Rsrc r = 4 * q + 4 < KS ? ws_r : null_r;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 we[1][i] = load4(r, sl, sgo[i] + (q + 1) * G * 256);
-            const Rsrc rs = 4 * q + 4 < KS ? acs_r : null_r;
-#pragma unroll
-            for (int j = 0; j < NL; ++j)
-                ax[1][j] = load4(rs, aso[j], (4 * q + 4) * 4);
         }
         step(q, std::integral_constant<int, 0>{});
         step(q, std::integral_constant<int, 1>{});
-        stage_begin(2 * q + 1, std::integral_constant<int, 4 + NL + 8>{});
+        stage_begin(2 * q + 1, std::integral_constant<int, kAxLoads + 4 + 8>{});
         step(q, std::integral_constant<int, 2>{});
         step(q, std::integral_constant<int, 3>{});
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             we[0][i] = we[1][i];
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-            ax[0][j] = ax[1][j];
     }
     if (!live)
         return;
@@ -401,7 +419,8 @@ gemm_stream_kernel(Shape s, StreamArgs g, int X)
 {
     constexpr int TB = BM / 16;
     __shared__ int prefix[kMaxLocalExperts + 1];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes<TB>];
+    // the fragment ring, then the activation exponents (two buffers)
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes<TB> + 2 * TB * 256];
     const int nchunks = plan_chunks<kThreads>(s, g.counts, BM, prefix);
     const int S = kGemm1 ? s.I / 32 : s.H / 64;
     const int SG = (S + 3) / 4;
