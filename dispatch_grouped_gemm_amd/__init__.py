@@ -13,7 +13,7 @@ Entry points (same names as the C ABI):
     moe_workspace_status_offset, moe_dispatch_workspace_size,
     moe_row_capacity, moe_resolve_y_format, moe_static_scratch_bytes,
     moe_forward_static_need, moe_set_tile_table, moe_get_tile_config,
-    moe_pack_weights, moe_packed_codes_bytes, moe_packed_scales_bytes,
+    moe_pack_weights, moe_unpack_weights, moe_packed_codes_bytes, moe_packed_scales_bytes,
     moe_gemm1_swiglu_packed, moe_gemm2_packed, moe_check_shape, moe_strerror
 """
 
@@ -34,7 +34,8 @@ __all__ = [
     "moe_gemm2", "moe_combine", "moe_gemm2_fp8", "moe_combine_fp8", "moe_resolve_y_format",
     "moe_forward", "moe_forward_persistent", "moe_forward_static",
     "moe_static_scratch_bytes", "moe_forward_static_need", "moe_strerror",
-    "moe_pack_weights", "moe_packed_codes_bytes", "moe_packed_scales_bytes", "PackedWeights",
+    "moe_pack_weights", "moe_unpack_weights", "moe_packed_codes_bytes",
+    "moe_packed_scales_bytes", "PackedWeights",
     "moe_gemm1_swiglu_packed", "moe_gemm2_packed",
     "pack_layer_weights", "DispatchBuffers",
     "alloc_dispatch", "alloc_workspace", "COMPACT", "FIXED_SLOT", "Y_BF16", "Y_FP8", "Y_AUTO",
@@ -58,7 +59,8 @@ EXPORTED = ["moe_check_shape", "moe_row_capacity", "moe_dispatch_workspace_size"
             "moe_combine", "moe_quant_mxfp8", "moe_forward", "moe_forward_persistent",
             "moe_forward_bf16", "moe_dispatch_valid", "moe_forward_ex", "moe_forward_static",
             "moe_static_scratch_bytes", "moe_forward_static_need", "moe_set_tile_table",
-            "moe_get_tile_config", "moe_pack_weights", "moe_packed_codes_bytes",
+            "moe_get_tile_config", "moe_pack_weights", "moe_unpack_weights",
+            "moe_packed_codes_bytes",
             "moe_packed_scales_bytes", "moe_gemm1_swiglu_packed", "moe_gemm2_packed",
             "moe_strerror"]
 
@@ -190,6 +192,8 @@ def lib() -> ctypes.CDLL:
         h.moe_pack_weights.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                        P, P]
         h.moe_pack_weights.restype = ctypes.c_int
+        h.moe_unpack_weights.argtypes = h.moe_pack_weights.argtypes
+        h.moe_unpack_weights.restype = ctypes.c_int
         for n in ("moe_packed_codes_bytes", "moe_packed_scales_bytes"):
             getattr(h, n).argtypes = [ctypes.c_int32] * 3
             getattr(h, n).restype = ctypes.c_size_t
@@ -658,6 +662,24 @@ def moe_pack_weights(w, w_scale, packed, packed_scale, stream=None) -> None:
     ps = _ptr(packed_scale, "packed_scale", (ns,), {torch.uint8}, dev)
     _check(lib().moe_pack_weights(args[0], args[1], E, N, K, pc, ps, _stream(stream, dev)),
            "moe_pack_weights")
+
+
+def moe_unpack_weights(packed, packed_scale, w, w_scale, stream=None) -> None:
+    """The inverse of moe_pack_weights: w [E, N, K/2] and w_scale [E, N, K/32]
+    (their shapes give E, N, K) from a packed pair."""
+    dev = w.device
+    if w.dim() != 3 or w_scale.dim() != 3:
+        raise ValueError("w and w_scale must be [E, N, K/2] and [E, N, K/32]")
+    E, N, K = int(w.shape[0]), int(w.shape[1]), int(w.shape[2]) * 2
+    nc, ns = moe_packed_codes_bytes(E, N, K), moe_packed_scales_bytes(E, N, K)
+    if nc == 0:
+        raise ValueError("moe_unpack_weights: unsupported sizes E=%d N=%d K=%d" % (E, N, K))
+    pc = _ptr(packed, "packed", (nc,), {torch.uint8}, dev)
+    ps = _ptr(packed_scale, "packed_scale", (ns,), {torch.uint8}, dev)
+    args = [_ptr(w, "w", (E, N, K // 2), _fp4(), dev),
+            _ptr(w_scale, "w_scale", (E, N, K // 32), _e8m0("w_scale"), dev)]
+    _check(lib().moe_unpack_weights(pc, ps, E, N, K, args[0], args[1], _stream(stream, dev)),
+           "moe_unpack_weights")
 
 
 @dataclass

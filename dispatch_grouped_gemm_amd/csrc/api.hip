@@ -587,6 +587,16 @@ int moe_pack_weights(const uint8_t *w, const uint8_t *w_scale, int32_t E, int32_
                                        as_stream(stream)));
 }
 
+int moe_unpack_weights(const uint8_t *packed, const uint8_t *packed_scale, int32_t E, int32_t N,
+                       int32_t K, uint8_t *w, uint8_t *w_scale, void *stream)
+{
+    if (!pack_dims_ok(E, N, K) || !w || !w_scale || !packed || !packed_scale ||
+        !all_aligned16(w, w_scale, packed, packed_scale))
+        return MOE_EINVAL;
+    return hip_status(moe::launch_unpack(packed, packed_scale, w, w_scale, E, N, K,
+                                         as_stream(stream)));
+}
+
 int moe_set_tile_table(const moe_tile_entry *entries, int32_t n)
 {
     return moe::set_tile_table(entries, n);

@@ -486,6 +486,48 @@ pack_scales_kernel(const uint8_t *__restrict__ ws, uint8_t *__restrict__ ps, int
     }
 }
 
+// The inverse of the two packing passes (moe_unpack_weights).
+__global__ void __launch_bounds__(256)
+unpack_codes_kernel(const uint8_t *__restrict__ p, uint8_t *__restrict__ w, int E, int N, int K)
+{
+    const int KS = K / 128, G = N / 16;
+    const long n = (long)E * KS * G * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const int lane = (int)(i & 63);
+        const long blk = i >> 6;   // (e * KS + ks) * G + g
+        const int gi = (int)(blk % G);
+        const long eks = blk / G;
+        const int ks = (int)(eks % KS);
+        const long e = eks / KS;
+        const long row = e * N + 16 * gi + (lane & 15);
+        *reinterpret_cast<uint4 *>(w + row * (K / 2) + 64 * ks + 16 * (lane >> 4)) =
+            *reinterpret_cast<const uint4 *>(p + i * 16);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+unpack_scales_kernel(const uint8_t *__restrict__ ps, uint8_t *__restrict__ ws, int E, int N,
+                     int K)
+{
+    const int KS = K / 128, KS4 = (KS + 3) / 4, G = N / 16;
+    const long n = (long)E * KS4 * G * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const int lane = (int)(i & 63);
+        const long blk = i >> 6;   // (e * KS4 + ks4) * G + g
+        const int gi = (int)(blk % G);
+        const long eks = blk / G;
+        const int ks4 = (int)(eks % KS4);
+        const long e = eks / KS4;
+        const long row = e * N + 16 * gi + (lane & 15);
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(ps + i * 4);
+        for (int j = 0; j < 4; ++j) {
+            const int ks = 4 * ks4 + j;
+            if (ks < KS)
+                ws[row * (K / 32) + 4 * ks + (lane >> 4)] = (uint8_t)(v >> (8 * j));
+        }
+    }
+}
+
 int stream_grid(const void *kernel)
 {
     int per_cu = 0;
@@ -550,6 +592,17 @@ hipError_t launch_pack(const uint8_t *w, const uint8_t *ws, uint8_t *p, uint8_t 
     auto grid = [](long n) { return (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536); };
     pack_codes_kernel<<<grid(nc), 256, 0, st>>>(w, p, E, N, K);
     pack_scales_kernel<<<grid(nsc), 256, 0, st>>>(ws, ps, E, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *p, const uint8_t *ps, uint8_t *w, uint8_t *ws, int E,
+                         int N, int K, hipStream_t st)
+{
+    const long nc = (long)E * (N / 16) * (K / 128) * 64;
+    const long nsc = (long)E * (N / 16) * ((K / 128 + 3) / 4) * 64;
+    auto grid = [](long n) { return (unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536); };
+    unpack_codes_kernel<<<grid(nc), 256, 0, st>>>(p, w, E, N, K);
+    unpack_scales_kernel<<<grid(nsc), 256, 0, st>>>(ps, ws, E, N, K);
     return hipGetLastError();
 }
 

@@ -530,6 +530,8 @@ size_t packed_codes_bytes(int E, int N, int K);
 size_t packed_scales_bytes(int E, int N, int K);
 hipError_t launch_pack(const uint8_t *w, const uint8_t *ws, uint8_t *p, uint8_t *ps, int E,
                        int N, int K, hipStream_t st);
+hipError_t launch_unpack(const uint8_t *p, const uint8_t *ps, uint8_t *w, uint8_t *ws, int E,
+                         int N, int K, hipStream_t st);
 bool use_stream_gemm(const moe_shape &s, bool gemm1);
 hipError_t launch_gemm1_stream(const moe_shape &s, const uint8_t *x, const uint8_t *xs,
                                const int32_t *counts, const int32_t *offsets,

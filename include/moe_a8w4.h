@@ -408,6 +408,11 @@ size_t moe_packed_codes_bytes(int32_t E, int32_t N, int32_t K);
 size_t moe_packed_scales_bytes(int32_t E, int32_t N, int32_t K);
 int moe_pack_weights(const uint8_t *w, const uint8_t *w_scale, int32_t E, int32_t N, int32_t K,
                      uint8_t *packed, uint8_t *packed_scale, void *stream);
+/* The inverse: the logical arrays back from a packed pair (exponent bytes
+ * past the last K step are ignored); the same sizes and refusals.  Packing
+ * then unpacking gives back every byte. */
+int moe_unpack_weights(const uint8_t *packed, const uint8_t *packed_scale, int32_t E, int32_t N,
+                       int32_t K, uint8_t *w, uint8_t *w_scale, void *stream);
 
 /*
  * moe_gemm1_swiglu and moe_gemm2 / moe_gemm2_fp8 on packed weights (the

@@ -289,6 +289,9 @@ def test_pack_sizes_and_refusals(lib):
     assert lib.moe_pack_weights(fake, fake, 1, 64, 128, fake, null, null) == -1
     assert lib.moe_pack_weights(odd, fake, 1, 64, 128, fake, fake, null) == -1
     assert lib.moe_pack_weights(fake, fake, 1, 64, 128, odd, fake, null) == -1
+    assert lib.moe_unpack_weights(fake, fake, 1, 48, 128, fake, fake, null) == -1
+    assert lib.moe_unpack_weights(fake, null, 1, 64, 128, fake, fake, null) == -1
+    assert lib.moe_unpack_weights(fake, fake, 1, 64, 128, odd, fake, null) == -1
     # a packed array without its exponents (or off a 16-byte boundary) is
     # refused after the workspace check, before any launch
     c = moe.MoeShape(**V4).c()

@@ -1,5 +1,6 @@
 """The packed-weight GEMMs: moe_pack_weights writes the layout the header
-defines (checked against that definition written out in numpy), and
+defines (checked against that definition written out in numpy, and
+moe_unpack_weights gives back every byte), and
 moe_forward_ex with the packed copies gives the same output bits as the
 LDS-tiled kernels on the same inputs -- every row-chunk height (32, and the
 96-row chunks that serve the 64-row tile class, with 1 to 6 live 16-row
@@ -55,6 +56,13 @@ def test_pack_layout(E, N, K):
     assert pc.numel() == c.size and ps.numel() == s.size
     np.testing.assert_array_equal(host(pc), c)
     np.testing.assert_array_equal(host(ps), s)
+    # pack -> unpack gives back every byte
+    w2 = torch.zeros((E, N, K // 2), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros((E, N, K // 32), dtype=torch.uint8, device=DEV)
+    moe.moe_unpack_weights(pc, ps, w2, ws2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(w2), w)
+    np.testing.assert_array_equal(host(ws2), ws)
 
 
 def _forward(case, g, packed, y_format=moe.Y_BF16, valid=None, x_bf16=None, ws=None):
