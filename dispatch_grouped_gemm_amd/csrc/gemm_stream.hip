@@ -24,13 +24,14 @@
 // stays in the wavefront) or GEMM2 64 output columns.  Each wavefront
 // streams its four weight groups into registers four K steps ahead with
 // 1 KiB buffer loads (no LDS for weights).  The activation fragments (the
-// gathered x rows, or h rows) of four K steps at a time go through a
-// two-stage LDS ring by LDS DMA, each K step fetched once per workgroup,
-// one barrier per four K steps: read by every wavefront from registers
-// instead, the activation reads quadruple the L1 traffic and the L1, not
-// HBM, becomes the bound.  Every output element is the same sequence of
-// scaled MFMAs over ascending K steps as in the LDS-tiled kernels, and the
-// epilogues are theirs, so the bits are the same.
+// gathered x rows, or h rows) go through a two-stage LDS ring by LDS DMA,
+// two K steps per stage, each K step fetched once per workgroup, one
+// barrier per stage; their exponents go through LDS too, four K steps at a
+// time.  Read by every wavefront into its own registers instead, the
+// activations quadruple the L1 traffic and the L1, not HBM, becomes the
+// bound.  Every output element is the same sequence of scaled MFMAs over
+// ascending K steps as in the LDS-tiled kernels, and the epilogues are
+// theirs, so the bits are the same.
 #include <type_traits>
 
 #include "moe_common.hpp"
@@ -72,14 +73,6 @@ __device__ __forceinline__ u32x4s load16(Rsrc r, uint32_t voff, int soff)
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, kAux);
 }
 
-// an activation fragment: bytes 0..15 and 64..79 of a K step
-__device__ __forceinline__ v8i load_frag(Rsrc r, uint32_t voff, int soff)
-{
-    const u32x4s lo = load16(r, voff, soff), hi = load16(r, voff + 64, soff);
-    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
 __device__ __forceinline__ uint32_t load4(Rsrc r, uint32_t voff, int soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, soff, 0);
@@ -110,9 +103,8 @@ constexpr int kStageBytes = 2 * NL * 2 * 1024;
 // One work item of a workgroup: NL (1 .. TB) live 16-row blocks of the chunk
 // at rows row0 .. row0 + nrows - 1 of expert e; wavefront w takes slice
 // 4 sg + w (four weight groups).  Each K step's activation fragments are
-// fetched once per workgroup -- wavefront w loads step 4 q + w of stage q --
-// and shared through a two-stage LDS ring, one barrier per four K steps;
-// every wavefront streams its own weights into registers.
+// fetched once per workgroup and shared through the LDS ring; every
+// wavefront streams its own weights into registers.
 template <bool kGemm1, int TB, int NL>
 __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g, int e, int row0,
                                             int nrows, int sg, uint8_t *lds)
@@ -150,8 +142,6 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     const uint32_t wl = 16 * lane, sl = 4 * lane;
     // activation rows of the live blocks (rows past nrows repeat the last):
     // GEMM1 gathered x rows (T H < 2^32), GEMM2 the chunk's h rows
-    const Rsrc act_r = kGemm1 ? make_rsrc(g.act, (uint32_t)s.T * (uint32_t)KT)
-                              : make_rsrc(g.act + (size_t)row0 * KT, (uint32_t)(nrows * KT));
     uint32_t ao[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
@@ -185,17 +175,10 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         for (int j = 0; j < NL; ++j)
             acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // weight fragments of K steps ks .. ks + 3 (slot ks mod 4)
+    // weight fragments of K steps ks .. ks + 3 (slot ks mod 4) and their
+    // exponents, four K steps to a dword, double-buffered
     u32x4s wr[4][4];
-    uint32_t we[2][4];   // exponents of four K steps, double-buffered
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wr[d][i] = load16<kNonTemporal>(d < KS ? wr_r : null_r, wl, wgo[i] + d * G * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        we[0][i] = load4(ws_r, sl, sgo[i]);
+    uint32_t we[2][4];
     // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
     // 2 p + (wave & 1), half wave >> 1, of every block, straight into the
     // ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
@@ -233,6 +216,17 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     raw_barrier();
     stage_load(0);
     ax_load(0);
+    // the first four K steps of weights, after the ring loads so that the
+    // first stage waits for those alone (kPrologue operations follow them)
+    constexpr int kPrologue = 16 + 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wr[d][i] = load16<kNonTemporal>(d < KS ? wr_r : null_r, wl, wgo[i] + d * G * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        we[0][i] = load4(ws_r, sl, sgo[i]);
 
     // Stage p is in the ring once this wavefront's loads of it are done
     // (issued at the start of stage p - 1, or in the prologue) and, after
@@ -248,7 +242,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     auto stage_begin = [&](int p, auto after) {
         asm volatile("" ::: "memory");
         if (p == 0)
-            wait_vmcnt<0>();
+            wait_vmcnt<kPrologue>();
         else
             wait_vmcnt<decltype(after)::value>();
         raw_barrier();
