@@ -140,6 +140,26 @@ def test_packed_ignored_outside_its_tiles():
     np.testing.assert_array_equal(host(_forward(case, g, pk)), host(_forward(case, g, None)))
 
 
+def test_packed_ignored_by_the_persistent_launch():
+    """persistent = 1 runs the single launch on the plain weights whether or
+    not packed copies come along: the same bits."""
+    case = synth.make_case("tiny", T=300, H=512, I=512, seed=3125)
+    spec = case["spec"]
+    shape = shape_of(spec)
+    g = upload(case)
+    pk = _pack(g)
+    outs = []
+    for p in (None, pk):
+        out = torch.zeros((spec.T, spec.H), dtype=torch.uint16, device=DEV)
+        ws = moe.alloc_workspace(shape, DEV)
+        moe.moe_forward_ex(shape, g["topk_ids"], g["topk_w"], g["w13"], g["w13_scale"],
+                           g["w2"], g["w2_scale"], out, ws, x_fp8=g["x_fp8"],
+                           x_scale=g["x_scale"], persistent=True, packed=p)
+        outs.append(host(out))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], host(_forward(case, g, pk)))
+
+
 def test_packed_layer_against_oracle_every_token():
     case = synth.make_case("tiny", T=300, H=512, I=640, seed=3130)
     g = upload(case)
