@@ -94,9 +94,7 @@ __device__ __forceinline__ u32x4s lds_read16(const uint8_t *p)
 }
 
 // LDS bytes of one activation stage: two K steps of NL 16-row blocks, each
-// block step two 1 KiB halves in the scaled MFMA's FP8 lane order
-// (lane (i16, kq): bytes 16 kq .. of the step (half 0) or 64 + 16 kq ..
-// (half 1) of block row i16).
+// block step 2 KiB (16 rows of 128 bytes, their 16-byte columns swizzled).
 template <int NL>
 constexpr int kStageBytes = 2 * NL * 2 * 1024;
 
@@ -140,15 +138,27 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         sgo[i] = grp * 256;
     }
     const uint32_t wl = 16 * lane, sl = 4 * lane;
-    // activation rows of the live blocks (rows past nrows repeat the last):
-    // GEMM1 gathered x rows (T H < 2^32), GEMM2 the chunk's h rows
+    // activation rows (rows past nrows repeat the last): GEMM1 gathered x
+    // rows (T H < 2^32), GEMM2 the chunk's h rows
+    auto arow_of = [&](int r) -> uint32_t {
+        r = min(r, nrows - 1);
+        return kGemm1 ? (uint32_t)(g.row_route[row0 + r] / s.K) : (uint32_t)r;
+    };
+    // A K step of a 16-row block sits in LDS as 16 rows of 128 bytes, row r's
+    // 16-byte column c at slot c ^ swz(r), swz(r) = (r >> 1) & 7 (the eight
+    // lanes of a fragment read that share a column hit distinct banks).  This
+    // wavefront fetches row octet wave >> 1 of every block: lane l the column
+    // stored at slot l & 7 of row 8 (wave >> 1) + (l >> 3), so an instruction
+    // reads eight whole 128-byte lines.
+    const int rl = 8 * (wave >> 1) + (lane >> 3);
+    const uint32_t col = 16 * ((lane & 7) ^ ((rl >> 1) & 7));
     uint32_t ao[NL];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const int r = min(16 * j + i16, nrows - 1);
-        const uint32_t arow = kGemm1 ? (uint32_t)(g.row_route[row0 + r] / s.K) : (uint32_t)r;
-        ao[j] = arow * (uint32_t)KT + 16 * kq;
-    }
+    for (int j = 0; j < NL; ++j)
+        ao[j] = arow_of(16 * j + rl) * (uint32_t)KT + col;
+    // the MFMA lane (i16, kq) reads columns kq and kq + 4 of row i16
+    const uint32_t frag_lo = 128 * i16 + 16 * (kq ^ ((i16 >> 1) & 7));
+    const uint32_t frag_hi = frag_lo ^ 64;
     // activation exponents, shared through LDS like the fragments: four K
     // steps at a time, per block 64 dwords, lane (i16, kq)'s dword the four
     // block exponents of K step 4 q + kq of its row; a step reads byte kq of
@@ -161,11 +171,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
 #pragma unroll
     for (int n = 0; n < kAxLoads; ++n) {
         axblk[n] = min(wave + 4 * n, NL - 1);
-        uint32_t v = ao[0];
-#pragma unroll
-        for (int j = 1; j < NL; ++j)
-            v = axblk[n] == j ? ao[j] : v;
-        axrow[n] = (v - 16 * kq) / 32;   // the row's first exponent byte
+        axrow[n] = arow_of(16 * axblk[n] + i16) * (uint32_t)(KT / 32);   // the row's first exponent byte
     }
 
     v4f acc[4][NL];
@@ -180,13 +186,13 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     u32x4s wr[4][4];
     uint32_t we[2][4];
     // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
-    // 2 p + (wave & 1), half wave >> 1, of every block, straight into the
-    // ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
+    // 2 p + (wave & 1), row octet wave >> 1, of every block, straight into
+    // the ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
     // step past the last reloads the last (never read).  These loads are
     // inline assembly, out of the compiler's wait accounting: the waits for
     // them are the explicit ones below, and the compiler's own waits for its
     // loads, which do not count them, only wait longer than needed.
-    const uint8_t *act = (kGemm1 ? g.act : g.act + (size_t)row0 * KT) + 64 * (wave >> 1);
+    const uint8_t *act = kGemm1 ? g.act : g.act + (size_t)row0 * KT;
     const uint32_t ring = lds_addr(lds) + (wave & 1) * (NL * 2048) + (wave >> 1) * 1024;
     auto stage_load = [&](int p) {
         const uint8_t *base = act + (size_t)min(2 * p + (wave & 1), KS - 1) * 128;
@@ -259,10 +265,11 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
         const int ks = 4 * q + D;
         if (ks < KS) {
             const uint8_t *b =
-                lds + ((2 * q + D / 2) & 1) * kStageBytes<NL> + (D & 1) * (NL * 2048) + 16 * lane;
+                lds + ((2 * q + D / 2) & 1) * kStageBytes<NL> + (D & 1) * (NL * 2048);
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
-                const u32x4s lo = lds_read16(b + j * 2048), hi = lds_read16(b + j * 2048 + 1024);
+                const u32x4s lo = lds_read16(b + j * 2048 + frag_lo),
+                             hi = lds_read16(b + j * 2048 + frag_hi);
                 const v8i bj = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 const int sb = ax_lds[(q & 1) * (NL * 256) + j * 256 + 4 * (i16 + 16 * D) + kq];
