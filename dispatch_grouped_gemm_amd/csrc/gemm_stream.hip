@@ -18,10 +18,11 @@
 // wavefronts of a launch, which advance through K at about the same pace,
 // read one contiguous span of the weights at a time.
 //
-// A workgroup of four wavefronts takes an item (row chunk, four slices of
-// the weight rows); a wavefront's slice is GEMM1 32 intermediate columns
-// (their gate and up groups, 64 W13 rows, so the requant's 32-column block
-// stays in the wavefront) or GEMM2 64 output columns.  Each wavefront
+// A workgroup of four or eight wavefronts takes an item (row chunk, one
+// slice of the weight rows per wavefront); a wavefront's slice is GEMM1 32
+// intermediate columns (their gate and up groups, 64 W13 rows, so the
+// requant's 32-column block stays in the wavefront) or GEMM2 64 output
+// columns.  Each wavefront
 // streams its four weight groups into registers four K steps ahead with
 // 1 KiB buffer loads (no LDS for weights).  The activation fragments (the
 // gathered x rows, or h rows) go through a two-stage LDS ring by LDS DMA,
@@ -40,8 +41,15 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kStreamBigRows = 96;
+// wavefronts per workgroup of the 96-row kernels (one workgroup per CU at
+// two wavefronts per SIMD with eight): GEMM2 shares each activation stage
+// among eight (half the activation fetches per weight byte: Flash 135 ->
+// 133 us, V4 at 2,048 tokens 110 -> 106 us); GEMM1 keeps two workgroups of
+// four per CU, whose items (two to three per workgroup) then overlap one
+// another's start (eight: V4 at 2,048 tokens 183 -> 203 us)
+template <bool kGemm1>
+constexpr int kStreamBigWaves = kGemm1 ? 4 : 8;
 
 typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
 
@@ -103,7 +111,7 @@ constexpr int kStageBytes = 2 * NL * 2 * 1024;
 // 4 sg + w (four weight groups).  Each K step's activation fragments are
 // fetched once per workgroup and shared through the LDS ring; every
 // wavefront streams its own weights into registers.
-template <bool kGemm1, int TB, int NL>
+template <bool kGemm1, int TB, int NL, int kW>
 __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g, int e, int row0,
                                             int nrows, int sg, uint8_t *lds)
 {
@@ -115,7 +123,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     const int N = kGemm1 ? 2 * I : H;
     const int G = N / 16;
     const int S = kGemm1 ? I / 32 : H / 64;
-    const int slice = 4 * sg + wave;
+    const int slice = kW * sg + wave;
     const bool live = slice < S;
     const Rsrc null_r = make_rsrc(g.wp, 0);
     // the wavefront's four 16-row weight groups: GEMM1 the gate groups of
@@ -147,15 +155,19 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     // A K step of a 16-row block sits in LDS as 16 rows of 128 bytes, row r's
     // 16-byte column c at slot c ^ swz(r), swz(r) = (r >> 1) & 7 (the eight
     // lanes of a fragment read that share a column hit distinct banks).  This
-    // wavefront fetches row octet wave >> 1 of every block: lane l the column
-    // stored at slot l & 7 of row 8 (wave >> 1) + (l >> 3), so an instruction
-    // reads eight whole 128-byte lines.
-    const int rl = 8 * (wave >> 1) + (lane >> 3);
+    // wavefront fetches row octet (wave >> 1) & 1 of its blocks (every block
+    // with four wavefronts; with eight, the blocks j = wave >> 2 mod 2): lane
+    // l the column stored at slot l & 7 of row 8 ((wave >> 1) & 1) + (l >> 3),
+    // so an instruction reads eight whole 128-byte lines.
+    constexpr int kBP = kW / 4;                   // block phases
+    constexpr int kOwn = (NL + kBP - 1) / kBP;    // blocks per wavefront, at most
+    const int bp = wave >> 2;
+    const int rl = 8 * ((wave >> 1) & 1) + (lane >> 3);
     const uint32_t col = 16 * ((lane & 7) ^ ((rl >> 1) & 7));
-    uint32_t ao[NL];
+    uint32_t ao[kOwn];
 #pragma unroll
-    for (int j = 0; j < NL; ++j)
-        ao[j] = arow_of(16 * j + rl) * (uint32_t)KT + col;
+    for (int m = 0; m < kOwn; ++m)
+        ao[m] = arow_of(16 * min(kBP * m + bp, NL - 1) + rl) * (uint32_t)KT + col;
     // the MFMA lane (i16, kq) reads columns kq and kq + 4 of row i16
     const uint32_t frag_lo = 128 * i16 + 16 * (kq ^ ((i16 >> 1) & 7));
     const uint32_t frag_hi = frag_lo ^ 64;
@@ -163,14 +175,14 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     // steps at a time, per block 64 dwords, lane (i16, kq)'s dword the four
     // block exponents of K step 4 q + kq of its row; a step reads byte kq of
     // lane i16 + 16 (ks mod 4)'s dword.  This wavefront loads blocks
-    // wave + 4 n (n < kAxLoads, clamped to the last block: a repeated block
+    // wave + kW n (n < kAxLoads, clamped to the last block: a repeated block
     // is the same bytes written twice).
-    constexpr int kAxLoads = (NL + 3) / 4;
+    constexpr int kAxLoads = (NL + kW - 1) / kW;
     uint32_t axrow[kAxLoads];
     int axblk[kAxLoads];
 #pragma unroll
     for (int n = 0; n < kAxLoads; ++n) {
-        axblk[n] = min(wave + 4 * n, NL - 1);
+        axblk[n] = min(wave + kW * n, NL - 1);
         axrow[n] = arow_of(16 * axblk[n] + i16) * (uint32_t)(KT / 32);   // the row's first exponent byte
     }
 
@@ -186,20 +198,23 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     u32x4s wr[4][4];
     uint32_t we[2][4];
     // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
-    // 2 p + (wave & 1), row octet wave >> 1, of every block, straight into
-    // the ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB block).  A
+    // 2 p + (wave & 1), row octet (wave >> 1) & 1, of its blocks, straight
+    // into the ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB
+    // block).  A
     // step past the last reloads the last (never read).  These loads are
     // inline assembly, out of the compiler's wait accounting: the waits for
     // them are the explicit ones below, and the compiler's own waits for its
     // loads, which do not count them, only wait longer than needed.
     const uint8_t *act = kGemm1 ? g.act : g.act + (size_t)row0 * KT;
-    const uint32_t ring = lds_addr(lds) + (wave & 1) * (NL * 2048) + (wave >> 1) * 1024;
+    const uint32_t ring = lds_addr(lds) + (wave & 1) * (NL * 2048) + ((wave >> 1) & 1) * 1024 +
+                          bp * 2048;
     auto stage_load = [&](int p) {
         const uint8_t *base = act + (size_t)min(2 * p + (wave & 1), KS - 1) * 128;
         const uint32_t m0 = ring + (p & 1) * kStageBytes<NL>;
 #pragma unroll
-        for (int j = 0; j < NL; ++j)
-            g2lds<16>(base, ao[j], m0 + j * 2048);
+        for (int m = 0; m < kOwn; ++m)
+            if (kBP * m + bp < NL)
+                g2lds<16>(base, ao[m], m0 + m * (kBP * 2048));
     };
     // exponents of K steps 4 q .. 4 q + 3 into buffer q mod 2 (a step past
     // the last reloads the last)
@@ -399,32 +414,32 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
 
 // The item code for NL live blocks, NL = nl (1 .. TB), each count its own
 // straight-line instance.
-template <bool kGemm1, int TB, int NL = 1>
+template <bool kGemm1, int TB, int kW, int NL = 1>
 __device__ __forceinline__ void dispatch_nl(int nl, const Shape &s, const StreamArgs &g, int e,
                                             int row0, int nrows, int sg, uint8_t *lds)
 {
     if (nl == NL)
-        stream_item<kGemm1, TB, NL>(s, g, e, row0, nrows, sg, lds);
+        stream_item<kGemm1, TB, NL, kW>(s, g, e, row0, nrows, sg, lds);
     else if constexpr (NL < TB)
-        dispatch_nl<kGemm1, TB, NL + 1>(nl, s, g, e, row0, nrows, sg, lds);
+        dispatch_nl<kGemm1, TB, kW, NL + 1>(nl, s, g, e, row0, nrows, sg, lds);
 }
 
-// Workgroup items: (row chunk q of BM rows, group of four slices)
+// Workgroup items: (row chunk q of BM rows, group of kW slices)
 // chunk-major.  Workgroup b runs on XCD b mod X (X XCDs, the grid a
 // multiple of X); XCD x takes the contiguous block x of the item list, so
 // the items of a chunk, which read the same activation rows, mostly share
 // one XCD's L2.
-template <bool kGemm1, int BM>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <bool kGemm1, int BM, int kW>
+__global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_stream_kernel(Shape s, StreamArgs g, int X)
 {
     constexpr int TB = BM / 16;
     __shared__ int prefix[kMaxLocalExperts + 1];
     // the fragment ring, then the activation exponents (two buffers)
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes<TB> + 2 * TB * 256];
-    const int nchunks = plan_chunks<kThreads>(s, g.counts, BM, prefix);
+    const int nchunks = plan_chunks<64 * kW>(s, g.counts, BM, prefix);
     const int S = kGemm1 ? s.I / 32 : s.H / 64;
-    const int SG = (S + 3) / 4;
+    const int SG = (S + kW - 1) / kW;
     const long items = (long)nchunks * SG;
     const long per = (items + X - 1) / X;
     const int xcd = blockIdx.x % X, nb = gridDim.x / X;
@@ -440,7 +455,7 @@ gemm_stream_kernel(Shape s, StreamArgs g, int X)
         const int nrows =
             __builtin_amdgcn_readfirstlane(min(BM, used_rows(s, g.counts[e]) - c * BM));
         const int nl = min((nrows + 15) >> 4, TB);
-        dispatch_nl<kGemm1, TB>(nl, s, g, e, row0, nrows, sg, ring);
+        dispatch_nl<kGemm1, TB, kW>(nl, s, g, e, row0, nrows, sg, ring);
     }
 }
 
@@ -529,10 +544,10 @@ unpack_scales_kernel(const uint8_t *__restrict__ ps, uint8_t *__restrict__ ws, i
     }
 }
 
-int stream_grid(const void *kernel)
+int stream_grid(const void *kernel, int threads)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) !=
             hipSuccess ||
         per_cu < 1)
         per_cu = 1;
@@ -552,13 +567,14 @@ template <bool kGemm1>
 hipError_t launch_stream(const moe_shape &sh, const StreamArgs &g, int bm, hipStream_t st)
 {
     if (bm == 32) {
-        auto k = gemm_stream_kernel<kGemm1, 32>;
-        const int grid = stream_grid(reinterpret_cast<const void *>(k));
-        k<<<grid, kThreads, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
+        auto k = gemm_stream_kernel<kGemm1, 32, 4>;
+        const int grid = stream_grid(reinterpret_cast<const void *>(k), 256);
+        k<<<grid, 256, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
     } else {
-        auto k = gemm_stream_kernel<kGemm1, kStreamBigRows>;
-        const int grid = stream_grid(reinterpret_cast<const void *>(k));
-        k<<<grid, kThreads, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
+        constexpr int kW = kStreamBigWaves<kGemm1>;
+        auto k = gemm_stream_kernel<kGemm1, kStreamBigRows, kW>;
+        const int grid = stream_grid(reinterpret_cast<const void *>(k), 64 * kW);
+        k<<<grid, 64 * kW, 0, st>>>(to_dev(sh), g, stream_xcds(grid));
     }
     return hipGetLastError();
 }
