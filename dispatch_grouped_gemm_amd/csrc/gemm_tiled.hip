@@ -494,9 +494,10 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
             for (int p = 0; p < (BM * PR + NTH - 1) / NTH; ++p) {
                 const int piece = p * NTH + tid, r = piece / PR, c = piece % PR;
                 if (piece < BM * PR && r < nrows)
-                    *reinterpret_cast<u32x4 *>(g.y8_out + (size_t)(row0 + r) * (size_t)H +
-                                               (size_t)nt * BN + 16 * c) =
-                        lds_read16(lds + r * YP + 16 * c);
+                    __builtin_nontemporal_store(
+                        lds_read16(lds + r * YP + 16 * c),
+                        reinterpret_cast<u32x4 *>(g.y8_out + (size_t)(row0 + r) * (size_t)H +
+                                                  (size_t)nt * BN + 16 * c));
             }
         } else {
             // the bf16 tile goes through LDS (rows of BN*2 + 16 bytes: the
@@ -516,13 +517,18 @@ __device__ __forceinline__ void tiled_item(const Shape &s, const TiledArgs &g,
                               f32_to_bf16(acc[i][j][2]) | (f32_to_bf16(acc[i][j][3]) << 16)};
             }
             __syncthreads();
+            // non-temporal: y is read once, by the combine (the stores drain
+            // sooner, and the next item's first wait, which counts them,
+            // ends sooner: -1% GEMM2 at 65,536 tokens, -6% at 2,048)
             constexpr int PR = BN / 8;                 // 16-byte pieces per row
 #pragma unroll
             for (int p = 0; p < BM * PR / NTH; ++p) {
                 const int piece = p * NTH + tid, r = piece / PR, c = piece % PR;
                 if (r < nrows)
-                    *reinterpret_cast<u32x4 *>(y_out + (size_t)(row0 + r) * (size_t)H +
-                                               (size_t)nt * BN + 8 * c) = lds_read16(lds + r * PITCH + 16 * c);
+                    __builtin_nontemporal_store(
+                        lds_read16(lds + r * PITCH + 16 * c),
+                        reinterpret_cast<u32x4 *>(y_out + (size_t)(row0 + r) * (size_t)H +
+                                                  (size_t)nt * BN + 8 * c));
             }
         }
         }
