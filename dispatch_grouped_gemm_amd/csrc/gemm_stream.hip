@@ -108,7 +108,7 @@ constexpr int kStageBytes = 2 * NL * 2 * 1024;
 
 // One work item of a workgroup: NL (1 .. TB) live 16-row blocks of the chunk
 // at rows row0 .. row0 + nrows - 1 of expert e; wavefront w takes slice
-// 4 sg + w (four weight groups).  Each K step's activation fragments are
+// kW sg + w (four weight groups).  Each K step's activation fragments are
 // fetched once per workgroup and shared through the LDS ring; every
 // wavefront streams its own weights into registers.
 template <bool kGemm1, int TB, int NL, int kW>
@@ -132,7 +132,7 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     // codes (K-step major: 1 KiB per group and K step, a K step's groups
     // adjacent) and exponents (256 bytes per group and four K steps).  A
     // slice past the last (the workgroup's last wavefronts where S is not a
-    // multiple of 4) reads zeros and stores nothing.
+    // multiple of kW) reads zeros and stores nothing.
     const Rsrc wr_r =
         live ? make_rsrc(g.wp + (size_t)e * G * KS * 1024, (uint32_t)(G * KS * 1024)) : null_r;
     const Rsrc ws_r =
@@ -200,11 +200,11 @@ __device__ __forceinline__ void stream_item(const Shape &s, const StreamArgs &g,
     // this wavefront's share of stage p (K steps 2 p, 2 p + 1): step
     // 2 p + (wave & 1), row octet (wave >> 1) & 1, of its blocks, straight
     // into the ring (LDS DMA: lane l's 16 bytes land at 16 l of a 1 KiB
-    // block).  A
-    // step past the last reloads the last (never read).  These loads are
-    // inline assembly, out of the compiler's wait accounting: the waits for
-    // them are the explicit ones below, and the compiler's own waits for its
-    // loads, which do not count them, only wait longer than needed.
+    // block).  A step past the last reloads the last (never read).  These
+    // loads are inline assembly, out of the compiler's wait accounting: the
+    // waits for them are the explicit ones below, and the compiler's own
+    // waits for its loads, which do not count them, only wait longer than
+    // needed.
     const uint8_t *act = kGemm1 ? g.act : g.act + (size_t)row0 * KT;
     const uint32_t ring = lds_addr(lds) + (wave & 1) * (NL * 2048) + ((wave >> 1) & 1) * 1024 +
                           bp * 2048;
