@@ -97,6 +97,10 @@ CASES = [
     ("96-row chunks", dict(T=500, H=512, I=512, seed=3101)),
     ("96-row chunks, ragged", dict(T=300, H=1024, I=896, seed=3102)),
     ("fixed slots", dict(T=300, H=512, I=640, dispatch_mode=1, capacity=80, seed=3103)),
+    # GEMM2 on eight wavefronts: H / 64 = 14 slices, so the second slice
+    # group of a chunk has two wavefronts without one; I = 640, five K steps
+    # (a partial group)
+    ("96-row chunks, idle wavefronts", dict(T=500, H=896, I=640, seed=3104)),
 ]
 
 
